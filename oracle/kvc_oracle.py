@@ -1,0 +1,272 @@
+"""fp64 CPU oracle for single-token decode attention over a KV cache.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke entry and the
+benchmark's CPU-baseline leg may import this module.  It shares no code with
+the HIP path and imports neither torch nor the kernel library.
+
+What it computes, and where the pages say so:
+
+* "KV cache" guide (this.guide/ai/kv-cache.html), section "A cache you keep
+  because attention looks backwards": at generation step t the current
+  token's query attends, through a causal mask, to the keys and values of
+  every position up to t; the key and value of position i depend only on
+  the hidden state at i, so caching them gives the same result as
+  recomputing them.  The attention equation itself was lost when the page
+  was extracted; this oracle uses the standard softmax(q.K^T * scale).V with
+  scale = 1/sqrt(d_h) (1/sqrt(576) for the latent cache).
+* Same guide, "Two tensors per layer": the cache of one layer and one
+  sequence is a key tensor and a value tensor, each [n_kv, L, d_h].
+* Same guide, "Fewer KV heads": grouped-query attention partitions the n_h
+  query heads into n_kv groups that share one KV head.  Reading: the groups
+  are contiguous, so query head i uses KV head i // (n_h / n_kv).
+* Same guide, "Caching a compressed latent": with the key up-projection
+  folded into the query, scores are taken directly against the cached
+  latent; the value side folds into the output projection, so the weighted
+  sum is taken over the latent itself.  The memory footnote fixes the row as
+  a 512-wide latent plus a 64-wide shared rotary key.
+* Podcast transcript (my-weird-prompts 640482), DeepSeek Sparse Attention
+  passage: a top-k subset of stored positions is read; attention runs over
+  those positions only.
+* Podcast transcript, decode walk-through: each new token attends to the
+  cache plus its own new pair, and its key and value are appended.  The
+  oracle appends first and then attends over [0, seq_len), which is the
+  same set of positions.
+
+Storage convention: caches and inputs are held in their storage form,
+float32 arrays or bf16 bit patterns in uint16 arrays.  Appends copy those
+bits.  Arithmetic is float64 throughout.
+
+Device-side conditions (defined here, mirrored by the library contract):
+* append when seq_len is not in [0, L_max): no write, no increment,
+  flag bit 0 (value 1) set;
+* a top-k index outside [0, seq_len): skipped, flag bit 1 (value 2) set;
+* a sequence with no positions to attend: output row 0, lse = -inf.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+FLAG_CACHE_FULL = 1
+FLAG_BAD_INDEX = 2
+
+
+# --------------------------------------------------------------------------
+# storage decoding
+# --------------------------------------------------------------------------
+def bf16_to_f64(u16: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> float64, exactly (bf16 is the top half of fp32)."""
+    u = np.asarray(u16, dtype=np.uint16).astype(np.uint32) << 16
+    return u.view(np.float32).astype(np.float64)
+
+
+def to_f64(raw: np.ndarray) -> np.ndarray:
+    """Storage form -> float64.  uint16 is read as bf16, float32 as is."""
+    raw = np.asarray(raw)
+    if raw.dtype == np.uint16:
+        return bf16_to_f64(raw)
+    if raw.dtype in (np.float32, np.float64):
+        return raw.astype(np.float64)
+    raise TypeError(f"unsupported storage dtype {raw.dtype}")
+
+
+# --------------------------------------------------------------------------
+# cache size ("KV cache" guide, "The size formula")
+# --------------------------------------------------------------------------
+def cache_bytes(n_l: int, n_kv: int, d_h: int, b: int, L: int, B: int) -> int:
+    """Two tensors x layers x KV heads x head dim x bytes x length x batch.
+
+    The guide's equation was lost in extraction; its prose lists exactly
+    these factors, and notes that n_h does not appear.
+    """
+    return 2 * n_l * n_kv * d_h * b * L * B
+
+
+def mla_cache_bytes(n_l: int, d_c: int, d_r: int, b: int, L: int, B: int) -> int:
+    """One latent (d_c) plus one shared rotary key (d_r) per layer and token."""
+    return n_l * (d_c + d_r) * b * L * B
+
+
+# --------------------------------------------------------------------------
+# append (podcast decode walk-through; guide "Two tensors per layer")
+# --------------------------------------------------------------------------
+def append(k_cache, v_cache, seq_lens, k_new, v_new) -> int:
+    """Write the new token's key/value at slot seq_lens[b], then increment.
+
+    k_cache, v_cache: [B, n_kv, L_max, d] storage arrays, modified in place.
+    v_cache may be None for a single-tensor (latent) cache.
+    seq_lens: int32 [B], modified in place.
+    k_new, v_new: [B, n_kv, d].
+    Returns the flag word (bit 0: a sequence had no free slot).
+    """
+    B, n_kv, L_max, d = k_cache.shape
+    flag = 0
+    for b in range(B):
+        n = int(seq_lens[b])
+        if n < 0 or n >= L_max:
+            flag |= FLAG_CACHE_FULL
+            continue
+        k_cache[b, :, n, :] = k_new[b]
+        if v_cache is not None:
+            v_cache[b, :, n, :] = v_new[b]
+        seq_lens[b] = n + 1
+    return flag
+
+
+# --------------------------------------------------------------------------
+# attention of one query over a set of rows
+# --------------------------------------------------------------------------
+def _attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float):
+    """softmax(scale * K q) . V for one query vector, plus its log-sum-exp.
+
+    q: [d_qk], K: [n, d_qk], V: [n, d_v], all float64.  The max is
+    subtracted before exponentiating (no change to the value, only to
+    overflow).  n == 0 gives a zero row and lse = -inf.
+    """
+    n = K.shape[0]
+    if n == 0:
+        return np.zeros(V.shape[1]), -math.inf
+    s = scale * (K @ q)
+    m = s.max()
+    w = np.exp(s - m)
+    z = w.sum()
+    return (w @ V) / z, m + math.log(z)
+
+
+# --------------------------------------------------------------------------
+# dense decode: MHA (G = 1), GQA (1 < G < n_h), MQA (n_kv = 1)
+# --------------------------------------------------------------------------
+def decode(q, k_cache, v_cache, seq_lens, scale: float):
+    """Each query head attends over positions [0, seq_lens[b]) of its KV head.
+
+    q: [B, n_h, d]; k_cache, v_cache: [B, n_kv, L_max, d] (storage form).
+    Returns (o [B, n_h, d] float64, lse [B, n_h] float64, natural log).
+    """
+    B, n_h, d = q.shape
+    n_kv = k_cache.shape[1]
+    assert n_h % n_kv == 0
+    G = n_h // n_kv
+    o = np.zeros((B, n_h, v_cache.shape[3]))
+    lse = np.full((B, n_h), -math.inf)
+    for b in range(B):
+        n = int(seq_lens[b])
+        for j in range(n_kv):
+            K = to_f64(k_cache[b, j, :n])
+            V = to_f64(v_cache[b, j, :n])
+            for i in range(j * G, (j + 1) * G):
+                o[b, i], lse[b, i] = _attend(to_f64(q[b, i]), K, V, scale)
+    return o, lse
+
+
+# --------------------------------------------------------------------------
+# MLA latent decode (guide "Caching a compressed latent")
+# --------------------------------------------------------------------------
+def decode_mla(q, ckv, seq_lens, d_c: int, d_r: int, scale: float):
+    """Attention over a latent cache with absorbed queries.
+
+    q: [B, n_h, d_c + d_r]: the absorbed latent query, then the rotary query.
+    ckv: [B, L_max, d_c + d_r]: per position the latent c, then the shared
+    rotary key.  Score = scale * (q_lat . c + q_rope . k_rope); output is the
+    softmax-weighted sum of the latents c (d_c wide).
+    Returns (o [B, n_h, d_c], lse [B, n_h]).
+    """
+    B, n_h, D = q.shape
+    assert D == d_c + d_r
+    if ckv.ndim == 4:
+        assert ckv.shape[1] == 1
+        ckv = ckv[:, 0]
+    o = np.zeros((B, n_h, d_c))
+    lse = np.full((B, n_h), -math.inf)
+    for b in range(B):
+        n = int(seq_lens[b])
+        rows = to_f64(ckv[b, :n])
+        c, k_rope = rows[:, :d_c], rows[:, d_c:]
+        for i in range(n_h):
+            qi = to_f64(q[b, i])
+            q_lat, q_rope = qi[:d_c], qi[d_c:]
+            if n == 0:
+                continue
+            s = scale * (c @ q_lat + k_rope @ q_rope)
+            m = s.max()
+            w = np.exp(s - m)
+            z = w.sum()
+            o[b, i] = (w @ c) / z
+            lse[b, i] = m + math.log(z)
+    return o, lse
+
+
+# --------------------------------------------------------------------------
+# top-k sparse decode (podcast, DeepSeek Sparse Attention passage)
+# --------------------------------------------------------------------------
+def decode_topk(q, k_cache, v_cache, seq_lens, idx, scale: float):
+    """Attend only over the listed positions: gather, then attend.
+
+    idx: [B, n_kv, K] int.  An index outside [0, seq_lens[b]) is skipped and
+    sets flag bit 1.  A position listed twice counts twice.
+    Returns (o [B, n_h, d], lse [B, n_h], flag).
+    """
+    B, n_h, d = q.shape
+    n_kv = k_cache.shape[1]
+    G = n_h // n_kv
+    o = np.zeros((B, n_h, v_cache.shape[3]))
+    lse = np.full((B, n_h), -math.inf)
+    flag = 0
+    for b in range(B):
+        n = int(seq_lens[b])
+        for j in range(n_kv):
+            listed = [int(t) for t in idx[b, j]]
+            kept = [t for t in listed if 0 <= t < n]
+            if len(kept) != len(listed):
+                flag |= FLAG_BAD_INDEX
+            K = to_f64(k_cache[b, j][kept]) if kept else np.zeros((0, d))
+            V = to_f64(v_cache[b, j][kept]) if kept else np.zeros((0, v_cache.shape[3]))
+            for i in range(j * G, (j + 1) * G):
+                o[b, i], lse[b, i] = _attend(to_f64(q[b, i]), K, V, scale)
+    return o, lse, flag
+
+
+# --------------------------------------------------------------------------
+# full recomputation with a causal mask (guide, first section)
+# --------------------------------------------------------------------------
+def full_causal(Q, K, V, scale: float):
+    """Attention for every position of one sequence, recomputed from scratch.
+
+    Q: [n, n_h, d]; K, V: [n, n_kv, d] (float64 or storage form).  Builds the
+    n x n score matrix per head, adds the causal mask (-inf above the
+    diagonal), takes a row softmax and multiplies by V.
+    Returns O [n, n_h, d_v].
+    """
+    Q, K, V = to_f64(Q), to_f64(K), to_f64(V)
+    n, n_h, _ = Q.shape
+    n_kv = K.shape[1]
+    G = n_h // n_kv
+    mask = np.triu(np.full((n, n), -np.inf), k=1)
+    O = np.zeros((n, n_h, V.shape[2]))
+    for i in range(n_h):
+        j = i // G
+        S = scale * (Q[:, i, :] @ K[:, j, :].T) + mask
+        S = S - S.max(axis=1, keepdims=True)
+        P = np.exp(S)
+        P = P / P.sum(axis=1, keepdims=True)
+        O[:, i, :] = P @ V[:, j, :]
+    return O
+
+
+# --------------------------------------------------------------------------
+# log-sum-exp merge of partial results over a partition of the positions
+# --------------------------------------------------------------------------
+def merge_partials(os_, lses):
+    """Combine per-part (o_p, lse_p) into the result over the union.
+
+    o = sum_p exp(lse_p - LSE) o_p with LSE = log sum_p exp(lse_p).  Parts
+    with lse_p = -inf contribute nothing.
+    """
+    lses = np.asarray(lses, dtype=np.float64)
+    if np.all(np.isneginf(lses)):
+        return np.zeros_like(np.asarray(os_[0], dtype=np.float64)), -math.inf
+    M = lses[~np.isneginf(lses)].max()
+    w = np.exp(lses - M)
+    Z = w.sum()
+    o = sum(wi * np.asarray(oi, dtype=np.float64) for wi, oi in zip(w, os_)) / Z
+    return o, M + math.log(Z)

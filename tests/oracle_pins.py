@@ -1,0 +1,405 @@
+"""Pins for the fp64 oracle: facts fixed by the pages and by mathematics.
+
+Each ``pin_*`` takes an oracle object (the real module, or a copy with a
+planted mistake) and raises AssertionError when the oracle disagrees with
+the fact.  None of them re-types the oracle's formula: they use closed
+forms, invariants, page figures, or an independent scalar brute force.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+
+import kvc_synth as syn
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "page_figures.json")
+
+
+def golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+def _f64_case(rng, B, n_h, n_kv, d, lens, L_max=None, dv=None):
+    """float64 storage-free case (float32 storage, so to_f64 is exact)."""
+    L_max = L_max or max(int(max(lens)), 1)
+    dv = dv or d
+    q = rng.standard_normal((B, n_h, d)).astype(np.float32)
+    kc = rng.standard_normal((B, n_kv, L_max, d)).astype(np.float32)
+    vc = rng.standard_normal((B, n_kv, L_max, dv)).astype(np.float32)
+    return q, kc, vc, np.asarray(lens, dtype=np.int32)
+
+
+# ---------------------------------------------------------------- brute force
+def brute_attend(q, K, V, scale):
+    """Scalar Python attention: math.exp and math.fsum, no numpy arithmetic."""
+    q = [float(x) for x in q]
+    s = [scale * math.fsum(qa * float(ka) for qa, ka in zip(q, row)) for row in K]
+    m = max(s)
+    w = [math.exp(x - m) for x in s]
+    z = math.fsum(w)
+    dv = len(V[0])
+    o = [math.fsum(w[t] * float(V[t][c]) for t in range(len(w))) / z for c in range(dv)]
+    return o, m + math.log(z)
+
+
+# ------------------------------------------------------------------- size
+def pin_size_llama2(orc):
+    """Podcast: Llama-2-7B at fp16, B = 1, 4096 tokens -> about two gigabytes."""
+    g = golden()["llama2_7b_cache"]
+    got = orc.cache_bytes(g["n_l"], g["n_kv"], g["d_h"], g["bytes_per_elem"], g["L"], g["B"])
+    assert abs(got - g["approx_bytes"]) <= g["relative_tolerance"] * g["approx_bytes"], got
+    # Doubling any one factor doubles the size; n_h does not enter.
+    base = got
+    assert orc.cache_bytes(g["n_l"] * 2, g["n_kv"], g["d_h"], 2, g["L"], 1) == 2 * base
+    assert orc.cache_bytes(g["n_l"], g["n_kv"], g["d_h"], 1, g["L"], 1) * 2 == base
+
+
+def pin_size_matches_storage(orc):
+    """The size formula equals the bytes of the cache tensors actually built."""
+    n_l, B, n_kv, d, L = 3, 2, 4, 64, 37
+    total = 0
+    for layer in range(n_l):
+        c = syn.dense_case(B, 8, n_kv, d, L, [L] * B, syn.BF16, layer=layer, poison=False)
+        total += c["k_cache"].nbytes + c["v_cache"].nbytes
+    assert total == orc.cache_bytes(n_l, n_kv, d, 2, L, B), total
+    m = syn.mla_case(B, 4, 512, 64, L, [L] * B, syn.BF16, poison=False)
+    assert m["ckv"].nbytes == orc.mla_cache_bytes(1, 512, 64, 2, L, B)
+
+
+# ---------------------------------------------------------------- causal
+def pin_causal_equals_recompute(orc):
+    """Guide, first section: cached decode step t equals row t of full causal
+    attention recomputed from scratch."""
+    rng = np.random.default_rng(7)
+    n, n_h, n_kv, d = 9, 6, 3, 5
+    Q = rng.standard_normal((n, n_h, d)).astype(np.float32)
+    K = rng.standard_normal((n, n_kv, d)).astype(np.float32)
+    V = rng.standard_normal((n, n_kv, d)).astype(np.float32)
+    scale = 1 / math.sqrt(d)
+    full = orc.full_causal(Q, K, V, scale)
+    kc = np.full((1, n_kv, n, d), np.nan, dtype=np.float32)
+    vc = np.full((1, n_kv, n, d), np.nan, dtype=np.float32)
+    lens = np.zeros(1, dtype=np.int32)
+    for t in range(n):
+        flag = orc.append(kc, vc, lens, K[t][None], V[t][None])
+        assert flag == 0 and lens[0] == t + 1
+        o, _ = orc.decode(Q[t][None], kc, vc, lens, scale)
+        np.testing.assert_allclose(o[0], full[t], rtol=0, atol=1e-12)
+
+
+def pin_full_causal_bruteforce(orc):
+    """full_causal row t equals a scalar brute force over positions 0..t."""
+    rng = np.random.default_rng(11)
+    n, n_h, n_kv, d = 5, 4, 2, 3
+    Q = rng.standard_normal((n, n_h, d))
+    K = rng.standard_normal((n, n_kv, d))
+    V = rng.standard_normal((n, n_kv, d))
+    full = orc.full_causal(Q, K, V, 0.7)
+    G = n_h // n_kv
+    for t in range(n):
+        for i in range(n_h):
+            j = i // G
+            ref, _ = brute_attend(Q[t, i], K[:t + 1, j], V[:t + 1, j], 0.7)
+            np.testing.assert_allclose(full[t, i], ref, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------- brute force
+def pin_decode_bruteforce(orc):
+    """Dense GQA decode equals a scalar brute force (independent arithmetic),
+    for ragged lengths including 0 and 1."""
+    rng = np.random.default_rng(3)
+    B, n_h, n_kv, d = 4, 6, 2, 4
+    lens = [5, 1, 0, 7]
+    q, kc, vc, sl = _f64_case(rng, B, n_h, n_kv, d, lens, L_max=8)
+    kc[:, :, 7:] = np.nan  # never read: lens <= 7
+    vc[:, :, 7:] = np.nan
+    o, lse = orc.decode(q, kc, vc, sl, 0.5)
+    G = n_h // n_kv
+    for b in range(B):
+        for i in range(n_h):
+            n = lens[b]
+            if n == 0:
+                assert np.all(o[b, i] == 0) and lse[b, i] == -math.inf
+                continue
+            ref, rl = brute_attend(q[b, i], kc[b, i // G, :n], vc[b, i // G, :n], 0.5)
+            np.testing.assert_allclose(o[b, i], ref, rtol=0, atol=1e-12)
+            assert abs(lse[b, i] - rl) < 1e-12
+
+
+# --------------------------------------------------------- closed forms
+def pin_single_position(orc):
+    """One position: weight 1, so o = v_0 exactly; lse = scale * q.k_0."""
+    rng = np.random.default_rng(5)
+    q, kc, vc, sl = _f64_case(rng, 2, 4, 2, 8, [1, 1], L_max=3)
+    kc[:, :, 1:] = np.nan
+    vc[:, :, 1:] = np.nan
+    o, lse = orc.decode(q, kc, vc, sl, 0.25)
+    for b in range(2):
+        for i in range(4):
+            assert np.array_equal(o[b, i], vc[b, i // 2, 0].astype(np.float64))
+            s = 0.25 * math.fsum(float(a) * float(c) for a, c in zip(q[b, i], kc[b, i // 2, 0]))
+            assert abs(lse[b, i] - s) < 1e-12
+
+
+def pin_weights_sum_to_one(orc):
+    """V = 1 everywhere gives o = 1 (the weights sum to one)."""
+    rng = np.random.default_rng(6)
+    q, kc, vc, sl = _f64_case(rng, 2, 8, 2, 16, [33, 70], L_max=70)
+    vc[:] = 1.0
+    o, _ = orc.decode(q * 3, kc, vc, sl, 1.0)
+    np.testing.assert_allclose(o, 1.0, rtol=0, atol=1e-13)
+
+
+def pin_two_positions(orc):
+    """n = 2: o = sigmoid(s0 - s1) v0 + sigmoid(s1 - s0) v1, with hand scores.
+
+    q = (1, 2), k0 = (1, 0), k1 = (0, 1), scale 1.5 -> s0 = 1.5, s1 = 3.
+    """
+    q = np.array([[[1.0, 2.0]]], dtype=np.float32)
+    kc = np.array([[[[1.0, 0.0], [0.0, 1.0]]]], dtype=np.float32)
+    vc = np.array([[[[10.0, -1.0], [2.0, 4.0]]]], dtype=np.float32)
+    o, lse = orc.decode(q, kc, vc, np.array([2], dtype=np.int32), 1.5)
+    w0 = 1.0 / (1.0 + math.exp(3.0 - 1.5))
+    w1 = 1.0 / (1.0 + math.exp(1.5 - 3.0))
+    np.testing.assert_allclose(o[0, 0], [10 * w0 + 2 * w1, -1 * w0 + 4 * w1], rtol=0, atol=1e-14)
+    assert abs(lse[0, 0] - (3.0 + math.log(1 + math.exp(-1.5)))) < 1e-14
+
+
+def pin_uniform_query(orc):
+    """q = 0 (or scale = 0): equal weights, o = mean of V rows; V[t] = t gives (n-1)/2."""
+    for n in (1, 2, 17, 64):
+        q = np.zeros((1, 2, 4), dtype=np.float32)
+        kc = np.random.default_rng(n).standard_normal((1, 1, n, 4)).astype(np.float32)
+        vc = np.repeat(np.arange(n, dtype=np.float32)[None, None, :, None], 4, axis=3)
+        o, lse = orc.decode(q, kc, vc, np.array([n], dtype=np.int32), 0.125)
+        np.testing.assert_allclose(o, (n - 1) / 2, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse, math.log(n), rtol=0, atol=1e-12)
+        q1 = np.random.default_rng(1).standard_normal((1, 2, 4)).astype(np.float32)
+        o0, _ = orc.decode(q1, kc, vc, np.array([n], dtype=np.int32), 0.0)
+        np.testing.assert_allclose(o0, (n - 1) / 2, rtol=0, atol=1e-12)
+
+
+def pin_saturation(orc):
+    """Scores far apart: the softmax is one-hot on the max, with no overflow."""
+    q = np.array([[[1.0]]], dtype=np.float32)
+    kc = np.array([[[[1000.0], [-50.0], [999.0 - 40.0]]]], dtype=np.float32)
+    vc = np.array([[[[3.0], [7.0], [11.0]]]], dtype=np.float32)
+    o, lse = orc.decode(q, kc, vc, np.array([3], dtype=np.int32), 1.0)
+    assert np.isfinite(o).all() and abs(o[0, 0, 0] - 3.0) < 1e-15
+    assert abs(lse[0, 0] - 1000.0) < 1e-12
+
+
+def pin_scale_is_multiplicative(orc):
+    """Scaling q by a and scale by 1/a leaves the result unchanged; and the
+    scale enters the scores (scale 0 vs 1 differ for random data)."""
+    rng = np.random.default_rng(8)
+    q, kc, vc, sl = _f64_case(rng, 1, 2, 1, 8, [20])
+    o1, _ = orc.decode(q, kc, vc, sl, 0.5)
+    o2, _ = orc.decode(q * 4, kc, vc, sl, 0.125)
+    np.testing.assert_allclose(o1, o2, rtol=0, atol=1e-12)
+    o3, _ = orc.decode(q, kc, vc, sl, 0.0)
+    assert np.abs(o1 - o3).max() > 1e-3
+
+
+# ------------------------------------------------------------- invariants
+def pin_permutation(orc):
+    """Permuting cached positions (K and V together) leaves o unchanged."""
+    rng = np.random.default_rng(9)
+    q, kc, vc, sl = _f64_case(rng, 1, 4, 2, 8, [31])
+    o, lse = orc.decode(q, kc, vc, sl, 0.3)
+    perm = rng.permutation(31)
+    o2, lse2 = orc.decode(q, kc[:, :, perm], vc[:, :, perm], sl, 0.3)
+    np.testing.assert_allclose(o, o2, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, lse2, rtol=0, atol=1e-12)
+
+
+def pin_split_merge(orc):
+    """Decoding disjoint parts and merging by log-sum-exp equals one pass;
+    lse equals log(sum(exp(s))) from a scalar brute force."""
+    rng = np.random.default_rng(10)
+    d, n = 8, 50
+    q, kc, vc, sl = _f64_case(rng, 1, 1, 1, d, [n])
+    o, lse = orc.decode(q, kc, vc, sl, 0.4)
+    s = [0.4 * math.fsum(float(a) * float(b) for a, b in zip(q[0, 0], kc[0, 0, t])) for t in range(n)]
+    m = max(s)
+    assert abs(lse[0, 0] - (m + math.log(math.fsum(math.exp(x - m) for x in s)))) < 1e-12
+    for cuts in ([25], [1, 2, 49], [10, 20, 30, 40], [0, 50]):
+        bounds = [0] + cuts + [n]
+        parts_o, parts_l = [], []
+        for a, b in zip(bounds[:-1], bounds[1:]):
+            po, pl = orc.decode(q, kc[:, :, a:b], vc[:, :, a:b], np.array([b - a], dtype=np.int32), 0.4)
+            parts_o.append(po[0, 0])
+            parts_l.append(pl[0, 0])
+        mo, ml = orc.merge_partials(parts_o, parts_l)
+        np.testing.assert_allclose(mo, o[0, 0], rtol=0, atol=1e-12)
+        assert abs(ml - lse[0, 0]) < 1e-12
+
+
+def pin_gqa_head_mapping(orc):
+    """Guide, 'Fewer KV heads': groups of G query heads share one KV head.
+    With V_j = j + 1 everywhere, head i returns i // G + 1; GQA equals MHA
+    with each KV head repeated G times; MQA is the n_kv = 1 case."""
+    rng = np.random.default_rng(12)
+    B, n_h, n_kv, d = 2, 12, 3, 8
+    G = n_h // n_kv
+    q, kc, vc, sl = _f64_case(rng, B, n_h, n_kv, d, [13, 40], L_max=40)
+    vconst = vc.copy()
+    for j in range(n_kv):
+        vconst[:, j] = j + 1
+    o, _ = orc.decode(q, kc, vconst, sl, 0.35)
+    for i in range(n_h):
+        np.testing.assert_allclose(o[:, i], i // G + 1, rtol=0, atol=1e-13)
+    og, lg = orc.decode(q, kc, vc, sl, 0.35)
+    om, lm = orc.decode(q, np.repeat(kc, G, axis=1), np.repeat(vc, G, axis=1), sl, 0.35)
+    np.testing.assert_allclose(og, om, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lg, lm, rtol=0, atol=1e-13)
+    oq, _ = orc.decode(q, kc[:, :1], vc[:, :1], sl, 0.35)
+    om1, _ = orc.decode(q, np.repeat(kc[:, :1], n_h, axis=1), np.repeat(vc[:, :1], n_h, axis=1), sl, 0.35)
+    np.testing.assert_allclose(oq, om1, rtol=0, atol=1e-13)
+
+
+# -------------------------------------------------------------------- MLA
+def pin_mla_dims_and_scale():
+    """Guide footnote: 512 + 64 per row, so the score scale 1/sqrt(576) = 1/24."""
+    g = golden()["mla_row"]
+    assert math.sqrt(g["d_c"] + g["d_r"]) == 24.0
+    assert syn.C4.d_c == g["d_c"] and syn.C4.d_r == g["d_r"] and syn.C4.scale == 1 / 24
+
+
+def pin_mla_reduces_to_dense(orc):
+    """MLA equals dense MQA decode with K = the whole row (latent and rotary
+    key) and V = the latent part only; checked also against brute force with
+    the two score terms written separately."""
+    rng = np.random.default_rng(13)
+    B, n_h, d_c, d_r = 2, 5, 12, 4
+    L_max = 20
+    lens = np.array([20, 3], dtype=np.int32)
+    q = rng.standard_normal((B, n_h, d_c + d_r)).astype(np.float32)
+    ckv = rng.standard_normal((B, L_max, d_c + d_r)).astype(np.float32)
+    o, lse = orc.decode_mla(q, ckv, lens, d_c, d_r, 0.2)
+    od, ld = orc.decode(q, ckv[:, None], np.ascontiguousarray(ckv[:, None, :, :d_c]), lens, 0.2)
+    np.testing.assert_allclose(o, od, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse, ld, rtol=0, atol=1e-13)
+    for b in range(B):
+        n = int(lens[b])
+        for i in range(n_h):
+            s = [0.2 * (math.fsum(float(a) * float(c) for a, c in zip(q[b, i, :d_c], ckv[b, t, :d_c]))
+                        + math.fsum(float(a) * float(c) for a, c in zip(q[b, i, d_c:], ckv[b, t, d_c:])))
+                 for t in range(n)]
+            m = max(s)
+            w = [math.exp(x - m) for x in s]
+            z = math.fsum(w)
+            ref = [math.fsum(w[t] * float(ckv[b, t, c]) for t in range(n)) / z for c in range(d_c)]
+            np.testing.assert_allclose(o[b, i], ref, rtol=0, atol=1e-12)
+
+
+def pin_mla_rope_matters(orc):
+    """The rotary part enters the score: zeroing q_rope changes the result,
+    and a latent-orthogonal rotary key alone can decide the weights."""
+    q = np.zeros((1, 1, 3), dtype=np.float32)
+    q[0, 0, 2] = 1.0  # rotary query only
+    ckv = np.array([[[5.0, 0.0, 100.0], [7.0, 1.0, 0.0]]], dtype=np.float32)
+    o, _ = orc.decode_mla(q, ckv, np.array([2], dtype=np.int32), 2, 1, 1.0)
+    np.testing.assert_allclose(o[0, 0], [5.0, 0.0], rtol=0, atol=1e-12)
+
+
+# ------------------------------------------------------------------ top-k
+def pin_topk(orc):
+    """Podcast, DSA passage: attend over the listed positions only.
+
+    * all positions listed -> dense decode;
+    * a subset -> dense decode of the gathered sub-cache;
+    * q = 0 and V[t, 0] = t -> o[0] = mean of the listed indices;
+    * out-of-range indices are skipped and raise flag bit 1.
+    """
+    rng = np.random.default_rng(14)
+    B, n_h, n_kv, d, L = 2, 4, 2, 8, 64
+    lens = np.array([64, 40], dtype=np.int32)
+    q, kc, vc, _ = _f64_case(rng, B, n_h, n_kv, d, [L, L], L_max=L)
+    allidx = np.broadcast_to(np.arange(40, dtype=np.int32), (B, n_kv, 40)).copy()
+    o, lse, flag = orc.decode_topk(q, kc, vc, np.array([40, 40], dtype=np.int32), allidx, 0.3)
+    od, ld = orc.decode(q, kc, vc, np.array([40, 40], dtype=np.int32), 0.3)
+    assert flag == 0
+    np.testing.assert_allclose(o, od, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse, ld, rtol=0, atol=1e-13)
+
+    idx = np.stack([np.stack([np.sort(rng.choice(int(lens[b]), 11, replace=False))
+                              for _ in range(n_kv)]) for b in range(B)]).astype(np.int32)
+    o, lse, flag = orc.decode_topk(q, kc, vc, lens, idx, 0.3)
+    assert flag == 0
+    G = n_h // n_kv
+    for b in range(B):
+        for i in range(n_h):
+            I = idx[b, i // G]
+            ref, rl = brute_attend(q[b, i], kc[b, i // G, I], vc[b, i // G, I], 0.3)
+            np.testing.assert_allclose(o[b, i], ref, rtol=0, atol=1e-12)
+            assert abs(lse[b, i] - rl) < 1e-12
+
+    vt = np.zeros_like(vc)
+    vt[..., 0] = np.arange(L, dtype=np.float32)[None, None, :]
+    o, _, _ = orc.decode_topk(np.zeros_like(q), kc, vt, lens, idx, 0.3)
+    for b in range(B):
+        for i in range(n_h):
+            assert abs(o[b, i, 0] - idx[b, i // G].mean()) < 1e-12
+
+    bad = idx.copy()
+    bad[1, 0, 0] = 45      # >= lens[1] = 40
+    bad[0, 1, 3] = -1
+    o, _, flag = orc.decode_topk(np.zeros_like(q), kc, vt, lens, bad, 0.3)
+    assert flag == orc.FLAG_BAD_INDEX
+    assert abs(o[1, 0, 0] - idx[1, 0, 1:].mean()) < 1e-12
+
+
+# ----------------------------------------------------------------- append
+def pin_append(orc):
+    """Append copies bits (NaN payloads, -0.0, bf16 patterns), increments the
+    length, touches nothing else; a full cache sets flag bit 0 and is left
+    untouched."""
+    B, n_kv, L_max, d = 3, 2, 4, 5
+    kc = np.full((B, n_kv, L_max, d), 0xABCD, dtype=np.uint16)
+    vc = np.full((B, n_kv, L_max, d), 0x1234, dtype=np.uint16)
+    lens = np.array([0, 2, 4], dtype=np.int32)
+    kn = np.arange(B * n_kv * d, dtype=np.uint16).reshape(B, n_kv, d) | 0x7F80
+    vn = np.array([0x8000, 0x7FC1, 0xFFFF, 0x0001, 0x3F80] * (B * n_kv), dtype=np.uint16).reshape(B, n_kv, d)
+    k0, v0 = kc.copy(), vc.copy()
+    flag = orc.append(kc, vc, lens, kn, vn)
+    assert flag == orc.FLAG_CACHE_FULL
+    assert lens.tolist() == [1, 3, 4]
+    for b, slot in ((0, 0), (1, 2)):
+        assert np.array_equal(kc[b, :, slot], kn[b]) and np.array_equal(vc[b, :, slot], vn[b])
+        keep = [t for t in range(L_max) if t != slot]
+        assert np.array_equal(kc[b, :, keep], k0[b, :, keep])
+        assert np.array_equal(vc[b, :, keep], v0[b, :, keep])
+    assert np.array_equal(kc[2], k0[2]) and np.array_equal(vc[2], v0[2])
+    # float32 storage: -0.0 and a NaN payload survive bit for bit
+    kf = np.zeros((1, 1, 2, 2), dtype=np.float32)
+    vf = np.zeros((1, 1, 2, 2), dtype=np.float32)
+    nan_payload = np.array([0x7FC00123], dtype=np.uint32).view(np.float32)[0]
+    new = np.array([[[-0.0, nan_payload]]], dtype=np.float32)
+    lf = np.array([1], dtype=np.int32)
+    orc.append(kf, vf, lf, new, new)
+    assert kf[0, 0, 1].view(np.uint32).tolist() == [0x80000000, 0x7FC00123]
+    assert lf[0] == 2
+
+
+def pin_bf16_decoding(orc):
+    """bf16 is the top half of an IEEE float32."""
+    bits = np.array([0x3F80, 0xC000, 0x7F80, 0xFF80, 0x0001, 0x8000, 0x4049], dtype=np.uint16)
+    got = orc.bf16_to_f64(bits)
+    want = [1.0, -2.0, math.inf, -math.inf, 2.0 ** -133, -0.0, 3.140625]
+    assert got.tolist() == want
+    assert math.copysign(1.0, got[5]) == -1.0
+
+
+ALL_PINS = [
+    pin_size_llama2, pin_size_matches_storage, pin_causal_equals_recompute,
+    pin_full_causal_bruteforce, pin_decode_bruteforce, pin_single_position,
+    pin_weights_sum_to_one, pin_two_positions, pin_uniform_query,
+    pin_saturation, pin_scale_is_multiplicative, pin_permutation,
+    pin_split_merge, pin_gqa_head_mapping, pin_mla_reduces_to_dense,
+    pin_mla_rope_matters, pin_topk, pin_append, pin_bf16_decoding,
+]

@@ -1,0 +1,199 @@
+"""Planted mistakes in copies of the oracle must each trip at least one pin.
+
+Each mutant is a plausible slip (a dropped term, a wrong sign or index, a
+transposed operand, an off-by-one).  The mistakes live only in this file and
+only run on the CPU.
+"""
+import math
+import types
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle_pins as P
+from oracle import kvc_oracle as K
+
+
+def _copy():
+    return types.SimpleNamespace(**{k: getattr(K, k) for k in dir(K) if not k.startswith("__")})
+
+
+def _decode_with(attend=None, head_of=None, length_of=None):
+    attend = attend or K._attend
+
+    def decode(q, k_cache, v_cache, seq_lens, scale):
+        B, n_h, d = q.shape
+        n_kv = k_cache.shape[1]
+        G = n_h // n_kv
+        o = np.zeros((B, n_h, v_cache.shape[3]))
+        lse = np.full((B, n_h), -math.inf)
+        for b in range(B):
+            n = int(seq_lens[b]) if length_of is None else length_of(int(seq_lens[b]))
+            for i in range(n_h):
+                j = i // G if head_of is None else head_of(i, G, n_kv)
+                Kb = K.to_f64(k_cache[b, j, :n])
+                Vb = K.to_f64(v_cache[b, j, :n])
+                o[b, i], lse[b, i] = attend(K.to_f64(q[b, i]), Kb, Vb, scale)
+        return o, lse
+    return decode
+
+
+def _attend_variant(kind):
+    def attend(q, Kr, Vr, scale):
+        n = Kr.shape[0]
+        if n == 0:
+            return np.zeros(Vr.shape[1]), -math.inf
+        if kind == "no_scale":
+            s = Kr @ q
+        elif kind == "neg":
+            s = -scale * (Kr @ q)
+        elif kind == "swap_kv":
+            s = scale * (Vr @ q[:Vr.shape[1]]) if Vr.shape[1] == q.shape[0] else scale * (Kr @ q)
+            Vr = Kr[:, :Vr.shape[1]]
+        else:
+            s = scale * (Kr @ q)
+        if kind == "no_max":
+            w = np.exp(s)
+            z = w.sum()
+            return (w @ Vr) / z, math.log(z)
+        m = s.max()
+        w = np.exp(s - m)
+        z = w.sum()
+        if kind == "log2_lse":
+            return (w @ Vr) / z, m + math.log2(z)
+        if kind == "no_norm":
+            return (w @ Vr), m + math.log(z)
+        return (w @ Vr) / z, m + math.log(z)
+    return attend
+
+
+def mutants():
+    out = {}
+    for kind in ("no_scale", "neg", "swap_kv", "no_max", "log2_lse", "no_norm"):
+        m = _copy()
+        m.decode = _decode_with(attend=_attend_variant(kind))
+        m._attend = _attend_variant(kind)
+        out["attend_" + kind] = m
+    m = _copy()
+    m.decode = _decode_with(head_of=lambda i, G, n_kv: i % n_kv)
+    out["gqa_interleaved_heads"] = m
+    m = _copy()
+    m.decode = _decode_with(length_of=lambda n: max(n - 1, 0))
+    out["drop_newest_position"] = m
+
+    m = _copy()
+
+    def append_no_inc(kc, vc, sl, kn, vn):
+        sl0 = sl.copy()
+        f = K.append(kc, vc, sl, kn, vn)
+        sl[:] = sl0
+        return f
+    m.append = append_no_inc
+    out["append_no_increment"] = m
+
+    m = _copy()
+
+    def append_next_slot(kc, vc, sl, kn, vn):
+        B, n_kv, L_max, d = kc.shape
+        f = 0
+        for b in range(B):
+            n = int(sl[b])
+            if n >= L_max:
+                f |= 1
+                continue
+            t = min(n + 1, L_max - 1)
+            kc[b, :, t] = kn[b]
+            if vc is not None:
+                vc[b, :, t] = vn[b]
+            sl[b] = n + 1
+        return f
+    m.append = append_next_slot
+    out["append_wrong_slot"] = m
+
+    m = _copy()
+
+    def mla_no_rope(q, ckv, seq_lens, d_c, d_r, scale):
+        q2 = q.copy()
+        q2[..., d_c:] = 0
+        return K.decode_mla(q2, ckv, seq_lens, d_c, d_r, scale)
+    m.decode_mla = mla_no_rope
+    out["mla_drops_rope_term"] = m
+
+    m = _copy()
+
+    def mla_rope_in_value(q, ckv, seq_lens, d_c, d_r, scale):
+        o, l = K.decode(q, ckv[:, None] if ckv.ndim == 3 else ckv,
+                        ckv[:, None] if ckv.ndim == 3 else ckv, seq_lens, scale)
+        return o[..., :d_c] * 0 + o[..., d_r:d_r + d_c], l
+    m.decode_mla = mla_rope_in_value
+    out["mla_value_misaligned"] = m
+
+    m = _copy()
+
+    def topk_dense(q, kc, vc, sl, idx, scale):
+        o, l = K.decode(q, kc, vc, sl, scale)
+        return o, l, 0
+    m.decode_topk = topk_dense
+    out["topk_ignores_indices"] = m
+
+    m = _copy()
+
+    def topk_no_skip(q, kc, vc, sl, idx, scale):
+        idx2 = np.clip(idx, 0, None)
+        return K.decode_topk(q, kc, vc, np.full_like(sl, kc.shape[2]), idx2, scale)
+    m.decode_topk = topk_no_skip
+    out["topk_no_range_check"] = m
+
+    m = _copy()
+    m.bf16_to_f64 = lambda u: (np.asarray(u, dtype=np.uint16).astype(np.uint32) << 15).view(np.float32).astype(np.float64)
+    out["bf16_wrong_shift"] = m
+
+    m = _copy()
+    m.cache_bytes = lambda n_l, n_kv, d_h, b, L, B: n_l * n_kv * d_h * b * L * B
+    out["size_missing_factor_two"] = m
+
+    m = _copy()
+
+    def full_causal_leaky(Q, Kk, V, scale):
+        Q, Kk, V = K.to_f64(Q), K.to_f64(Kk), K.to_f64(V)
+        n, n_h, _ = Q.shape
+        G = n_h // Kk.shape[1]
+        mask = np.triu(np.full((n, n), -np.inf), k=2)
+        O = np.zeros((n, n_h, V.shape[2]))
+        for i in range(n_h):
+            S = scale * (Q[:, i] @ Kk[:, i // G].T) + mask
+            P_ = np.exp(S - S.max(axis=1, keepdims=True))
+            O[:, i] = (P_ / P_.sum(axis=1, keepdims=True)) @ V[:, i // G]
+        return O
+    m.full_causal = full_causal_leaky
+    out["causal_mask_off_by_one"] = m
+
+    m = _copy()
+
+    def merge_unweighted(os_, lses):
+        return sum(np.asarray(o) for o in os_) / len(os_), max(lses)
+    m.merge_partials = merge_unweighted
+    out["merge_ignores_lse"] = m
+    return out
+
+
+MUTANTS = mutants()
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name):
+    m = MUTANTS[name]
+    caught = []
+    for pin in P.ALL_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin(m)
+        except (AssertionError, ValueError, FloatingPointError, IndexError):
+            caught.append(pin.__name__)
+    assert caught, f"no pin caught mutant {name}"
+
+
+def test_real_oracle_passes_all():
+    for pin in P.ALL_PINS:
+        pin(oracle)
