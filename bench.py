@@ -1,0 +1,407 @@
+#!/usr/bin/env python3
+"""Decode-attention benchmark on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config C2] [--others C3,C4,C5]
+
+A step is one decode step of every layer of the workload: per layer, the new
+token's key/value are appended (kvc_append) and the token attends over the
+cache (kvc_decode_attn / _mla / _topk).  The step is captured once in a HIP
+graph and replayed; W untimed replays, then K replays between HIP events.
+Each replay appends one more token, so the attended length grows by one per
+step (as in real decoding).
+
+The headline (`value`) is the Llama-2-7B-like MHA workload (32 layers,
+B = 1, 32 heads, d = 128, 4096 cached + 1 appended, bf16): achieved HBM
+GB/s over the algorithmic bytes of a step (cache read + q read + out write +
+new k/v read and written + lengths).  `roofline` is the dense decode kernel
+alone, timed with HIP events over back-to-back launches of one step's
+layers.  `also` carries the same figures for the GQA, MLA and top-k
+workloads.  `cpu_baseline` is the fp64 oracle on the same inputs (copied to
+the host), on a time-bounded sample of layer-steps.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import kvc_synth as syn  # noqa: E402
+
+PEAK_GBS = 8000.0          # MI355X HBM3E, published peak
+CPU_BUDGET_S = 12.0        # oracle sample budget
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="C2", choices=["C2", "C3", "C4", "C5"])
+    ap.add_argument("--others", default="C3,C4,C5",
+                    help="also-measured workloads (comma list, '' for none)")
+    ap.add_argument("--kernel-reps", type=int, default=10)
+    ap.add_argument("--no-cpu", action="store_true")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------- workloads
+class DenseWorkload:
+    """MHA/GQA layers over [B, n_kv, L_max, d] caches (C2, C3)."""
+
+    kernel = "dense_mfma_kernel"
+
+    def __init__(self, cfg, slack, torch, kvc):
+        self.cfg, self.torch, self.kvc = cfg, torch, kvc
+        B, n_h, n_kv, d = cfg.B, cfg.n_h, cfg.n_kv, cfg.d
+        self.pre = syn.pre_append_lens(cfg).astype(np.int64)
+        self.L_max = int(max(cfg.L_max, self.pre.max() + 1) + slack)
+        self.layers = cfg.layers
+        self.nbuf = cfg.distinct_buffers
+        dt = torch.bfloat16
+        self.K, self.V = [], []
+        for i in range(self.nbuf):
+            self.K.append(syn.device_normal_(torch.empty(B, n_kv, self.L_max, d, dtype=dt, device="cuda"),
+                                             syn.device_seed(cfg.cfg_id, i, "k")))
+            self.V.append(syn.device_normal_(torch.empty(B, n_kv, self.L_max, d, dtype=dt, device="cuda"),
+                                             syn.device_seed(cfg.cfg_id, i, "v")))
+        mk = lambda shape, l, t: syn.device_normal_(torch.empty(*shape, dtype=dt, device="cuda"),
+                                                    syn.device_seed(cfg.cfg_id, l, t))
+        self.q = [mk((B, n_h, d), l, "q") for l in range(self.layers)]
+        self.kn = [mk((B, n_kv, d), l, "k_new") for l in range(self.layers)]
+        self.vn = [mk((B, n_kv, d), l, "v_new") for l in range(self.layers)]
+        self.out = [torch.empty(B, n_h, d, dtype=dt, device="cuda") for _ in range(self.layers)]
+        pre_t = torch.tensor(self.pre, dtype=torch.int32)
+        self.sl = [pre_t.clone().cuda() for _ in range(self.layers)]
+        self.ws = kvc.workspace(kvc.kvc_decode_attn_workspace_size(B, n_h, n_kv, self.L_max, d, kvc.KVC_BF16))
+        self.steps_done = 0
+
+    def step(self):
+        kvc = self.kvc
+        for l in range(self.layers):
+            b = l % self.nbuf
+            kvc.kvc_append(self.K[b], self.V[b], self.sl[l], self.kn[l], self.vn[l])
+            kvc.kvc_decode_attn(self.q[l], self.K[b], self.V[b], self.sl[l], self.out[l],
+                                None, scale=self.cfg.scale, workspace=self.ws)
+
+    def decode_only(self):
+        for l in range(self.layers):
+            b = l % self.nbuf
+            self.kvc.kvc_decode_attn(self.q[l], self.K[b], self.V[b], self.sl[l], self.out[l],
+                                     None, scale=self.cfg.scale, workspace=self.ws)
+
+    def lens_after(self, steps_done):
+        """Attended lengths during the step that follows `steps_done` steps."""
+        return np.minimum(self.pre + 1 + steps_done, self.L_max)
+
+    def kernel_bytes(self, n):
+        c = self.cfg
+        return int(2 * c.n_kv * c.d * 2 * n.sum() + c.B * c.n_h * c.d * (2 + 2) + 4 * c.B)
+
+    def step_bytes(self, steps_done):
+        c = self.cfg
+        n = self.lens_after(steps_done)
+        per_layer = self.kernel_bytes(n) + 4 * c.B * c.n_kv * c.d * 2 + 4 * c.B
+        return per_layer * self.layers
+
+    def describe(self):
+        c = self.cfg
+        lens = ("%d cached + 1 appended" % c.pre_len) if c.pre_len is not None else \
+            "seq_lens ~ U[%d, %d] (post-append)" % c.len_range
+        return (f"{c.name}: B={c.B} n_h={c.n_h} n_kv={c.n_kv} d={c.d} bf16, {lens}, "
+                f"{self.layers} layers ({self.nbuf} distinct cache buffers)")
+
+    # oracle on the host, one layer-step at a time
+    def cpu_sample(self, budget_s, oracle):
+        torch, c = self.torch, self.cfg
+        done_bytes, secs, layers = 0, 0.0, 0
+        for l in range(self.layers):
+            b = l % self.nbuf
+            h = lambda t: t.view(torch.int16).cpu().numpy().view(np.uint16)
+            kc, vc = h(self.K[b]), h(self.V[b])
+            q, kn, vn = h(self.q[l]), h(self.kn[l]), h(self.vn[l])
+            sl = self.pre.astype(np.int32).copy()
+            t0 = time.perf_counter()
+            oracle.append(kc, vc, sl, kn, vn)
+            oracle.decode(q, kc, vc, sl, c.scale)
+            secs += time.perf_counter() - t0
+            layers += 1
+            done_bytes += self.step_bytes(0) // self.layers
+            del kc, vc
+            if secs >= budget_s:
+                break
+        return done_bytes, secs, f"{layers} of {self.layers} layer-steps of the same workload"
+
+
+class MlaWorkload:
+    """Latent-cache layers, [B, L_max, 576] per layer buffer (C4)."""
+
+    kernel = "mla_kernel"
+
+    def __init__(self, cfg, slack, torch, kvc):
+        self.cfg, self.torch, self.kvc = cfg, torch, kvc
+        B, n_h, D = cfg.B, cfg.n_h, cfg.d_c + cfg.d_r
+        self.pre = np.full(B, cfg.pre_len, dtype=np.int64)
+        self.L_max = int(cfg.L_max + slack)
+        self.layers = cfg.layers
+        self.nbuf = cfg.distinct_buffers
+        dt = torch.bfloat16
+        mk = lambda shape, l, t: syn.device_normal_(torch.empty(*shape, dtype=dt, device="cuda"),
+                                                    syn.device_seed(cfg.cfg_id, l, t))
+        self.C = [mk((B, self.L_max, D), i, "ckv") for i in range(self.nbuf)]
+        self.q = [mk((B, n_h, D), l, "q") for l in range(self.layers)]
+        self.cn = [mk((B, D), l, "ckv_new") for l in range(self.layers)]
+        self.out = [torch.empty(B, n_h, cfg.d_c, dtype=dt, device="cuda") for _ in range(self.layers)]
+        pre_t = torch.tensor(self.pre, dtype=torch.int32)
+        self.sl = [pre_t.clone().cuda() for _ in range(self.layers)]
+        self.ws = kvc.workspace(kvc.kvc_decode_attn_mla_workspace_size(
+            B, n_h, self.L_max, cfg.d_c, cfg.d_r, kvc.KVC_BF16))
+
+    def step(self):
+        for l in range(self.layers):
+            b = l % self.nbuf
+            self.kvc.kvc_append(self.C[b], None, self.sl[l], self.cn[l], None)
+            self.kvc.kvc_decode_attn_mla(self.q[l], self.C[b], self.sl[l], self.out[l], None,
+                                         scale=self.cfg.scale, workspace=self.ws)
+
+    def decode_only(self):
+        for l in range(self.layers):
+            b = l % self.nbuf
+            self.kvc.kvc_decode_attn_mla(self.q[l], self.C[b], self.sl[l], self.out[l], None,
+                                         scale=self.cfg.scale, workspace=self.ws)
+
+    def lens_after(self, steps_done):
+        return np.minimum(self.pre + 1 + steps_done, self.L_max)
+
+    def kernel_bytes(self, n):
+        c = self.cfg
+        D = c.d_c + c.d_r
+        return int(D * 2 * n.sum() + c.B * c.n_h * (D * 2 + c.d_c * 2) + 4 * c.B)
+
+    def step_bytes(self, steps_done):
+        c = self.cfg
+        per_layer = self.kernel_bytes(self.lens_after(steps_done)) + 2 * c.B * (c.d_c + c.d_r) * 2 + 4 * c.B
+        return per_layer * self.layers
+
+    def describe(self):
+        c = self.cfg
+        return (f"{c.name}: B={c.B} n_h={c.n_h} latent {c.d_c} + rope {c.d_r} bf16, "
+                f"{c.pre_len} cached + 1 appended, scale 1/24, {self.layers} layers")
+
+
+class TopKWorkload:
+    """Top-k sparse GQA over [B, n_kv, L_max, d] caches (C5)."""
+
+    kernel = "dense_mfma_kernel"
+
+    def __init__(self, cfg, slack, torch, kvc):
+        self.cfg, self.torch, self.kvc = cfg, torch, kvc
+        B, n_h, n_kv, d = cfg.B, cfg.n_h, cfg.n_kv, cfg.d
+        self.pre = np.full(B, cfg.pre_len, dtype=np.int64)
+        self.L_max = int(cfg.L_max + slack)
+        self.layers = cfg.index_sets
+        self.nbuf = cfg.distinct_buffers
+        dt = torch.bfloat16
+        mk = lambda shape, l, t: syn.device_normal_(torch.empty(*shape, dtype=dt, device="cuda"),
+                                                    syn.device_seed(cfg.cfg_id, l, t))
+        self.K = [mk((B, n_kv, self.L_max, d), i, "k") for i in range(self.nbuf)]
+        self.V = [mk((B, n_kv, self.L_max, d), i, "v") for i in range(self.nbuf)]
+        self.q = [mk((B, n_h, d), l, "q") for l in range(self.layers)]
+        self.kn = [mk((B, n_kv, d), l, "k_new") for l in range(self.layers)]
+        self.vn = [mk((B, n_kv, d), l, "v_new") for l in range(self.layers)]
+        self.idx = [torch.from_numpy(syn.topk_indices(cfg.cfg_id, 0, B, n_kv, cfg.K, cfg.pre_len,
+                                                      index_set=l)).cuda()
+                    for l in range(self.layers)]
+        self.out = [torch.empty(B, n_h, d, dtype=dt, device="cuda") for _ in range(self.layers)]
+        pre_t = torch.tensor(self.pre, dtype=torch.int32)
+        self.sl = [pre_t.clone().cuda() for _ in range(self.layers)]
+        self.ws = kvc.workspace(kvc.kvc_decode_attn_topk_workspace_size(B, n_h, n_kv, cfg.K, d, kvc.KVC_BF16))
+
+    def step(self):
+        for l in range(self.layers):
+            b = l % self.nbuf
+            self.kvc.kvc_append(self.K[b], self.V[b], self.sl[l], self.kn[l], self.vn[l])
+            self.kvc.kvc_decode_attn_topk(self.q[l], self.K[b], self.V[b], self.sl[l], self.idx[l],
+                                          self.out[l], None, scale=self.cfg.scale, workspace=self.ws)
+
+    def decode_only(self):
+        for l in range(self.layers):
+            b = l % self.nbuf
+            self.kvc.kvc_decode_attn_topk(self.q[l], self.K[b], self.V[b], self.sl[l], self.idx[l],
+                                          self.out[l], None, scale=self.cfg.scale, workspace=self.ws)
+
+    def kernel_bytes(self, n=None):
+        c = self.cfg
+        return int(c.B * c.n_kv * c.K * (2 * c.d * 2 + 4) + c.B * c.n_h * c.d * (2 + 2) + 4 * c.B)
+
+    def lens_after(self, steps_done):
+        return np.minimum(self.pre + 1 + steps_done, self.L_max)
+
+    def step_bytes(self, steps_done):
+        c = self.cfg
+        return (self.kernel_bytes() + 4 * c.B * c.n_kv * c.d * 2 + 4 * c.B) * self.layers
+
+    def describe(self):
+        c = self.cfg
+        return (f"{c.name}: B={c.B} n_h={c.n_h} n_kv={c.n_kv} d={c.d} bf16, K={c.K} sorted distinct "
+                f"indices of L={c.pre_len}, {self.layers} index sets over {self.nbuf} cache buffers")
+
+
+WORKLOADS = {"C2": (syn.C2, DenseWorkload), "C3": (syn.C3, DenseWorkload),
+             "C4": (syn.C4, MlaWorkload), "C5": (syn.C5, TopKWorkload)}
+
+
+# ---------------------------------------------------------------- timing
+def time_graph(torch, fn, reps):
+    """Capture fn once, replay `reps` times between HIP events on the
+    replay stream; returns (ms total, graph)."""
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=s):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def measure(name, args, torch, kvc):
+    cfg, cls = WORKLOADS[name]
+    slack = args.warmup + args.steps + args.kernel_reps + 4
+    wl = cls(cfg, slack, torch, kvc)
+    wl.decode_only()            # first launches outside capture (no state change)
+    torch.cuda.synchronize()
+
+    g = time_graph(torch, wl.step, 1)
+    done = 0
+    for _ in range(args.warmup):
+        g.replay()
+        done += 1
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(args.steps):
+        g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1)
+    bytes_total = sum(wl.step_bytes(done + i) for i in range(args.steps))
+    done += args.steps
+    ms_step = ms / args.steps
+    gbs = bytes_total / (ms * 1e-3) / 1e9
+
+    # the attention kernel alone: one launch per layer, back to back
+    gk = time_graph(torch, wl.decode_only, 1)
+    gk.replay()
+    torch.cuda.synchronize()
+    k0, k1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    k0.record()
+    for _ in range(args.kernel_reps):
+        gk.replay()
+    k1.record()
+    torch.cuda.synchronize()
+    k_us = k0.elapsed_time(k1) * 1e3 / (args.kernel_reps * wl.layers)
+    n_now = wl.lens_after(done - 1)
+    k_bytes = wl.kernel_bytes(n_now)
+    res = dict(
+        workload=wl.describe(), layers=wl.layers, ms_per_step=ms_step,
+        us_per_layer_step=ms_step * 1e3 / wl.layers, gbs=gbs, pct_of_peak=100 * gbs / PEAK_GBS,
+        kernel=wl.kernel, kernel_us=k_us, kernel_bytes=k_bytes,
+        kernel_gbs=k_bytes / (k_us * 1e-6) / 1e9,
+        bytes_per_step=bytes_total / args.steps)
+    return wl, res
+
+
+def read_ceiling(torch, kvc, nbytes=4 << 30, reps=10):
+    buf = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda")
+    buf.fill_(1.0)
+    sink = torch.empty(kvc.kvc_stream_read_sink_floats(nbytes), dtype=torch.float32, device="cuda")
+    kvc.kvc_stream_read(buf, sink)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        kvc.kvc_stream_read(buf, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del buf, sink
+    torch.cuda.empty_cache()
+    return gbs
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+        return max(n) if n else 1
+    except Exception:
+        return 1
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(no multi-GPU path is built)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import kv_cache_decode_kvc_amd as kvc
+    kvc.lib()
+    torch.cuda.set_device(0)
+
+    wl, head = measure(args.config, args, torch, kvc)
+    line = {
+        "metric": "decode-attention achieved HBM GB/s (% of peak) and us/layer-step",
+        "value": round(head["gbs"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1), bf16 round-to-nearest-even)",
+        "config": {"workload": head["workload"], "layers_per_step": head["layers"],
+                   "pct_of_peak": round(head["pct_of_peak"], 2),
+                   "us_per_layer_step": round(head["us_per_layer_step"], 3)},
+        "roofline": {"bound": "hbm", "achieved": round(head["kernel_gbs"], 2),
+                     "peak": PEAK_GBS, "unit": "GB/s",
+                     "frac": round(head["kernel_gbs"] / PEAK_GBS, 4), "traffic": None,
+                     "kernel": head["kernel"], "kernel_us": round(head["kernel_us"], 3),
+                     "algorithmic_bytes_per_launch": head["kernel_bytes"]},
+    }
+
+    if not args.no_cpu:
+        import oracle
+        nbytes, secs, sample = wl.cpu_sample(CPU_BUDGET_S, oracle)
+        line["cpu_baseline"] = {"value": round(nbytes / secs / 1e9, 4), "unit": "GB/s",
+                                "cores": blas_threads(), "kind": "oracle",
+                                "sample": f"{sample}, {secs:.1f} s"}
+    del wl
+    torch.cuda.empty_cache()
+
+    line["read_ceiling_gbs"] = round(read_ceiling(torch, kvc), 1)
+    also = {}
+    for name in [x for x in args.others.split(",") if x and x != args.config]:
+        w, r = measure(name, args, torch, kvc)
+        also[name] = {k: (round(v, 3) if isinstance(v, float) else v) for k, v in r.items()}
+        del w
+        torch.cuda.empty_cache()
+    if also:
+        line["also"] = also
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

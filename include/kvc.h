@@ -1,0 +1,200 @@
+/*
+ * kvc.h - single-token decode attention over a KV cache, for AMD MI355X
+ * (gfx950).  C ABI: plain pointers and sizes only.
+ *
+ * What the calls compute (sources are the pages' titles and sections):
+ *
+ *  - "KV cache" guide (this.guide), "A cache you keep because attention
+ *    looks backwards": at each generation step the new token's query attends
+ *    to the key and value of every earlier position and of itself; keys and
+ *    values are cached because they never change once produced.
+ *  - Same guide, "Two tensors per layer": per layer and sequence the cache is
+ *    a key tensor and a value tensor, each [n_kv, L, d_h].  Here a batch is
+ *    stored as [B, n_kv, L_max, d_h] (a contiguous reservation at the maximum
+ *    length, as in the guide's "The allocator, not the algorithm") with a
+ *    per-sequence length seq_lens[b].
+ *  - Same guide, "Fewer KV heads": grouped-query attention; n_h query heads
+ *    in n_kv contiguous groups of G = n_h / n_kv, query head i reading KV
+ *    head i / G.  G = 1 is multi-head attention, n_kv = 1 multi-query.
+ *  - Same guide, "Caching a compressed latent" and the memory footnote: a
+ *    latent cache row is a 512-wide latent c plus a 64-wide shared rotary
+ *    key; with the key up-projection folded into the query, scores are taken
+ *    directly against the cached row and the output is the weighted sum of
+ *    the latents.
+ *  - Podcast transcript (my-weird-prompts 640482), DeepSeek Sparse Attention
+ *    passage: a top-k list of stored positions is read instead of all of them.
+ *  - Same transcript, the decode walk-through: each new token's key and value
+ *    are appended to the cache, one entry per layer per token.
+ *
+ * Conventions for every call:
+ *  - All tensor pointers are DEVICE pointers, row-major and contiguous, owned
+ *    by the caller.  The library allocates no memory and keeps no per-call
+ *    state.  q/k/v/out pointers must be 16-byte aligned; seq_lens, idx, lse
+ *    and flag 4-byte aligned.
+ *  - dtype is KVC_F32 or KVC_BF16 and applies to q, caches, new rows and out.
+ *    Arithmetic is float32 (exp, sums, products accumulate in float32); bf16
+ *    outputs are rounded to nearest even.  lse is float32, natural log.
+ *  - `stream` is a hipStream_t passed as void*; NULL is the default stream.
+ *    Calls are asynchronous and ordered on that stream.
+ *  - Errors found on the host are returned synchronously before anything is
+ *    enqueued (and before any HIP runtime call): KVC_ERR_* below.  KVC_ERR_HIP
+ *    means a launch failed.
+ *  - Conditions only the device can see are reported through an optional
+ *    device int32 `flag` (bits OR-ed in, never cleared by the library):
+ *    KVC_FLAG_CACHE_FULL and KVC_FLAG_BAD_INDEX.
+ *  - A sequence with nothing to attend gives an output row of zeros and
+ *    lse = -inf.
+ *  - Workspace: decode calls that split the positions of a sequence across
+ *    workgroups need a device workspace of the size the matching *_workspace
+ *    _size call returns (0 means none).  It must be zero-filled before its
+ *    first use; every call leaves it zero-filled again.  Calls that may run
+ *    at the same time need separate workspaces.
+ */
+#ifndef KVC_H
+#define KVC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* element types */
+#define KVC_F32 0
+#define KVC_BF16 1
+
+/* status codes */
+#define KVC_OK 0
+#define KVC_ERR_NULL_PTR (-1)    /* a required pointer is NULL */
+#define KVC_ERR_BAD_SHAPE (-2)   /* non-positive size, n_h % n_kv != 0, K > L_max, offsets beyond 2^31 */
+#define KVC_ERR_BAD_DTYPE (-3)   /* dtype is not KVC_F32 or KVC_BF16 */
+#define KVC_ERR_UNSUPPORTED (-4) /* a shape this build has no kernel for */
+#define KVC_ERR_WORKSPACE (-5)   /* workspace smaller than required */
+#define KVC_ERR_MISALIGNED (-6)  /* pointer alignment rule broken */
+#define KVC_ERR_HIP (-7)         /* HIP launch error */
+#define KVC_ERR_BAD_ARG (-8)     /* non-finite scale, negative split override, ... */
+
+/* device-side condition bits */
+#define KVC_FLAG_CACHE_FULL 1 /* append found seq_lens[b] outside [0, L_max) */
+#define KVC_FLAG_BAD_INDEX 2  /* a top-k index outside [0, seq_lens[b]) */
+
+/*
+ * kvc_append - write the new token's key and value into the cache.
+ * (Podcast transcript, decode walk-through; guide "Two tensors per layer".)
+ *
+ * For each b with n = seq_lens[b] in [0, L_max):
+ *     k_cache[b, :, n, :] = k_new[b]; v_cache[b, :, n, :] = v_new[b];
+ *     seq_lens[b] = n + 1.
+ * Otherwise nothing is written for b and KVC_FLAG_CACHE_FULL is OR-ed into
+ * *flag (when flag is not NULL).  The copy is bit-exact.
+ *
+ *   k_cache, v_cache  [B, n_kv, L_max, d]; v_cache NULL means a single-tensor
+ *                     cache (the latent cache: n_kv = 1, d = d_c + d_r) and
+ *                     then v_new must be NULL too.
+ *   seq_lens          [B] int32, read and incremented on the device.
+ *   k_new, v_new      [B, n_kv, d].
+ *   d                 any positive width.
+ */
+int kvc_append(void* k_cache, void* v_cache, int32_t* seq_lens,
+               const void* k_new, const void* v_new,
+               int B, int n_kv, int L_max, int d, int dtype,
+               int32_t* flag, void* stream);
+
+/*
+ * kvc_decode_attn - dense decode attention (MHA, GQA, MQA).
+ * (Guide, first section and "Fewer KV heads".)
+ *
+ * For each b and query head i, with j = i / (n_h / n_kv), n = seq_lens[b]:
+ *     s_t = scale * <q[b,i,:], k_cache[b,j,t,:]>   for t < n
+ *     out[b,i,:] = sum_t softmax(s)_t * v_cache[b,j,t,:]
+ *     lse[b,i]   = log(sum_t exp(s_t))
+ * Positions t >= n are never read.  seq_lens must already count the token
+ * appended this step (append first, then attend).
+ *
+ *   q      [B, n_h, d]          k_cache, v_cache [B, n_kv, L_max, d]
+ *   out    [B, n_h, d]          lse [B, n_h] float32 or NULL
+ *   d in {64, 128}; n_h / n_kv <= 16; L_max * d * elem_bytes < 2^31.
+ */
+size_t kvc_decode_attn_workspace_size(int B, int n_h, int n_kv, int L_max,
+                                      int d, int dtype);
+int kvc_decode_attn(const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* seq_lens, void* out, float* lse,
+                    int B, int n_h, int n_kv, int L_max, int d, float scale,
+                    int dtype, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * kvc_decode_attn_mla - decode attention over a latent (MLA) cache.
+ * (Guide, "Caching a compressed latent" and the memory footnote.)
+ *
+ * For each b and head i, n = seq_lens[b]:
+ *     s_t = scale * (<q_lat[b,i], c[b,t]> + <q_rope[b,i], k_rope[b,t]>)
+ *     out[b,i,:] = sum_t softmax(s)_t * c[b,t,:]        (d_c wide)
+ * where q[b,i] = q_lat (d_c) followed by q_rope (d_r), and
+ * ckv[b,t] = c (d_c) followed by k_rope (d_r).  Queries are the absorbed
+ * ones; the up-projections are outside this call.
+ *
+ *   q [B, n_h, d_c + d_r]   ckv [B, L_max, d_c + d_r]   out [B, n_h, d_c]
+ *   This build supports dtype KVC_BF16, d_c = 512, d_r = 64, n_h % 64 == 0.
+ */
+size_t kvc_decode_attn_mla_workspace_size(int B, int n_h, int L_max, int d_c,
+                                          int d_r, int dtype);
+int kvc_decode_attn_mla(const void* q, const void* ckv,
+                        const int32_t* seq_lens, void* out, float* lse,
+                        int B, int n_h, int L_max, int d_c, int d_r,
+                        float scale, int dtype, void* workspace,
+                        size_t ws_bytes, void* stream);
+
+/*
+ * kvc_decode_attn_topk - decode attention over listed positions only.
+ * (Podcast, DeepSeek Sparse Attention passage.)
+ *
+ * As kvc_decode_attn, but query heads of KV head j attend only over the
+ * positions idx[b, j, 0..K-1] (gather, then attend; a position listed twice
+ * counts twice).  An index outside [0, seq_lens[b]) is skipped and sets
+ * KVC_FLAG_BAD_INDEX.
+ *
+ *   idx [B, n_kv, K] int32 device.   1 <= K <= L_max.
+ */
+size_t kvc_decode_attn_topk_workspace_size(int B, int n_h, int n_kv, int K,
+                                           int d, int dtype);
+int kvc_decode_attn_topk(const void* q, const void* k_cache,
+                         const void* v_cache, const int32_t* seq_lens,
+                         const int32_t* idx, int K, void* out, float* lse,
+                         int B, int n_h, int n_kv, int L_max, int d,
+                         float scale, int dtype, int32_t* flag,
+                         void* workspace, size_t ws_bytes, void* stream);
+
+/* Text for a status code (static storage). */
+const char* kvc_status_string(int status);
+
+/*
+ * Positions handled by one workgroup before results are merged across
+ * workgroups.  0 restores the built-in policy; other values are rounded up
+ * to the kernel granularity.  Process-wide; meant for tests and tuning, not
+ * for concurrent use with decode calls.  Returns KVC_ERR_BAD_ARG if negative.
+ */
+int kvc_set_split_override(int positions);
+
+/* Positions per workgroup the policy would pick (after any override). */
+int kvc_split_positions(int kind, int B, int units, int n_max);
+#define KVC_KIND_DENSE 0
+#define KVC_KIND_TOPK 1
+#define KVC_KIND_MLA 2
+
+/*
+ * Diagnostics for bandwidth measurement (not part of the attention path).
+ * kvc_stream_read reads `bytes` (multiple of 16) from src with 16-byte loads
+ * and writes one float per workgroup to sink (so the loads are kept);
+ * sink needs kvc_stream_read_sink_floats(bytes) floats.
+ * kvc_copy copies `bytes` (multiple of 16) from src to dst.
+ */
+size_t kvc_stream_read_sink_floats(size_t bytes);
+int kvc_stream_read(const void* src, size_t bytes, float* sink, void* stream);
+int kvc_copy(void* dst, const void* src, size_t bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVC_H */

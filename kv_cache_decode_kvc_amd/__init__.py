@@ -1,0 +1,230 @@
+"""Thin Python binding over libkvc (include/kvc.h).
+
+Argument marshalling only: every function here reads shapes, dtypes and
+device pointers off torch tensors and calls the C entry point of the same
+name on the current torch stream.  All arithmetic runs in the HIP kernels of
+libkvc.so.  There is no fallback: if the library is missing, or a call
+returns an error status, a KvcError is raised.
+
+Build the library with ``python -m kv_cache_decode_kvc_amd.build``.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvc.so")
+
+KVC_F32 = 0
+KVC_BF16 = 1
+KVC_FLAG_CACHE_FULL = 1
+KVC_FLAG_BAD_INDEX = 2
+KVC_KIND_DENSE = 0
+KVC_KIND_TOPK = 1
+KVC_KIND_MLA = 2
+
+STATUS = {0: "KVC_OK", -1: "KVC_ERR_NULL_PTR", -2: "KVC_ERR_BAD_SHAPE",
+          -3: "KVC_ERR_BAD_DTYPE", -4: "KVC_ERR_UNSUPPORTED",
+          -5: "KVC_ERR_WORKSPACE", -6: "KVC_ERR_MISALIGNED", -7: "KVC_ERR_HIP",
+          -8: "KVC_ERR_BAD_ARG"}
+
+
+class KvcError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)} "
+                         f"({lib().kvc_status_string(status).decode()})")
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_Z = ctypes.c_size_t
+_F = ctypes.c_float
+
+
+def lib() -> ctypes.CDLL:
+    """Load libkvc.so (once).  Raises ImportError if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing; build it with "
+                          "`python -m kv_cache_decode_kvc_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    sig = {
+        "kvc_append": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P]),
+        "kvc_decode_attn_workspace_size": (_Z, [_I, _I, _I, _I, _I, _I]),
+        "kvc_decode_attn": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
+                                 _F, _I, _P, _Z, _P]),
+        "kvc_decode_attn_mla_workspace_size": (_Z, [_I, _I, _I, _I, _I, _I]),
+        "kvc_decode_attn_mla": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
+                                     _F, _I, _P, _Z, _P]),
+        "kvc_decode_attn_topk_workspace_size": (_Z, [_I, _I, _I, _I, _I, _I]),
+        "kvc_decode_attn_topk": (_I, [_P, _P, _P, _P, _P, _I, _P, _P, _I, _I,
+                                      _I, _I, _I, _F, _I, _P, _P, _Z, _P]),
+        "kvc_status_string": (ctypes.c_char_p, [_I]),
+        "kvc_set_split_override": (_I, [_I]),
+        "kvc_split_positions": (_I, [_I, _I, _I, _I]),
+        "kvc_stream_read_sink_floats": (_Z, [_Z]),
+        "kvc_stream_read": (_I, [_P, _Z, _P, _P]),
+        "kvc_copy": (_I, [_P, _P, _Z, _P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = L
+    return L
+
+
+# ---------------------------------------------------------------- helpers
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return KVC_F32
+    if t.dtype == torch.bfloat16:
+        return KVC_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise KvcError(status, where)
+
+
+def workspace(nbytes: int, device="cuda"):
+    """A zero-filled workspace buffer of at least nbytes (None if 0)."""
+    import torch
+    if nbytes == 0:
+        return None
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device)
+
+
+def _ws(ws):
+    return (None, 0) if ws is None else (_ptr(ws), ws.numel() * ws.element_size())
+
+
+# ---------------------------------------------------------------- calls
+def kvc_status_string(status: int) -> str:
+    return lib().kvc_status_string(status).decode()
+
+
+def kvc_set_split_override(positions: int) -> None:
+    _check(lib().kvc_set_split_override(positions), "kvc_set_split_override")
+
+
+def kvc_split_positions(kind: int, B: int, units: int, n_max: int) -> int:
+    v = lib().kvc_split_positions(kind, B, units, n_max)
+    if v < 0:
+        raise KvcError(v, "kvc_split_positions")
+    return v
+
+
+def kvc_append(k_cache, v_cache, seq_lens, k_new, v_new, flag=None, stream=None):
+    """Append k_new/v_new [B, n_kv, d] at slot seq_lens[b]; bump seq_lens.
+
+    k_cache/v_cache: [B, n_kv, L_max, d], or a latent cache [B, L_max, D]
+    with v_cache = v_new = None.
+    """
+    if k_cache.dim() == 3:
+        B, L_max, d = k_cache.shape
+        n_kv = 1
+    else:
+        B, n_kv, L_max, d = k_cache.shape
+    st = lib().kvc_append(_ptr(k_cache), _ptr(v_cache), _ptr(seq_lens),
+                          _ptr(k_new), _ptr(v_new), B, n_kv, L_max, d,
+                          _dtype_code(k_cache), _ptr(flag), _stream(stream))
+    _check(st, "kvc_append")
+
+
+def kvc_decode_attn_workspace_size(B, n_h, n_kv, L_max, d, dtype) -> int:
+    return lib().kvc_decode_attn_workspace_size(B, n_h, n_kv, L_max, d, dtype)
+
+
+def kvc_decode_attn(q, k_cache, v_cache, seq_lens, out, lse=None, scale=None,
+                    workspace=None, stream=None):
+    """Dense decode attention; q/out [B, n_h, d], caches [B, n_kv, L_max, d]."""
+    B, n_h, d = q.shape
+    _, n_kv, L_max, _ = k_cache.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    wp, wn = _ws(workspace)
+    st = lib().kvc_decode_attn(_ptr(q), _ptr(k_cache), _ptr(v_cache),
+                               _ptr(seq_lens), _ptr(out), _ptr(lse), B, n_h,
+                               n_kv, L_max, d, scale, _dtype_code(q), wp, wn,
+                               _stream(stream))
+    _check(st, "kvc_decode_attn")
+
+
+def kvc_decode_attn_mla_workspace_size(B, n_h, L_max, d_c, d_r, dtype) -> int:
+    return lib().kvc_decode_attn_mla_workspace_size(B, n_h, L_max, d_c, d_r, dtype)
+
+
+def kvc_decode_attn_mla(q, ckv, seq_lens, out, lse=None, scale=None,
+                        workspace=None, stream=None):
+    """Latent-cache decode; q [B, n_h, d_c + d_r], ckv [B, L_max, d_c + d_r],
+    out [B, n_h, d_c]."""
+    B, n_h, D = q.shape
+    L_max = ckv.shape[-2]
+    d_c = out.shape[-1]
+    d_r = D - d_c
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    wp, wn = _ws(workspace)
+    st = lib().kvc_decode_attn_mla(_ptr(q), _ptr(ckv), _ptr(seq_lens), _ptr(out),
+                                   _ptr(lse), B, n_h, L_max, d_c, d_r, scale,
+                                   _dtype_code(q), wp, wn, _stream(stream))
+    _check(st, "kvc_decode_attn_mla")
+
+
+def kvc_decode_attn_topk_workspace_size(B, n_h, n_kv, K, d, dtype) -> int:
+    return lib().kvc_decode_attn_topk_workspace_size(B, n_h, n_kv, K, d, dtype)
+
+
+def kvc_decode_attn_topk(q, k_cache, v_cache, seq_lens, idx, out, lse=None,
+                         scale=None, flag=None, workspace=None, stream=None):
+    """Decode attention over idx [B, n_kv, K] (int32) listed positions."""
+    B, n_h, d = q.shape
+    _, n_kv, L_max, _ = k_cache.shape
+    K = idx.shape[-1]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    wp, wn = _ws(workspace)
+    st = lib().kvc_decode_attn_topk(_ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                    _ptr(seq_lens), _ptr(idx), K, _ptr(out),
+                                    _ptr(lse), B, n_h, n_kv, L_max, d, scale,
+                                    _dtype_code(q), _ptr(flag), wp, wn,
+                                    _stream(stream))
+    _check(st, "kvc_decode_attn_topk")
+
+
+def kvc_stream_read_sink_floats(nbytes: int) -> int:
+    return lib().kvc_stream_read_sink_floats(nbytes)
+
+
+def kvc_stream_read(src, sink, nbytes=None, stream=None):
+    nbytes = src.numel() * src.element_size() if nbytes is None else nbytes
+    _check(lib().kvc_stream_read(_ptr(src), nbytes, _ptr(sink), _stream(stream)),
+           "kvc_stream_read")
+
+
+def kvc_copy(dst, src, nbytes=None, stream=None):
+    nbytes = src.numel() * src.element_size() if nbytes is None else nbytes
+    _check(lib().kvc_copy(_ptr(dst), _ptr(src), nbytes, _stream(stream)), "kvc_copy")

@@ -1,0 +1,563 @@
+// Dense (MHA / GQA / MQA) and top-k decode attention kernels for gfx950.
+//
+// What is computed: for each sequence b and query head i with KV head
+// j = i / G, softmax(scale * q K^T) V over the positions [0, seq_lens[b])
+// (or over the listed positions for top-k) - the "KV cache" guide
+// (this.guide), first section and "Fewer KV heads"; the podcast transcript's
+// DeepSeek Sparse Attention passage for the listed-position variant.
+//
+// Work decomposition (same for both kernels): one workgroup of 4 waves per
+// (b, j, split), where a split is S consecutive positions (or list slots).
+// The G query heads of one KV head share every K/V row the workgroup reads,
+// so each cache byte crosses HBM once per step.  Waves keep an online
+// softmax (running max, running sum, rescaled accumulators) in log2 units.
+// A workgroup merges its waves through LDS; when a sequence needs several
+// splits, each writes a normalised partial (o_p, lse_p) to the workspace
+// and the last workgroup to finish (a device-scope ticket) merges them by
+// log-sum-exp and resets the ticket.
+
+#include "kvc_device.h"
+#include "kvc_internal.h"
+
+namespace kvc {
+
+// ---------------------------------------------------------------------------
+// shared epilogue
+// ---------------------------------------------------------------------------
+template <int D>
+struct MergeLds {
+  float o[4][kMaxGroup][D];
+  float m[4][kMaxGroup];
+  float l[4][kMaxGroup];
+  int last;
+};
+
+template <typename OutT, int CPT>
+__device__ inline void store_row(OutT* dst, const float* o);
+
+template <>
+__device__ inline void store_row<uint16_t, 8>(uint16_t* dst, const float* o) {
+  u32x4 v = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]),
+             pack_bf16x2(o[4], o[5]), pack_bf16x2(o[6], o[7])};
+  *reinterpret_cast<u32x4*>(dst) = v;
+}
+template <>
+__device__ inline void store_row<uint16_t, 4>(uint16_t* dst, const float* o) {
+  uint2 v = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+  *reinterpret_cast<uint2*>(dst) = v;
+}
+template <>
+__device__ inline void store_row<float, 8>(float* dst, const float* o) {
+  reinterpret_cast<float4*>(dst)[0] = make_float4(o[0], o[1], o[2], o[3]);
+  reinterpret_cast<float4*>(dst)[1] = make_float4(o[4], o[5], o[6], o[7]);
+}
+template <>
+__device__ inline void store_row<float, 4>(float* dst, const float* o) {
+  reinterpret_cast<float4*>(dst)[0] = make_float4(o[0], o[1], o[2], o[3]);
+}
+
+// Thread t of the workgroup owns local head t/16 and columns
+// (t%16)*D/16 .. +D/16 in every epilogue step.
+template <typename OutT, int D>
+__device__ inline void write_final(const DenseParams& p, size_t bh,
+                                   const float* o, float lse2) {
+  constexpr int CPT = D / 16;
+  const int c0 = (threadIdx.x & 15) * CPT;
+  store_row<OutT, CPT>(reinterpret_cast<OutT*>(p.out) + bh * D + c0, o);
+  if (p.lse && (threadIdx.x & 15) == 0) p.lse[bh] = lse2 * kLn2;
+}
+
+template <typename OutT, int D>
+__device__ void write_empty(const DenseParams& p, int b, int j) {
+  constexpr int CPT = D / 16;
+  const int hl = threadIdx.x >> 4;
+  if (hl >= p.G) return;
+  float o[CPT];
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) o[c] = 0.f;
+  write_final<OutT, D>(p, (size_t)b * p.n_h + j * p.G + hl, o, kNegInf);
+}
+
+template <typename OutT, int D>
+__device__ void finish_split(const DenseParams& p, int b, int j, int split,
+                             int nsplit, MergeLds<D>& L) {
+  constexpr int CPT = D / 16;
+  const int t = threadIdx.x;
+  const int hl = t >> 4;
+  const int c0 = (t & 15) * CPT;
+  const bool active = hl < p.G;
+  const size_t bh = (size_t)b * p.n_h + j * p.G + hl;
+
+  float o[CPT];
+  float lse2 = kNegInf;
+  if (active) {
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, L.m[w][hl]);
+    const float Mu = (M == kNegInf) ? 0.f : M;
+    float Z = 0.f;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) o[c] = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float e = __builtin_amdgcn_exp2f(L.m[w][hl] - Mu);
+      Z += e * L.l[w][hl];
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) o[c] += e * L.o[w][hl][c0 + c];
+    }
+    const float inv = Z > 0.f ? 1.f / Z : 0.f;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) o[c] *= inv;
+    lse2 = Z > 0.f ? M + __log2f(Z) : kNegInf;
+  }
+
+  if (nsplit == 1) {
+    if (active) write_final<OutT, D>(p, bh, o, lse2);
+    return;
+  }
+
+  // Several splits: publish this one, then the last to arrive merges.
+  const size_t slot = bh * p.P_max + split;
+  if (active) {
+    store_row<float, CPT>(p.ws_o + slot * D + c0, o);
+    if ((t & 15) == 0) p.ws_lse[slot] = lse2;
+  }
+  __threadfence();
+  __syncthreads();
+  int32_t* ticket = p.ws_cnt + (size_t)b * p.n_kv + j;
+  if (t == 0) L.last = (atomicAdd(ticket, 1) == nsplit - 1);
+  __syncthreads();
+  if (!L.last) return;
+  __threadfence();
+
+  if (active) {
+    const float* lp = p.ws_lse + bh * p.P_max;
+    const float* op = p.ws_o + bh * p.P_max * D + c0;
+    float M = kNegInf;
+    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, lp[s]);
+    const float Mu = (M == kNegInf) ? 0.f : M;
+    float Z = 0.f;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) o[c] = 0.f;
+    for (int s = 0; s < nsplit; ++s) {
+      const float e = __builtin_amdgcn_exp2f(lp[s] - Mu);
+      Z += e;
+      const float* row = op + (size_t)s * D;
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) o[c] += e * row[c];
+    }
+    const float inv = Z > 0.f ? 1.f / Z : 0.f;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) o[c] *= inv;
+    write_final<OutT, D>(p, bh, o, Z > 0.f ? M + __log2f(Z) : kNegInf);
+  }
+  if (t == 0) *ticket = 0;
+}
+
+__device__ inline void decode_unit(const DenseParams& p, int& b, int& j,
+                                   int& split) {
+  int wg = blockIdx.x;
+  split = wg % p.P_max;
+  wg /= p.P_max;
+  j = wg % p.n_kv;
+  b = wg / p.n_kv;
+}
+
+// ---------------------------------------------------------------------------
+// MFMA kernel: bf16, d = 128, G <= 16.
+//
+// Per wave and 32-position chunk (lane = 16*g + r):
+//  scores  S^T[t][h] = K[t,:] . q[h,:] as two 16x16x32 MFMA tiles x 4 k-steps;
+//          A = K rows straight from HBM (lane r reads row pi(a,r), 16 B at
+//          column kk*32 + g*8), B = q (16 heads, heads >= G are zero).
+//          The row order pi(a, r) = (r/4)*8 + a*4 + r%4 makes the output land
+//          as: lane (r, g) holds head r at positions g*8 + 0..7.
+//  weights those 8 scores are exactly the B operand of the value product
+//          (P[h = r][slot j = position g*8 + j]), after an online softmax.
+//  values  O^T[c][h] += V^T[c][t] P^T[t][h]: 8 tiles of 16 columns; lane
+//          (r, g) reads rows g*8 + 0..7 at columns r*8..r*8+7 (each load
+//          instruction covers 4 whole 256-B rows) and transposes 8x8 bf16 in
+//          registers with v_perm so that tile m row r is column r*8 + m.
+//  result  lane (r, g) ends with head r, columns 32g .. 32g+31.
+// ---------------------------------------------------------------------------
+struct Chunk {
+  u32x4 k[2][4];
+  u32x4 v[8];
+  uint32_t vmask;   // top-k: slot g*8+e valid
+};
+
+template <bool TOPK>
+__device__ inline void load_chunk(Chunk& c, int cs, int end, int n,
+                                  __amdgpu_buffer_rsrc_t kr,
+                                  __amdgpu_buffer_rsrc_t vr,
+                                  __amdgpu_buffer_rsrc_t ir, int r, int g,
+                                  bool& bad) {
+  constexpr uint32_t kRow = 256;
+  if constexpr (!TOPK) {
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      const uint32_t row = cs + (r >> 2) * 8 + a * 4 + (r & 3);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        c.k[a][kk] = buf_load16(kr, row * kRow + kk * 64 + g * 16);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      c.v[e] = buf_load16(vr, (uint32_t)(cs + g * 8 + e) * kRow + r * 16);
+    c.vmask = 0xFF;
+  } else {
+    // slots for the V rows: cs + g*8 + 0..7; for the K rows: cs + pi(a, r).
+    const u32x4 i0 = buf_load16(ir, (uint32_t)(cs + g * 8) * 4);
+    const u32x4 i1 = buf_load16(ir, (uint32_t)(cs + g * 8 + 4) * 4);
+    const uint32_t iv[8] = {i0[0], i0[1], i0[2], i0[3], i1[0], i1[1], i1[2], i1[3]};
+    uint32_t mask = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int slot = cs + g * 8 + e;
+      const bool in_list = slot < end;
+      const bool ok = iv[e] < (uint32_t)n;
+      if (in_list && !ok) bad = true;
+      const bool use = in_list && ok;
+      mask |= (use ? 1u : 0u) << e;
+      c.v[e] = buf_load16(vr, use ? iv[e] * kRow + r * 16 : kOobOffset);
+    }
+    c.vmask = mask;
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      const int slot = cs + (r >> 2) * 8 + a * 4 + (r & 3);
+      const uint32_t t = __builtin_amdgcn_raw_buffer_load_b32(ir, (uint32_t)slot * 4, 0, 0);
+      const bool use = slot < end && t < (uint32_t)n;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        c.k[a][kk] = buf_load16(kr, use ? t * kRow + kk * 64 + g * 16 : kOobOffset);
+    }
+  }
+}
+
+struct WaveState {
+  float m;        // running max (log2 units), same in the 4 lanes of a head
+  float l;        // this lane's share of the running sum
+  f32x4 acc[8];   // O^T tiles
+};
+
+template <bool TOPK>
+__device__ inline void compute_chunk(const Chunk& c, int cs, int end,
+                                     const bf16x8 (&qop)[4], float scale_log2,
+                                     int g, WaveState& st) {
+  f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(c.k[0][kk]), qop[kk], s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(c.k[1][kk]), qop[kk], s1, 0, 0, 0);
+  }
+  float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+  float mx = kNegInf;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    bool valid;
+    if constexpr (TOPK) valid = (c.vmask >> e) & 1;
+    else valid = cs + g * 8 + e < end;
+    sv[e] = valid ? sv[e] * scale_log2 : kNegInf;
+    mx = fmaxf(mx, sv[e]);
+  }
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float m_new = fmaxf(st.m, mx);
+  const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+  const float alpha = __builtin_amdgcn_exp2f(st.m - m_use);
+  st.m = m_new;
+  if (__any(alpha != 1.f)) {
+#pragma unroll
+    for (int m = 0; m < 8; ++m) st.acc[m] *= alpha;
+  }
+  uint32_t pp[4];
+  float psum = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    pp[e] = pack_bf16x2(__builtin_amdgcn_exp2f(sv[2 * e] - m_use),
+                        __builtin_amdgcn_exp2f(sv[2 * e + 1] - m_use));
+    psum += bf16_lo(pp[e]) + bf16_hi(pp[e]);
+  }
+  st.l = st.l * alpha + psum;
+  const u32x4 pv = {pp[0], pp[1], pp[2], pp[3]};
+  const bf16x8 pop = as_bf16x8(pv);
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    const uint32_t sel = (m & 1) ? 0x07060302u : 0x05040100u;
+    const int dw = m >> 1;
+    u32x4 a;
+    a[0] = __builtin_amdgcn_perm(c.v[1][dw], c.v[0][dw], sel);
+    a[1] = __builtin_amdgcn_perm(c.v[3][dw], c.v[2][dw], sel);
+    a[2] = __builtin_amdgcn_perm(c.v[5][dw], c.v[4][dw], sel);
+    a[3] = __builtin_amdgcn_perm(c.v[7][dw], c.v[6][dw], sel);
+    st.acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), pop, st.acc[m], 0, 0, 0);
+  }
+}
+
+template <bool TOPK>
+__global__ __launch_bounds__(256) void dense_mfma_kernel(DenseParams p) {
+  __shared__ MergeLds<128> L;
+  int b, j, split;
+  decode_unit(p, b, j, split);
+  const int n = min(max(p.seq_lens[b], 0), p.L_max);
+  const int count = TOPK ? p.K : n;
+  const int start = split * p.S;
+  if (start >= count) {
+    if (split == 0) write_empty<uint16_t, 128>(p, b, j);
+    return;
+  }
+  const int end = min(count, start + p.S);
+  const int nsplit = (count + p.S - 1) / p.S;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const size_t unit = (size_t)b * p.n_kv + j;
+  const size_t unit_bytes = (size_t)p.L_max * 256;
+  const __amdgpu_buffer_rsrc_t kr =
+      make_rsrc((const char*)p.k + unit * unit_bytes, (uint32_t)n * 256u);
+  const __amdgpu_buffer_rsrc_t vr =
+      make_rsrc((const char*)p.v + unit * unit_bytes, (uint32_t)n * 256u);
+  const __amdgpu_buffer_rsrc_t ir =
+      TOPK ? make_rsrc(p.idx + unit * p.K, (uint32_t)p.K * 4u) : kr;
+
+  bf16x8 qop[4];
+  if (r < p.G) {
+    const uint16_t* qrow =
+        (const uint16_t*)p.q + ((size_t)b * p.n_h + j * p.G + r) * 128;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      qop[kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow + kk * 32 + g * 8));
+  } else {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) qop[kk] = as_bf16x8(z);
+  }
+
+  WaveState st;
+  st.m = kNegInf;
+  st.l = 0.f;
+#pragma unroll
+  for (int m = 0; m < 8; ++m) st.acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  bool bad = false;
+  int cs = start + wave * kDenseChunk;
+  constexpr int kStride = kDenseChunk * 4;
+  if (cs < end) {
+    Chunk A, Bc;
+    load_chunk<TOPK>(A, cs, end, n, kr, vr, ir, r, g, bad);
+    while (true) {
+      int cn = cs + kStride;
+      bool more = cn < end;
+      if (more) load_chunk<TOPK>(Bc, cn, end, n, kr, vr, ir, r, g, bad);
+      compute_chunk<TOPK>(A, cs, end, qop, p.scale_log2, g, st);
+      if (!more) break;
+      cs = cn;
+      cn = cs + kStride;
+      more = cn < end;
+      if (more) load_chunk<TOPK>(A, cn, end, n, kr, vr, ir, r, g, bad);
+      compute_chunk<TOPK>(Bc, cs, end, qop, p.scale_log2, g, st);
+      if (!more) break;
+      cs = cn;
+    }
+  }
+  if constexpr (TOPK) {
+    if (p.flag && __any(bad) && lane == 0) atomicOr(p.flag, 2);
+  }
+
+  float l_tot = st.l + __shfl_xor(st.l, 16);
+  l_tot += __shfl_xor(l_tot, 32);
+  if (g == 0) {
+    L.m[wave][r] = st.m;
+    L.l[wave][r] = l_tot;
+  }
+#pragma unroll
+  for (int m = 0; m < 8; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) L.o[wave][r][(4 * g + i) * 8 + m] = st.acc[m][i];
+  __syncthreads();
+  finish_split<uint16_t, 128>(p, b, j, split, nsplit, L);
+}
+
+// ---------------------------------------------------------------------------
+// Generic VALU kernel: float32 or bf16, d in {64, 128}, G <= 16.
+// Lane = position for the scores; lane = column for the weighted sum, with
+// each position's weight broadcast by readlane.
+// ---------------------------------------------------------------------------
+template <typename T>
+__device__ inline float ld_f32(const T* p);
+template <>
+__device__ inline float ld_f32<float>(const float* p) { return *p; }
+template <>
+__device__ inline float ld_f32<uint16_t>(const uint16_t* p) {
+  return __uint_as_float((uint32_t)*p << 16);
+}
+
+// Eight consecutive elements as float32.
+__device__ inline void load8(const float* p, float (&x)[8]) {
+  const float4 a = reinterpret_cast<const float4*>(p)[0];
+  const float4 b = reinterpret_cast<const float4*>(p)[1];
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+__device__ inline void load8(const uint16_t* p, float (&x)[8]) {
+  const u32x4 k = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    x[2 * e] = bf16_lo(k[e]);
+    x[2 * e + 1] = bf16_hi(k[e]);
+  }
+}
+
+template <typename T, int D, bool TOPK>
+__global__ __launch_bounds__(256) void dense_generic_kernel(DenseParams p) {
+  __shared__ MergeLds<D> L;
+  __shared__ float sq[kMaxGroup][D];
+  int b, j, split;
+  decode_unit(p, b, j, split);
+  const int n = min(max(p.seq_lens[b], 0), p.L_max);
+  const int count = TOPK ? p.K : n;
+  const int start = split * p.S;
+  if (start >= count) {
+    if (split == 0) write_empty<T, D>(p, b, j);
+    return;
+  }
+  const int end = min(count, start + p.S);
+  const int nsplit = (count + p.S - 1) / p.S;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int G = p.G;
+
+  const T* qg = (const T*)p.q + ((size_t)b * p.n_h + j * G) * D;
+  for (int e = tid; e < G * D; e += 256) sq[e / D][e % D] = ld_f32<T>(qg + e);
+  __syncthreads();
+
+  const size_t unit = (size_t)b * p.n_kv + j;
+  const T* kb = (const T*)p.k + unit * p.L_max * D;
+  const T* vb = (const T*)p.v + unit * p.L_max * D;
+  constexpr int U = D / 64;
+
+  float m_run[kMaxGroup], l_run[kMaxGroup], o[kMaxGroup][U];
+#pragma unroll
+  for (int h = 0; h < kMaxGroup; ++h) {
+    m_run[h] = kNegInf;
+    l_run[h] = 0.f;
+#pragma unroll
+    for (int u = 0; u < U; ++u) o[h][u] = 0.f;
+  }
+
+  bool bad = false;
+  for (int blk = start + wave * 64; blk < end; blk += 256) {
+    const int slot = blk + lane;
+    bool valid = slot < end;
+    int row = slot;
+    if constexpr (TOPK) {
+      row = valid ? p.idx[unit * p.K + slot] : 0;
+      const bool ok = (unsigned)row < (unsigned)n;
+      if (valid && !ok) bad = true;
+      valid = valid && ok;
+    }
+    float s[kMaxGroup];
+#pragma unroll
+    for (int h = 0; h < kMaxGroup; ++h) s[h] = 0.f;
+    if (valid) {
+      const T* krow = kb + (size_t)row * D;
+#pragma unroll 2
+      for (int d0 = 0; d0 < D; d0 += 8) {
+        float kv[8];
+        load8(krow + d0, kv);
+#pragma unroll
+        for (int h = 0; h < kMaxGroup; ++h) {
+          if (h >= G) continue;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) s[h] += sq[h][d0 + e] * kv[e];
+        }
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < kMaxGroup; ++h)
+      s[h] = (valid && h < G) ? s[h] * p.scale_log2 : kNegInf;
+    float pw[kMaxGroup];
+#pragma unroll
+    for (int h = 0; h < kMaxGroup; ++h) {
+      if (h >= G) { pw[h] = 0.f; continue; }
+      const float m_new = fmaxf(m_run[h], wave_max(s[h]));
+      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run[h] - m_use);
+      pw[h] = __builtin_amdgcn_exp2f(s[h] - m_use);
+      l_run[h] = l_run[h] * alpha + wave_sum(pw[h]);
+      m_run[h] = m_new;
+#pragma unroll
+      for (int u = 0; u < U; ++u) o[h][u] *= alpha;
+    }
+    const int nrows = min(64, end - blk);
+    for (int tt = 0; tt < nrows; ++tt) {
+      const int vt = __builtin_amdgcn_readlane((int)valid, tt);
+      if (!vt) continue;
+      const int rt = __builtin_amdgcn_readlane(row, tt);
+      const T* vrow = vb + (size_t)rt * D;
+      float v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = ld_f32<T>(vrow + lane + 64 * u);
+#pragma unroll
+      for (int h = 0; h < kMaxGroup; ++h) {
+        if (h >= G) continue;
+        const float pt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pw[h]), tt));
+#pragma unroll
+        for (int u = 0; u < U; ++u) o[h][u] += pt * v[u];
+      }
+    }
+  }
+  if constexpr (TOPK) {
+    if (p.flag && __any(bad) && lane == 0) atomicOr(p.flag, 2);
+  }
+
+#pragma unroll
+  for (int h = 0; h < kMaxGroup; ++h) {
+    if (h >= G) continue;
+    if (lane == 0) {
+      L.m[wave][h] = m_run[h];
+      L.l[wave][h] = l_run[h];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) L.o[wave][h][lane + 64 * u] = o[h][u];
+  }
+  __syncthreads();
+  finish_split<T, D>(p, b, j, split, nsplit, L);
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+static dim3 dense_grid(const DenseParams& p) {
+  return dim3((unsigned)((size_t)p.B * p.n_kv * p.P_max));
+}
+
+hipError_t launch_dense_mfma(const DenseParams& p, bool topk, hipStream_t s) {
+  if (topk)
+    hipLaunchKernelGGL(dense_mfma_kernel<true>, dense_grid(p), dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL(dense_mfma_kernel<false>, dense_grid(p), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+static void launch_generic_t(const DenseParams& p, bool topk, hipStream_t s) {
+  if (topk)
+    hipLaunchKernelGGL((dense_generic_kernel<T, D, true>), dense_grid(p), dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((dense_generic_kernel<T, D, false>), dense_grid(p), dim3(256), 0, s, p);
+}
+
+hipError_t launch_dense_generic(const DenseParams& p, int dtype, bool topk,
+                                hipStream_t s) {
+  const bool bf = dtype == 1;
+  if (p.d == 64) {
+    if (bf) launch_generic_t<uint16_t, 64>(p, topk, s);
+    else launch_generic_t<float, 64>(p, topk, s);
+  } else {
+    if (bf) launch_generic_t<uint16_t, 128>(p, topk, s);
+    else launch_generic_t<float, 128>(p, topk, s);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace kvc

@@ -1,0 +1,302 @@
+// Host side of the C ABI declared in include/kvc.h: argument checks (done
+// before any HIP runtime call, so they work on a machine with no GPU), the
+// split policy, workspace layout and kernel launches on the caller's stream.
+
+#include "kvc.h"
+
+#include <math.h>
+
+#include <atomic>
+
+#include "kvc_internal.h"
+
+using namespace kvc;
+
+namespace {
+
+std::atomic<int> g_split_override{0};
+
+constexpr int64_t kMaxOffset = (int64_t)1 << 31;
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int elem_bytes(int dtype) { return dtype == KVC_BF16 ? 2 : 4; }
+
+bool good_dtype(int dtype) { return dtype == KVC_F32 || dtype == KVC_BF16; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Workgroups the dense/top-k grid aims for: about 32 per compute unit of a
+// 256-CU MI355X, enough to hide a ragged tail without making splits tiny.
+constexpr int64_t kDenseTargetWgs = 8192;
+constexpr int kCUs = 256;
+
+int policy_split(int kind, int64_t B, int64_t units, int64_t n_max) {
+  const int gran = kind == KVC_KIND_MLA ? kMlaChunk : kDenseGran;
+  const int ov = g_split_override.load();
+  if (ov > 0) return (int)round_up((size_t)ov, (size_t)gran);
+  if (n_max < 1) n_max = 1;
+  if (units < 1) units = 1;  // empty batch: any valid split will do
+  if (kind == KVC_KIND_MLA) {
+    // A workgroup covers 64 heads and occupies a compute unit; aim for one
+    // workgroup per CU.  Each split's partial output costs n_h * d_c floats,
+    // so keep splits at least 256 positions long.  `units` counts
+    // (sequence, 64-head group) pairs.
+    int64_t P = ceil_div(kCUs, units);
+    if (P < 1) P = 1;
+    int64_t S = round_up((size_t)ceil_div(n_max, P), (size_t)gran);
+    if (S < 256) S = 256;
+    return (int)S;
+  }
+  int64_t S = gran;
+  while (units * ceil_div(n_max, S) > kDenseTargetWgs && S < ((int64_t)1 << 24))
+    S *= 2;
+  return (int)S;
+}
+
+int64_t splits_for(int64_t n_max, int S) { return n_max < 1 ? 1 : ceil_div(n_max, S); }
+
+struct DenseCheck {
+  int status;
+  int S;
+  int64_t P_max;
+  WsLayout ws;
+};
+
+DenseCheck check_dense_shape(int B, int n_h, int n_kv, int L_max, int d,
+                             int dtype, int K, bool topk) {
+  DenseCheck c{KVC_OK, 0, 1, {}};
+  if (!good_dtype(dtype)) { c.status = KVC_ERR_BAD_DTYPE; return c; }
+  if (B < 0 || n_h < 1 || n_kv < 1 || L_max < 1 || d < 1) {
+    c.status = KVC_ERR_BAD_SHAPE; return c;
+  }
+  if (n_h % n_kv != 0) { c.status = KVC_ERR_BAD_SHAPE; return c; }
+  if (topk && (K < 1 || K > L_max)) { c.status = KVC_ERR_BAD_SHAPE; return c; }
+  if ((int64_t)L_max * d * elem_bytes(dtype) >= kMaxOffset) {
+    c.status = KVC_ERR_BAD_SHAPE; return c;
+  }
+  if (d != 64 && d != 128) { c.status = KVC_ERR_UNSUPPORTED; return c; }
+  if (n_h / n_kv > kMaxGroup) { c.status = KVC_ERR_UNSUPPORTED; return c; }
+  const int64_t units = (int64_t)B * n_kv;
+  const int64_t n_max = topk ? K : L_max;
+  c.S = policy_split(topk ? KVC_KIND_TOPK : KVC_KIND_DENSE, B, units, n_max);
+  c.P_max = splits_for(n_max, c.S);
+  if (units * c.P_max >= kMaxOffset) { c.status = KVC_ERR_BAD_SHAPE; return c; }
+  c.ws = ws_layout((size_t)units, (size_t)B, (size_t)n_h, (size_t)c.P_max, (size_t)d);
+  return c;
+}
+
+int check_workspace(const WsLayout& ws, void* workspace, size_t ws_bytes) {
+  if (ws.total == 0) return KVC_OK;
+  if (!workspace) return KVC_ERR_NULL_PTR;
+  if (!aligned(workspace, 256)) return KVC_ERR_MISALIGNED;
+  if (ws_bytes < ws.total) return KVC_ERR_WORKSPACE;
+  return KVC_OK;
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? KVC_OK : KVC_ERR_HIP; }
+
+void fill_ws(DenseParams& p, const WsLayout& ws, void* workspace) {
+  if (ws.total == 0) {
+    p.ws_cnt = nullptr; p.ws_lse = nullptr; p.ws_o = nullptr;
+    return;
+  }
+  char* base = static_cast<char*>(workspace);
+  p.ws_cnt = reinterpret_cast<int32_t*>(base + ws.cnt_off);
+  p.ws_lse = reinterpret_cast<float*>(base + ws.lse_off);
+  p.ws_o = reinterpret_cast<float*>(base + ws.o_off);
+}
+
+struct MlaCheck {
+  int status;
+  int S;
+  int64_t P_max;
+  WsLayout ws;
+};
+
+MlaCheck check_mla_shape(int B, int n_h, int L_max, int d_c, int d_r, int dtype) {
+  MlaCheck c{KVC_OK, 0, 1, {}};
+  if (!good_dtype(dtype)) { c.status = KVC_ERR_BAD_DTYPE; return c; }
+  if (B < 0 || n_h < 1 || L_max < 1 || d_c < 1 || d_r < 0) {
+    c.status = KVC_ERR_BAD_SHAPE; return c;
+  }
+  if ((int64_t)L_max * (d_c + d_r) * elem_bytes(dtype) >= kMaxOffset) {
+    c.status = KVC_ERR_BAD_SHAPE; return c;
+  }
+  if (dtype != KVC_BF16 || d_c != kMlaDc || d_r != kMlaDr ||
+      n_h % kMlaHeadsPerWg != 0) {
+    c.status = KVC_ERR_UNSUPPORTED; return c;
+  }
+  c.S = policy_split(KVC_KIND_MLA, B, (int64_t)B * (n_h / kMlaHeadsPerWg), L_max);
+  c.P_max = splits_for(L_max, c.S);
+  const int64_t groups = n_h / kMlaHeadsPerWg;
+  if ((int64_t)B * groups * c.P_max >= kMaxOffset) { c.status = KVC_ERR_BAD_SHAPE; return c; }
+  c.ws = ws_layout((size_t)B * groups, (size_t)B, (size_t)n_h, (size_t)c.P_max, (size_t)d_c);
+  return c;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kvc_status_string(int status) {
+  switch (status) {
+    case KVC_OK: return "ok";
+    case KVC_ERR_NULL_PTR: return "a required pointer is NULL";
+    case KVC_ERR_BAD_SHAPE: return "bad shape (non-positive size, n_h % n_kv != 0, K out of range, or offsets beyond 2^31)";
+    case KVC_ERR_BAD_DTYPE: return "dtype must be KVC_F32 or KVC_BF16";
+    case KVC_ERR_UNSUPPORTED: return "shape or dtype has no kernel in this build";
+    case KVC_ERR_WORKSPACE: return "workspace smaller than the size query returned";
+    case KVC_ERR_MISALIGNED: return "pointer alignment rule broken";
+    case KVC_ERR_HIP: return "HIP launch error";
+    case KVC_ERR_BAD_ARG: return "bad argument (non-finite scale or negative override)";
+    default: return "unknown status";
+  }
+}
+
+int kvc_set_split_override(int positions) {
+  if (positions < 0) return KVC_ERR_BAD_ARG;
+  g_split_override.store(positions);
+  return KVC_OK;
+}
+
+int kvc_split_positions(int kind, int B, int units, int n_max) {
+  if (kind < KVC_KIND_DENSE || kind > KVC_KIND_MLA || B < 1 || units < 1)
+    return KVC_ERR_BAD_ARG;
+  return policy_split(kind, B, units, n_max);
+}
+
+int kvc_append(void* k_cache, void* v_cache, int32_t* seq_lens,
+               const void* k_new, const void* v_new, int B, int n_kv,
+               int L_max, int d, int dtype, int32_t* flag, void* stream) {
+  if (!good_dtype(dtype)) return KVC_ERR_BAD_DTYPE;
+  if (B < 0 || n_kv < 1 || L_max < 1 || d < 1) return KVC_ERR_BAD_SHAPE;
+  if ((int64_t)n_kv * d >= kMaxOffset) return KVC_ERR_BAD_SHAPE;
+  if (!k_cache || !seq_lens || !k_new) return KVC_ERR_NULL_PTR;
+  if ((v_cache == nullptr) != (v_new == nullptr)) return KVC_ERR_NULL_PTR;
+  if (!aligned(k_cache, 16) || !aligned(k_new, 16) ||
+      (v_cache && (!aligned(v_cache, 16) || !aligned(v_new, 16))) ||
+      !aligned(seq_lens, 4) || (flag && !aligned(flag, 4)))
+    return KVC_ERR_MISALIGNED;
+  if (B == 0) return KVC_OK;
+  AppendParams p{k_cache, v_cache, seq_lens, k_new, v_new, flag,
+                 B, n_kv, L_max, d, elem_bytes(dtype)};
+  return launch_status(launch_append(p, static_cast<hipStream_t>(stream)));
+}
+
+size_t kvc_decode_attn_workspace_size(int B, int n_h, int n_kv, int L_max,
+                                      int d, int dtype) {
+  const DenseCheck c = check_dense_shape(B, n_h, n_kv, L_max, d, dtype, 0, false);
+  return c.status == KVC_OK ? c.ws.total : 0;
+}
+
+size_t kvc_decode_attn_topk_workspace_size(int B, int n_h, int n_kv, int K,
+                                           int d, int dtype) {
+  // The workspace depends on K, not on L_max; any L_max >= K gives the same.
+  const DenseCheck c = check_dense_shape(B, n_h, n_kv, K < 1 ? 1 : K, d, dtype, K, true);
+  return c.status == KVC_OK ? c.ws.total : 0;
+}
+
+static int dense_common(const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* seq_lens, const int32_t* idx, int K,
+                        void* out, float* lse, int B, int n_h, int n_kv,
+                        int L_max, int d, float scale, int dtype, int32_t* flag,
+                        void* workspace, size_t ws_bytes, void* stream,
+                        bool topk) {
+  const DenseCheck c = check_dense_shape(B, n_h, n_kv, L_max, d, dtype, K, topk);
+  if (c.status != KVC_OK) return c.status;
+  if (!isfinite(scale)) return KVC_ERR_BAD_ARG;
+  if (!q || !k_cache || !v_cache || !seq_lens || !out || (topk && !idx))
+    return KVC_ERR_NULL_PTR;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(out, 16) || !aligned(seq_lens, 4) || (lse && !aligned(lse, 4)) ||
+      (idx && !aligned(idx, 16)) || (flag && !aligned(flag, 4)))
+    return KVC_ERR_MISALIGNED;
+  if (B == 0) return KVC_OK;
+  const int ws_status = check_workspace(c.ws, workspace, ws_bytes);
+  if (ws_status != KVC_OK) return ws_status;
+
+  DenseParams p{};
+  p.q = q; p.k = k_cache; p.v = v_cache; p.seq_lens = seq_lens;
+  p.idx = topk ? idx : nullptr; p.out = out; p.lse = lse;
+  p.flag = topk ? flag : nullptr;
+  fill_ws(p, c.ws, workspace);
+  p.B = B; p.n_h = n_h; p.n_kv = n_kv; p.G = n_h / n_kv; p.L_max = L_max;
+  p.d = d; p.K = topk ? K : 0; p.S = c.S; p.P_max = (int)c.P_max;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == KVC_BF16 && d == 128) return launch_status(launch_dense_mfma(p, topk, s));
+  return launch_status(launch_dense_generic(p, dtype, topk, s));
+}
+
+int kvc_decode_attn(const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* seq_lens, void* out, float* lse, int B,
+                    int n_h, int n_kv, int L_max, int d, float scale, int dtype,
+                    void* workspace, size_t ws_bytes, void* stream) {
+  return dense_common(q, k_cache, v_cache, seq_lens, nullptr, 0, out, lse, B,
+                      n_h, n_kv, L_max, d, scale, dtype, nullptr, workspace,
+                      ws_bytes, stream, false);
+}
+
+int kvc_decode_attn_topk(const void* q, const void* k_cache,
+                         const void* v_cache, const int32_t* seq_lens,
+                         const int32_t* idx, int K, void* out, float* lse,
+                         int B, int n_h, int n_kv, int L_max, int d,
+                         float scale, int dtype, int32_t* flag,
+                         void* workspace, size_t ws_bytes, void* stream) {
+  return dense_common(q, k_cache, v_cache, seq_lens, idx, K, out, lse, B, n_h,
+                      n_kv, L_max, d, scale, dtype, flag, workspace, ws_bytes,
+                      stream, true);
+}
+
+size_t kvc_decode_attn_mla_workspace_size(int B, int n_h, int L_max, int d_c,
+                                          int d_r, int dtype) {
+  const MlaCheck c = check_mla_shape(B, n_h, L_max, d_c, d_r, dtype);
+  return c.status == KVC_OK ? c.ws.total : 0;
+}
+
+int kvc_decode_attn_mla(const void* q, const void* ckv,
+                        const int32_t* seq_lens, void* out, float* lse, int B,
+                        int n_h, int L_max, int d_c, int d_r, float scale,
+                        int dtype, void* workspace, size_t ws_bytes,
+                        void* stream) {
+  const MlaCheck c = check_mla_shape(B, n_h, L_max, d_c, d_r, dtype);
+  if (c.status != KVC_OK) return c.status;
+  if (!isfinite(scale)) return KVC_ERR_BAD_ARG;
+  if (!q || !ckv || !seq_lens || !out) return KVC_ERR_NULL_PTR;
+  if (!aligned(q, 16) || !aligned(ckv, 16) || !aligned(out, 16) ||
+      !aligned(seq_lens, 4) || (lse && !aligned(lse, 4)))
+    return KVC_ERR_MISALIGNED;
+  if (B == 0) return KVC_OK;
+  const int ws_status = check_workspace(c.ws, workspace, ws_bytes);
+  if (ws_status != KVC_OK) return ws_status;
+  MlaParams p{};
+  p.q = q; p.ckv = ckv; p.seq_lens = seq_lens; p.out = out; p.lse = lse;
+  if (c.ws.total) {
+    char* base = static_cast<char*>(workspace);
+    p.ws_cnt = reinterpret_cast<int32_t*>(base + c.ws.cnt_off);
+    p.ws_lse = reinterpret_cast<float*>(base + c.ws.lse_off);
+    p.ws_o = reinterpret_cast<float*>(base + c.ws.o_off);
+  }
+  p.B = B; p.n_h = n_h; p.L_max = L_max; p.S = c.S; p.P_max = (int)c.P_max;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  return launch_status(launch_mla(p, static_cast<hipStream_t>(stream)));
+}
+
+size_t kvc_stream_read_sink_floats(size_t bytes) { return stream_read_blocks(bytes); }
+
+int kvc_stream_read(const void* src, size_t bytes, float* sink, void* stream) {
+  if (!src || !sink) return KVC_ERR_NULL_PTR;
+  if (bytes % 16 || !aligned(src, 16)) return KVC_ERR_MISALIGNED;
+  if (bytes == 0) return KVC_OK;
+  return launch_status(launch_stream_read(src, bytes, sink, static_cast<hipStream_t>(stream)));
+}
+
+int kvc_copy(void* dst, const void* src, size_t bytes, void* stream) {
+  if (!src || !dst) return KVC_ERR_NULL_PTR;
+  if (bytes % 16 || !aligned(src, 16) || !aligned(dst, 16)) return KVC_ERR_MISALIGNED;
+  if (bytes == 0) return KVC_OK;
+  return launch_status(launch_copy(dst, src, bytes, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

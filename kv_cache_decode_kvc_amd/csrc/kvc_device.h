@@ -1,0 +1,71 @@
+// Device helpers for gfx950 (CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvc {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer resource word 3 for gfx9-family raw buffers: 32-bit data format,
+// no swizzle.  Accesses at offsets >= num_records return zero, which is how
+// the kernels keep reads inside one sequence's valid rows.
+constexpr int kBufWord3 = 0x00020000;
+constexpr uint32_t kOobOffset = 0x80000000u;
+
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base,
+                                                   uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                           (int)bytes, kBufWord3);
+}
+
+__device__ inline u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4,
+                            __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+__device__ inline bf16x8 as_bf16x8(u32x4 x) {
+  return __builtin_bit_cast(bf16x8, x);
+}
+
+// float -> bf16 round to nearest even (hardware conversion on gfx950).
+__device__ inline uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ inline uint16_t to_bf16_bits(float x) {
+  return __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+
+__device__ inline float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ inline float bf16_hi(uint32_t u) {
+  return __uint_as_float(u & 0xFFFF0000u);
+}
+
+__device__ inline float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+
+__device__ inline float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kLn2 = 0.693147180559945309f;
+
+// exp2 of (x - m) where m may be -inf (then every x is -inf too): 0.
+__device__ inline float exp2_rel(float x, float m_use) {
+  return __builtin_amdgcn_exp2f(x - m_use);
+}
+
+}  // namespace kvc

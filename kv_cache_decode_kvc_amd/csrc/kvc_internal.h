@@ -1,0 +1,98 @@
+// Internal declarations shared by the host API and the kernel sources.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+namespace kvc {
+
+// Positions one wave consumes per step of the MFMA dense kernel, and the
+// split granularity of dense / top-k decode (4 waves x 32 positions).
+constexpr int kDenseChunk = 32;
+constexpr int kDenseGran = 128;
+constexpr int kMaxGroup = 16;        // query heads per KV head a kernel serves
+// MLA kernel: positions per step (also the split granularity); a workgroup
+// of 4 waves covers 64 heads, two waves sharing each 32 heads.
+constexpr int kMlaChunk = 32;
+constexpr int kMlaHeadsPerWave = 32;
+constexpr int kMlaWaves = 4;
+constexpr int kMlaHeadsPerWg = 64;
+constexpr int kMlaDc = 512;
+constexpr int kMlaDr = 64;
+
+struct AppendParams {
+  void* k_cache;
+  void* v_cache;          // may be null
+  int32_t* seq_lens;
+  const void* k_new;
+  const void* v_new;      // may be null
+  int32_t* flag;          // may be null
+  int B, n_kv, L_max, d, elem_bytes;
+};
+
+// Dense and top-k decode.  Workspace pointers are null when P_max == 1.
+struct DenseParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* seq_lens;
+  const int32_t* idx;     // top-k only
+  void* out;
+  float* lse;             // may be null
+  int32_t* flag;          // may be null (top-k only)
+  int32_t* ws_cnt;        // [B * n_kv] completion tickets
+  float* ws_lse;          // [B * n_h * P_max] log2-domain partial lse
+  float* ws_o;            // [B * n_h * P_max * d] normalised partial outputs
+  int B, n_h, n_kv, G, L_max, d;
+  int K;                  // top-k list length (0 for dense)
+  int S;                  // positions per split
+  int P_max;              // splits per (b, kv head) in the grid
+  float scale_log2;       // scale * log2(e)
+};
+
+struct MlaParams {
+  const void* q;
+  const void* ckv;
+  const int32_t* seq_lens;
+  void* out;
+  float* lse;
+  int32_t* ws_cnt;        // [B]
+  float* ws_lse;          // [B * n_h * P_max]
+  float* ws_o;            // [B * n_h * P_max * d_c]
+  int B, n_h, L_max;
+  int S, P_max;
+  float scale_log2;
+};
+
+struct WsLayout {
+  size_t cnt_off, lse_off, o_off, total;
+};
+
+inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+inline WsLayout ws_layout(size_t units, size_t B, size_t n_h, size_t P_max,
+                          size_t d) {
+  WsLayout w{};
+  if (P_max <= 1) return w;
+  w.cnt_off = 0;
+  w.lse_off = round_up(units * sizeof(int32_t), 256);
+  w.o_off = w.lse_off + round_up(B * n_h * P_max * sizeof(float), 256);
+  w.total = w.o_off + B * n_h * P_max * d * sizeof(float);
+  return w;
+}
+
+// Kernel launchers (defined in the .hip sources).
+hipError_t launch_append(const AppendParams& p, hipStream_t s);
+hipError_t launch_dense_mfma(const DenseParams& p, bool topk, hipStream_t s);
+hipError_t launch_dense_generic(const DenseParams& p, int dtype, bool topk,
+                                hipStream_t s);
+hipError_t launch_mla(const MlaParams& p, hipStream_t s);
+hipError_t launch_stream_read(const void* src, size_t bytes, float* sink,
+                              hipStream_t s);
+hipError_t launch_copy(void* dst, const void* src, size_t bytes,
+                       hipStream_t s);
+size_t stream_read_blocks(size_t bytes);
+
+}  // namespace kvc

@@ -1,0 +1,157 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/kvc.h declares, and rejects bad arguments before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import kv_cache_decode_kvc_amd as kvc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvc.h")
+
+# fake, never-dereferenced device addresses with chosen alignment
+A16 = ctypes.c_void_p(0x10000)
+A4 = ctypes.c_void_p(0x10004)
+A8 = ctypes.c_void_p(0x10008)
+NULL = None
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvc_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return kvc.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared_functions()
+    assert len(names) >= 13
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    for code in range(-8, 1):
+        assert kvc.kvc_status_string(code)
+    assert kvc.kvc_status_string(-99) == "unknown status"
+
+
+def dense(L, **kw):
+    a = dict(q=A16, k=A16, v=A16, sl=A4, out=A16, lse=NULL, B=2, n_h=8, n_kv=2,
+             L_max=64, d=128, scale=0.1, dt=kvc.KVC_BF16, ws=A16, wsb=1 << 30,
+             stream=NULL)
+    a.update(kw)
+    return L.kvc_decode_attn(a["q"], a["k"], a["v"], a["sl"], a["out"], a["lse"],
+                             a["B"], a["n_h"], a["n_kv"], a["L_max"], a["d"],
+                             a["scale"], a["dt"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_dense_validation(L):
+    assert dense(L, q=NULL) == -1
+    assert dense(L, sl=NULL) == -1
+    assert dense(L, n_h=7) == -2                  # n_h % n_kv
+    assert dense(L, L_max=0) == -2
+    assert dense(L, B=-1) == -2
+    assert dense(L, dt=5) == -3
+    assert dense(L, d=96) == -4
+    assert dense(L, n_h=34, n_kv=2) == -4         # group of 17 > 16
+    assert dense(L, L_max=1 << 23) == -2          # 2^23 * 256 B >= 2^31
+    assert dense(L, q=A8) == -6
+    assert dense(L, out=A4) == -6
+    assert dense(L, scale=float("nan")) == -8
+    assert dense(L, scale=float("inf")) == -8
+    assert dense(L, B=0) == 0                     # empty batch: nothing to do
+
+
+def test_dense_workspace_rules(L):
+    need = L.kvc_decode_attn_workspace_size(4, 64, 8, 32768, 128, kvc.KVC_BF16)
+    assert need > 0
+    assert dense(L, B=4, n_h=64, n_kv=8, L_max=32768, ws=NULL, wsb=need) == -1
+    assert dense(L, B=4, n_h=64, n_kv=8, L_max=32768, wsb=need - 1) == -5
+    assert dense(L, B=4, n_h=64, n_kv=8, L_max=32768, ws=ctypes.c_void_p(0x10010), wsb=need) == -6
+    # a single split needs no workspace
+    assert L.kvc_decode_attn_workspace_size(1, 8, 2, 64, 64, kvc.KVC_F32) == 0
+    assert L.kvc_decode_attn_workspace_size(1, 8, 2, 64, 96, kvc.KVC_F32) == 0  # unsupported -> 0
+
+
+def test_split_policy_and_override(L):
+    S = kvc.kvc_split_positions(kvc.KVC_KIND_DENSE, 32, 256, 32768)
+    assert S % 128 == 0 and 256 * -(-32768 // S) <= 8192
+    assert kvc.kvc_split_positions(kvc.KVC_KIND_DENSE, 1, 32, 4097) == 128
+    Sm = kvc.kvc_split_positions(kvc.KVC_KIND_MLA, 64, 128, 8193)
+    assert Sm % 32 == 0 and Sm >= 256
+    try:
+        kvc.kvc_set_split_override(300)
+        assert kvc.kvc_split_positions(kvc.KVC_KIND_DENSE, 1, 1, 1000) == 384
+        assert kvc.kvc_split_positions(kvc.KVC_KIND_MLA, 1, 1, 1000) == 320
+    finally:
+        kvc.kvc_set_split_override(0)
+    assert L.kvc_set_split_override(-1) == -8
+    assert L.kvc_split_positions(7, 1, 1, 1) == -8
+
+
+def test_append_validation(L):
+    def ap(**kw):
+        a = dict(k=A16, v=A16, sl=A4, kn=A16, vn=A16, B=2, n_kv=2, L_max=8, d=64,
+                 dt=kvc.KVC_BF16, flag=NULL, stream=NULL)
+        a.update(kw)
+        return L.kvc_append(a["k"], a["v"], a["sl"], a["kn"], a["vn"], a["B"],
+                            a["n_kv"], a["L_max"], a["d"], a["dt"], a["flag"], a["stream"])
+    assert ap(k=NULL) == -1
+    assert ap(v=NULL) == -1          # v_cache NULL needs v_new NULL
+    assert ap(vn=NULL) == -1
+    assert ap(dt=2) == -3
+    assert ap(d=0) == -2
+    assert ap(k=A8) == -6
+    assert ap(sl=ctypes.c_void_p(0x10002)) == -6
+    assert ap(B=0) == 0
+
+
+def test_mla_validation(L):
+    def ml(**kw):
+        a = dict(q=A16, c=A16, sl=A4, out=A16, lse=NULL, B=2, n_h=128, L_max=100,
+                 d_c=512, d_r=64, scale=1 / 24, dt=kvc.KVC_BF16, ws=A16, wsb=1 << 30,
+                 stream=NULL)
+        a.update(kw)
+        return L.kvc_decode_attn_mla(a["q"], a["c"], a["sl"], a["out"], a["lse"], a["B"],
+                                     a["n_h"], a["L_max"], a["d_c"], a["d_r"], a["scale"],
+                                     a["dt"], a["ws"], a["wsb"], a["stream"])
+    assert ml(c=NULL) == -1
+    assert ml(dt=kvc.KVC_F32) == -4
+    assert ml(d_c=256) == -4
+    assert ml(n_h=96) == -4
+    assert ml(n_h=0) == -2
+    assert ml(out=A8) == -6
+    assert ml(scale=float("nan")) == -8
+    assert ml(B=0) == 0
+    assert L.kvc_decode_attn_mla_workspace_size(64, 128, 8193, 512, 64, kvc.KVC_BF16) > 0
+
+
+def test_topk_validation(L):
+    def tk(**kw):
+        a = dict(q=A16, k=A16, v=A16, sl=A4, idx=A16, K=16, out=A16, lse=NULL, B=2,
+                 n_h=8, n_kv=2, L_max=64, d=128, scale=0.1, dt=kvc.KVC_BF16,
+                 flag=NULL, ws=A16, wsb=1 << 30, stream=NULL)
+        a.update(kw)
+        return L.kvc_decode_attn_topk(a["q"], a["k"], a["v"], a["sl"], a["idx"], a["K"],
+                                      a["out"], a["lse"], a["B"], a["n_h"], a["n_kv"],
+                                      a["L_max"], a["d"], a["scale"], a["dt"], a["flag"],
+                                      a["ws"], a["wsb"], a["stream"])
+    assert tk(idx=NULL) == -1
+    assert tk(K=0) == -2
+    assert tk(K=65) == -2
+    assert tk(idx=A8) == -6
+    assert tk(B=0) == 0
+
+
+def test_diag_validation(L):
+    assert L.kvc_stream_read(NULL, 16, A16, NULL) == -1
+    assert L.kvc_stream_read(A16, 8, A16, NULL) == -6
+    assert L.kvc_copy(A16, A8, 16, NULL) == -6
+    assert L.kvc_copy(A16, A16, 0, NULL) == 0
