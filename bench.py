@@ -319,6 +319,18 @@ def measure(name, args, torch, kvc):
     return wl, res
 
 
+def calibrate_copy(torch, kvc, nbytes=1 << 30):
+    """One plain copy of known size: hardware byte counters (FETCH_SIZE,
+    WRITE_SIZE) read for this dispatch scale the attention kernels' counts."""
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    kvc.kvc_copy(dst, src)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
+
+
 def read_ceiling(torch, kvc, nbytes=4 << 30, reps=10):
     buf = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda")
     buf.fill_(1.0)
@@ -391,6 +403,7 @@ def main():
     del wl
     torch.cuda.empty_cache()
 
+    calibrate_copy(torch, kvc)
     line["read_ceiling_gbs"] = round(read_ceiling(torch, kvc), 1)
     also = {}
     for name in [x for x in args.others.split(",") if x and x != args.config]:

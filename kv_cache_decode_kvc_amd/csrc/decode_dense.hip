@@ -26,7 +26,10 @@ namespace kvc {
 // ---------------------------------------------------------------------------
 template <int D>
 struct MergeLds {
-  float o[4][kMaxGroup][D];
+  union {
+    float o[4][kMaxGroup][D];          // per-wave accumulators
+    float w[kMaxGroup][kMaxSplits];    // split lse values while merging
+  };
   float m[4][kMaxGroup];
   float l[4][kMaxGroup];
   int last;
@@ -116,35 +119,59 @@ __device__ void finish_split(const DenseParams& p, int b, int j, int split,
     return;
   }
 
-  // Several splits: publish this one, then the last to arrive merges.
+  // Several splits: publish this one (device-coherent stores), then the
+  // last workgroup to take a ticket merges all of them.
+  const __amdgpu_buffer_rsrc_t wo = make_rsrc(p.ws_o, kWsRecords);
+  const __amdgpu_buffer_rsrc_t wl = make_rsrc(p.ws_lse, kWsRecords);
   const size_t slot = bh * p.P_max + split;
   if (active) {
-    store_row<float, CPT>(p.ws_o + slot * D + c0, o);
-    if ((t & 15) == 0) p.ws_lse[slot] = lse2;
+#pragma unroll
+    for (int c = 0; c < CPT; c += 4)
+      store_coherent(wo, (uint32_t)((slot * D + c0 + c) * 4),
+                     f32x4{o[c], o[c + 1], o[c + 2], o[c + 3]});
+    if ((t & 15) == 0) store_coherent(wl, (uint32_t)(slot * 4), lse2);
   }
-  __threadfence();
+  wait_vm_all();
   __syncthreads();
   int32_t* ticket = p.ws_cnt + (size_t)b * p.n_kv + j;
   if (t == 0) L.last = (atomicAdd(ticket, 1) == nsplit - 1);
   __syncthreads();
   if (!L.last) return;
-  __threadfence();
 
+  // Last workgroup: stage the split lse values of the G heads in LDS (all
+  // loads in flight together), then sum the partial rows in batches of 4.
+  const size_t bh0 = (size_t)b * p.n_h + (size_t)j * p.G;
+  for (int e = t; e < p.G * nsplit; e += blockDim.x) {
+    const int h2 = e / nsplit, s = e - h2 * nsplit;
+    L.w[h2][s] = load_coherent1(wl, (uint32_t)(((bh0 + h2) * p.P_max + s) * 4));
+  }
+  __syncthreads();
   if (active) {
-    const float* lp = p.ws_lse + bh * p.P_max;
-    const float* op = p.ws_o + bh * p.P_max * D + c0;
+    const size_t base = bh * p.P_max;
     float M = kNegInf;
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, lp[s]);
+    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, L.w[hl][s]);
     const float Mu = (M == kNegInf) ? 0.f : M;
     float Z = 0.f;
 #pragma unroll
     for (int c = 0; c < CPT; ++c) o[c] = 0.f;
-    for (int s = 0; s < nsplit; ++s) {
-      const float e = __builtin_amdgcn_exp2f(lp[s] - Mu);
-      Z += e;
-      const float* row = op + (size_t)s * D;
+    for (int s0 = 0; s0 < nsplit; s0 += 4) {
+      f32x4 v[4][CPT / 4];
 #pragma unroll
-      for (int c = 0; c < CPT; ++c) o[c] += e * row[c];
+      for (int u = 0; u < 4; ++u) {
+        const int su = min(s0 + u, nsplit - 1);
+#pragma unroll
+        for (int c = 0; c < CPT / 4; ++c)
+          v[u][c] = load_coherent4(wo, (uint32_t)(((base + su) * D + c0 + 4 * c) * 4));
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float e = (s0 + u < nsplit) ? __builtin_amdgcn_exp2f(L.w[hl][s0 + u] - Mu) : 0.f;
+        Z += e;
+#pragma unroll
+        for (int c = 0; c < CPT / 4; ++c)
+#pragma unroll
+          for (int k = 0; k < 4; ++k) o[4 * c + k] += e * v[u][c][k];
+      }
     }
     const float inv = Z > 0.f ? 1.f / Z : 0.f;
 #pragma unroll
@@ -199,11 +226,11 @@ __device__ inline void load_chunk(Chunk& c, int cs, int end, int n,
       const uint32_t row = cs + (r >> 2) * 8 + a * 4 + (r & 3);
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
-        c.k[a][kk] = buf_load16(kr, row * kRow + kk * 64 + g * 16);
+        c.k[a][kk] = buf_load16_stream(kr, row * kRow + kk * 64 + g * 16);
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e)
-      c.v[e] = buf_load16(vr, (uint32_t)(cs + g * 8 + e) * kRow + r * 16);
+      c.v[e] = buf_load16_stream(vr, (uint32_t)(cs + g * 8 + e) * kRow + r * 16);
     c.vmask = 0xFF;
   } else {
     // slots for the V rows: cs + g*8 + 0..7; for the K rows: cs + pi(a, r).
@@ -219,7 +246,7 @@ __device__ inline void load_chunk(Chunk& c, int cs, int end, int n,
       if (in_list && !ok) bad = true;
       const bool use = in_list && ok;
       mask |= (use ? 1u : 0u) << e;
-      c.v[e] = buf_load16(vr, use ? iv[e] * kRow + r * 16 : kOobOffset);
+      c.v[e] = buf_load16_stream(vr, use ? iv[e] * kRow + r * 16 : kOobOffset);
     }
     c.vmask = mask;
 #pragma unroll
@@ -229,7 +256,7 @@ __device__ inline void load_chunk(Chunk& c, int cs, int end, int n,
       const bool use = slot < end && t < (uint32_t)n;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
-        c.k[a][kk] = buf_load16(kr, use ? t * kRow + kk * 64 + g * 16 : kOobOffset);
+        c.k[a][kk] = buf_load16_stream(kr, use ? t * kRow + kk * 64 + g * 16 : kOobOffset);
     }
   }
 }
@@ -262,9 +289,12 @@ __device__ inline void compute_chunk(const Chunk& c, int cs, int end,
   }
   mx = fmaxf(mx, __shfl_xor(mx, 16));
   mx = fmaxf(mx, __shfl_xor(mx, 32));
-  const float m_new = fmaxf(st.m, mx);
+  // Lazy reference max: move it (and rescale) only when this chunk would
+  // push weights above 2^kRescaleMargin.
+  const bool move = mx > st.m + kRescaleMargin;
+  const float m_new = move ? mx : st.m;
+  const float alpha = (move && st.m != kNegInf) ? __builtin_amdgcn_exp2f(st.m - m_new) : 1.f;
   const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-  const float alpha = __builtin_amdgcn_exp2f(st.m - m_use);
   st.m = m_new;
   if (__any(alpha != 1.f)) {
 #pragma unroll
@@ -479,9 +509,11 @@ __global__ __launch_bounds__(256) void dense_generic_kernel(DenseParams p) {
 #pragma unroll
     for (int h = 0; h < kMaxGroup; ++h) {
       if (h >= G) { pw[h] = 0.f; continue; }
-      const float m_new = fmaxf(m_run[h], wave_max(s[h]));
+      const float mx = wave_max(s[h]);
+      const bool move = mx > m_run[h] + kRescaleMargin;
+      const float m_new = move ? mx : m_run[h];
       const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run[h] - m_use);
+      const float alpha = (move && m_run[h] != kNegInf) ? __builtin_amdgcn_exp2f(m_run[h] - m_new) : 1.f;
       pw[h] = __builtin_amdgcn_exp2f(s[h] - m_use);
       l_run[h] = l_run[h] * alpha + wave_sum(pw[h]);
       m_run[h] = m_new;

@@ -64,7 +64,7 @@ __device__ inline void issue_tile(char* stage, __amdgpu_buffer_rsrc_t cr,
   for (int k = 0; k < kLoadsPerWave; ++k) {
     const int blk = wave * kLoadsPerWave + k;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        cr, (lds_void*)(stage + blk * 1024), 16, goff[k], cs * kRowB, 0, 0);
+        cr, (lds_void*)(stage + blk * 1024), 16, goff[k], cs * kRowB, 0, kStream);
   }
 }
 
@@ -146,15 +146,18 @@ __global__ __launch_bounds__(256, 1) void mla_kernel(MlaParams p) {
     goff[k] = (uint32_t)(rho * kRowB + ((pc ^ (rho & 7)) << 4));
   }
   // LDS read bases.  Scores: row r, logical chunk q = 2kk + g, stored at
-  // 8*(q/8) + ((q & 7) ^ (r & 7)), so k-steps kk and kk+4 differ by 128
-  // bytes: four bases cover all k-steps.  Values: row
-  // rho = 8*(2ks + jj/4) + 4g + (jj & 3) has rho & 7 = 4g + (jj & 3), and
-  // logical chunk 32h + r (this half's columns r*8..r*8+7) lands at
+  // 8*(q/8) + ((q & 7) ^ (r & 7)).  This wave's k-steps are kk = 18h + k;
+  // writing k = 4a + u and x = 2h + u gives kk & 3 = x & 3 and
+  // kk >> 2 = 4h + a + (x >> 2), so four per-wave bases plus a*128 cover
+  // every k-step.  Values: row rho = 8*(2ks + jj/4) + 4g + (jj & 3) has
+  // rho & 7 = 4g + (jj & 3); this half's chunk 32h + r sits at
   // 32h + (r ^ (4g + (jj & 3))): four bases plus constants.
-  uint32_t qk_base[4], pv_base[4];
+  uint32_t wqk[4], pv_base[4];
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
-    qk_base[v] = (uint32_t)(r * kRowB + (((2 * v + g) ^ (r & 7)) << 4));
+    const int x = 2 * half + v;
+    wqk[v] = (uint32_t)(r * kRowB + (((2 * (x & 3) + g) ^ (r & 7)) << 4) +
+                        (4 * half + (x >> 2)) * 128);
     const int y = 4 * g + v;
     pv_base[v] = (uint32_t)(y * kRowB + ((r ^ y) << 4) + half * 512);
   }
@@ -189,19 +192,38 @@ __global__ __launch_bounds__(256, 1) void mla_kernel(MlaParams p) {
     if (c + 2 < nchunks)
       issue_tile(smem + ((c + 2) % kStages) * kTileB, cr,
                  start + (c + 2) * kMlaChunk, wave, goff);
-    const char* tile = smem + (c % kStages) * kTileB;
     const int cs = start + c * kMlaChunk;
+    // This chunk's LDS bases, materialised once per chunk so that every read
+    // below is base + constant (the constant goes in the instruction).
+    const uint32_t toff = (uint32_t)((c % kStages) * kTileB);
+    uint32_t qb[4], pb[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      qb[v] = toff + wqk[v];
+      pb[v] = toff + pv_base[v];
+      asm volatile("" : "+v"(qb[v]), "+v"(pb[v]));
+    }
 
-    // this half's score contribution
+    // this half's score contribution; LDS reads run four k-steps ahead
     f32x16 sacc;
 #pragma unroll
     for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
+    u32x4 A[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) A[k] = lds_load16(smem, qb[k & 3] + (k >> 2) * 128);
 #pragma unroll
     for (int k = 0; k < kKHalf; ++k) {
-      const int kk = half * kKHalf + k;
-      const u32x4 a = lds_load16(tile, qk_base[kk & 3] + (kk >> 2) * 128);
-      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), qop[k], sacc, 0, 0, 0);
+      sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(A[k & 3]), qop[k], sacc, 0, 0, 0);
+      if (k + 4 < kKHalf) A[k & 3] = lds_load16(smem, qb[(k + 4) & 3] + ((k + 4) >> 2) * 128);
     }
+    // value rows of both k-steps, read while the scores are exchanged
+    u32x4 vr[2][8];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj)
+        vr[ks][jj] = lds_load16(smem, pb[jj & 3] + (8 * (2 * ks + (jj >> 2))) * kRowB);
+
     // add the other half's contribution
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4)
@@ -214,7 +236,8 @@ __global__ __launch_bounds__(256, 1) void mla_kernel(MlaParams p) {
       for (int e = 0; e < 4; ++e) sacc[4 * q4 + e] += o[e];
     }
 
-    // online softmax over this lane's 16 positions of head r
+    // online softmax over this lane's 16 positions of head r, with a lazy
+    // reference max (moved only when weights would exceed 2^kRescaleMargin)
     float sv[16];
     float mx = kNegInf;
 #pragma unroll
@@ -224,9 +247,10 @@ __global__ __launch_bounds__(256, 1) void mla_kernel(MlaParams p) {
       mx = fmaxf(mx, sv[i]);
     }
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
+    const bool move = mx > m_run + kRescaleMargin;
+    const float m_new = move ? mx : m_run;
+    const float alpha = (move && m_run != kNegInf) ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
     const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
     m_run = m_new;
     if (__any(alpha != 1.f)) {
 #pragma unroll
@@ -247,19 +271,15 @@ __global__ __launch_bounds__(256, 1) void mla_kernel(MlaParams p) {
     for (int ks = 0; ks < 2; ++ks) {
       const u32x4 pv = {pp[4 * ks], pp[4 * ks + 1], pp[4 * ks + 2], pp[4 * ks + 3]};
       const bf16x8 pop = as_bf16x8(pv);
-      u32x4 vr[8];
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj)
-        vr[jj] = lds_load16(tile, pv_base[jj & 3] + (8 * (2 * ks + (jj >> 2))) * kRowB);
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
         const uint32_t sel = (m & 1) ? 0x07060302u : 0x05040100u;
         const int dw = m >> 1;
         u32x4 a;
-        a[0] = __builtin_amdgcn_perm(vr[1][dw], vr[0][dw], sel);
-        a[1] = __builtin_amdgcn_perm(vr[3][dw], vr[2][dw], sel);
-        a[2] = __builtin_amdgcn_perm(vr[5][dw], vr[4][dw], sel);
-        a[3] = __builtin_amdgcn_perm(vr[7][dw], vr[6][dw], sel);
+        a[0] = __builtin_amdgcn_perm(vr[ks][1][dw], vr[ks][0][dw], sel);
+        a[1] = __builtin_amdgcn_perm(vr[ks][3][dw], vr[ks][2][dw], sel);
+        a[2] = __builtin_amdgcn_perm(vr[ks][5][dw], vr[ks][4][dw], sel);
+        a[3] = __builtin_amdgcn_perm(vr[ks][7][dw], vr[ks][6][dw], sel);
         acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), pop, acc[m], 0, 0, 0);
       }
     }
@@ -285,8 +305,12 @@ __global__ __launch_bounds__(256, 1) void mla_kernel(MlaParams p) {
     return;
   }
 
+  // Several splits: publish this one with device-coherent stores; the last
+  // workgroup of the (sequence, head group) to take a ticket merges them.
+  const __amdgpu_buffer_rsrc_t wo = make_rsrc(p.ws_o, kWsRecords);
+  const __amdgpu_buffer_rsrc_t wl = make_rsrc(p.ws_lse, kWsRecords);
   {
-    float* o = p.ws_o + (bh * p.P_max + split) * kMlaDc;
+    const size_t row = (bh * p.P_max + split) * kMlaDc;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int c0 = col0 + (8 * (i >> 2) + 4 * g + (i & 3)) * 8;
@@ -296,40 +320,58 @@ __global__ __launch_bounds__(256, 1) void mla_kernel(MlaParams p) {
         v0[e] = acc[e][i] * inv;
         v1[e] = acc[4 + e][i] * inv;
       }
-      *reinterpret_cast<f32x4*>(o + c0) = v0;
-      *reinterpret_cast<f32x4*>(o + c0 + 4) = v1;
+      store_coherent(wo, (uint32_t)((row + c0) * 4), v0);
+      store_coherent(wo, (uint32_t)((row + c0 + 4) * 4), v1);
     }
-    if (half == 0 && g == 0) p.ws_lse[bh * p.P_max + split] = lse2;
+    if (half == 0 && g == 0) store_coherent(wl, (uint32_t)((bh * p.P_max + split) * 4), lse2);
   }
-  __threadfence();
+  wait_vm_all();
   __syncthreads();
   int32_t* ticket = p.ws_cnt + (size_t)b * groups + hg;
   if (tid == 0) s_last = (atomicAdd(ticket, 1) == nsplit - 1);
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
 
-  // Last split to finish merges every split of the 64 heads.  Thread t takes
-  // columns (t % 64) * 8 .. +8 of heads t / 64, t / 64 + 4, ...
+  // Last split to finish merges every split of the 64 heads.  The split
+  // lse values go to LDS first (the tile stages are free now), all loads in
+  // flight together; then thread t sums columns (t % 64) * 8 .. +8 of heads
+  // t / 64, t / 64 + 4, ... over the splits in batches of 4.
+  float* wsm = reinterpret_cast<float*>(smem);
+  const size_t bh0 = (size_t)b * p.n_h + hg * kMlaHeadsPerWg;
+  for (int e = tid; e < kMlaHeadsPerWg * nsplit; e += blockDim.x) {
+    const int h2 = e / nsplit, s = e - h2 * nsplit;
+    wsm[e] = load_coherent1(wl, (uint32_t)(((bh0 + h2) * p.P_max + s) * 4));
+  }
+  __syncthreads();
   const int c0 = (tid & 63) * 8;
   for (int hl = tid >> 6; hl < kMlaHeadsPerWg; hl += 4) {
-    const size_t bhh = (size_t)b * p.n_h + hg * kMlaHeadsPerWg + hl;
-    const float* lp = p.ws_lse + bhh * p.P_max;
+    const size_t bhh = bh0 + hl;
+    const size_t base = bhh * p.P_max;
+    const float* lw = wsm + hl * nsplit;
     float M = kNegInf;
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, lp[s]);
+    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, lw[s]);
     const float Mu = (M == kNegInf) ? 0.f : M;
     float Z = 0.f, o[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = 0.f;
-    for (int s = 0; s < nsplit; ++s) {
-      const float w = __builtin_amdgcn_exp2f(lp[s] - Mu);
-      Z += w;
-      const f32x4* row = reinterpret_cast<const f32x4*>(p.ws_o + (bhh * p.P_max + s) * kMlaDc + c0);
-      const f32x4 a = row[0], bq = row[1];
+    for (int s0 = 0; s0 < nsplit; s0 += 4) {
+      f32x4 va[4], vb[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        o[e] += w * a[e];
-        o[4 + e] += w * bq[e];
+      for (int u = 0; u < 4; ++u) {
+        const int su = min(s0 + u, nsplit - 1);
+        const uint32_t off = (uint32_t)(((base + su) * kMlaDc + c0) * 4);
+        va[u] = load_coherent4(wo, off);
+        vb[u] = load_coherent4(wo, off + 16);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float w = (s0 + u < nsplit) ? __builtin_amdgcn_exp2f(lw[s0 + u] - Mu) : 0.f;
+        Z += w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          o[e] += w * va[u][e];
+          o[4 + e] += w * vb[u][e];
+        }
       }
     }
     const float zi = Z > 0.f ? 1.f / Z : 0.f;

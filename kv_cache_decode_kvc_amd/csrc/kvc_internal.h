@@ -13,6 +13,13 @@ namespace kvc {
 constexpr int kDenseChunk = 32;
 constexpr int kDenseGran = 128;
 constexpr int kMaxGroup = 16;        // query heads per KV head a kernel serves
+// Upper bound on the splits of one sequence (the merge stages their weights
+// in LDS); the split policy raises the split size to respect it.
+constexpr int kMaxSplits = 256;
+// Online softmax: the reference max moves only when a chunk's max exceeds it
+// by this much (log2 units), so weights stay <= 2^8 and rescaling of the
+// accumulators is rare.  The result is the same; only rounding differs.
+constexpr float kRescaleMargin = 8.0f;
 // MLA kernel: positions per step (also the split granularity); a workgroup
 // of 4 waves covers 64 heads, two waves sharing each 32 heads.
 constexpr int kMlaChunk = 32;

@@ -82,8 +82,10 @@ def test_dense_workspace_rules(L):
 
 def test_split_policy_and_override(L):
     S = kvc.kvc_split_positions(kvc.KVC_KIND_DENSE, 32, 256, 32768)
-    assert S % 128 == 0 and 256 * -(-32768 // S) <= 8192
-    assert kvc.kvc_split_positions(kvc.KVC_KIND_DENSE, 1, 32, 4097) == 128
+    assert S % 128 == 0 and 256 * -(-32768 // S) <= 4608
+    assert kvc.kvc_split_positions(kvc.KVC_KIND_DENSE, 1, 32, 4097) == 256
+    # at most 256 splits per sequence
+    assert kvc.kvc_split_positions(kvc.KVC_KIND_DENSE, 1, 1, 1 << 20) >= (1 << 20) // 256
     Sm = kvc.kvc_split_positions(kvc.KVC_KIND_MLA, 64, 128, 8193)
     assert Sm % 32 == 0 and Sm >= 256
     try:
