@@ -124,6 +124,31 @@ int kvc_decode_attn(const void* q, const void* k_cache, const void* v_cache,
                     int dtype, void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * kvc_append_decode_attn - kvc_append followed by kvc_decode_attn, in one
+ * kernel launch.  (Podcast transcript, decode walk-through: the new token's
+ * pair is appended and the token attends over the cache including it.)
+ *
+ * For each b with n = seq_lens[b] in [0, L_max): k_new[b]/v_new[b] are
+ * written at slot n, every query head attends over [0, n + 1), and
+ * seq_lens[b] becomes n + 1.  If n is outside [0, L_max) nothing is written,
+ * the head attends over [0, clamp(n, 0, L_max)) and KVC_FLAG_CACHE_FULL is
+ * set.  Results are those of the two separate calls (bit-identical cache and
+ * lengths; outputs equal up to rounding order).
+ *
+ * Arguments as for kvc_append and kvc_decode_attn; the workspace comes from
+ * kvc_append_decode_attn_workspace_size (never 0: it holds one arrival
+ * counter per sequence) and follows the same zero-fill rule.
+ */
+size_t kvc_append_decode_attn_workspace_size(int B, int n_h, int n_kv,
+                                             int L_max, int d, int dtype);
+int kvc_append_decode_attn(const void* q, void* k_cache, void* v_cache,
+                           int32_t* seq_lens, const void* k_new,
+                           const void* v_new, void* out, float* lse,
+                           int B, int n_h, int n_kv, int L_max, int d,
+                           float scale, int dtype, int32_t* flag,
+                           void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * kvc_decode_attn_mla - decode attention over a latent (MLA) cache.
  * (Guide, "Caching a compressed latent" and the memory footnote.)
  *

@@ -59,6 +59,9 @@ def lib() -> ctypes.CDLL:
         "kvc_decode_attn_workspace_size": (_Z, [_I, _I, _I, _I, _I, _I]),
         "kvc_decode_attn": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
                                  _F, _I, _P, _Z, _P]),
+        "kvc_append_decode_attn_workspace_size": (_Z, [_I, _I, _I, _I, _I, _I]),
+        "kvc_append_decode_attn": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I,
+                                        _I, _F, _I, _P, _P, _Z, _P]),
         "kvc_decode_attn_mla_workspace_size": (_Z, [_I, _I, _I, _I, _I, _I]),
         "kvc_decode_attn_mla": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
                                      _F, _I, _P, _Z, _P]),
@@ -173,6 +176,27 @@ def kvc_decode_attn(q, k_cache, v_cache, seq_lens, out, lse=None, scale=None,
                                n_kv, L_max, d, scale, _dtype_code(q), wp, wn,
                                _stream(stream))
     _check(st, "kvc_decode_attn")
+
+
+def kvc_append_decode_attn_workspace_size(B, n_h, n_kv, L_max, d, dtype) -> int:
+    return lib().kvc_append_decode_attn_workspace_size(B, n_h, n_kv, L_max, d, dtype)
+
+
+def kvc_append_decode_attn(q, k_cache, v_cache, seq_lens, k_new, v_new, out,
+                           lse=None, scale=None, flag=None, workspace=None,
+                           stream=None):
+    """Append k_new/v_new at slot seq_lens[b], attend over the cache
+    including it, bump seq_lens -- one kernel launch."""
+    B, n_h, d = q.shape
+    _, n_kv, L_max, _ = k_cache.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    wp, wn = _ws(workspace)
+    st = lib().kvc_append_decode_attn(_ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                      _ptr(seq_lens), _ptr(k_new), _ptr(v_new),
+                                      _ptr(out), _ptr(lse), B, n_h, n_kv, L_max,
+                                      d, scale, _dtype_code(q), _ptr(flag), wp, wn,
+                                      _stream(stream))
+    _check(st, "kvc_append_decode_attn")
 
 
 def kvc_decode_attn_mla_workspace_size(B, n_h, L_max, d_c, d_r, dtype) -> int:

@@ -181,6 +181,73 @@ __device__ void finish_split(const DenseParams& p, int b, int j, int split,
   if (t == 0) *ticket = 0;
 }
 
+// Length attended by this workgroup.  Plain decode: seq_lens[b] (the caller
+// appended already).  Fused append-and-attend: n = seq_lens[b] is the slot
+// of the new token; the split that owns slot n writes the new K/V row (and,
+// with WAIT_WRITE, waits for it before any of its waves reads it; the MFMA
+// kernel instead replaces that row's registers with k_new/v_new after
+// loading), and the attended length is n + 1.  A full cache
+// (n outside [0, L_max)) writes nothing, attends the stored positions and
+// sets flag bit 0.
+//
+// The length itself is bumped once every workgroup of sequence b has read
+// the old value: thread 0 of each workgroup arrives on its unit's counter
+// (issued here, result checked in complete_length after the main work), the
+// last arrival of a unit arrives on the sequence's counter, and the last of
+// those writes seq_lens[b] = n + 1.  Every workgroup arrives, including ones
+// with no positions.
+struct LengthState {
+  int n_raw;
+  bool ok;
+  int unit_prev;   // thread 0: value returned by the unit arrival
+};
+
+template <bool APPEND, int D, typename T, bool WAIT_WRITE = true>
+__device__ inline int attended_length(const DenseParams& p, int b, int j, int split,
+                                      LengthState& ls) {
+  const int n_raw = *static_cast<const volatile int32_t*>(p.seq_lens + b);
+  if constexpr (!APPEND) {
+    return min(max(n_raw, 0), p.L_max);
+  } else {
+    const bool ok = n_raw >= 0 && n_raw < p.L_max;
+    ls.n_raw = n_raw;
+    ls.ok = ok;
+    ls.unit_prev = 0;
+    if (threadIdx.x == 0)
+      ls.unit_prev = atomicAdd(p.ws_ucnt + (size_t)b * p.n_kv + j, 1);
+    if (ok && split == n_raw / p.S) {
+      constexpr int U = D * (int)sizeof(T) / 16;    // 16-byte pieces per row
+      const size_t unit = (size_t)b * p.n_kv + j;
+      const size_t dst = (unit * p.L_max + n_raw) * U;
+      const int t = threadIdx.x;
+      if (t < U)
+        reinterpret_cast<u32x4*>(p.k)[dst + t] = reinterpret_cast<const u32x4*>(p.k_new)[unit * U + t];
+      else if (t < 2 * U)
+        reinterpret_cast<u32x4*>(p.v)[dst + t - U] = reinterpret_cast<const u32x4*>(p.v_new)[unit * U + t - U];
+      if constexpr (WAIT_WRITE) {   // otherwise the reader patches the row in registers
+        wait_vm_all();
+        __syncthreads();
+      }
+    }
+    if (!ok && j == 0 && split == 0 && threadIdx.x == 0 && p.flag) atomicOr(p.flag, 1);
+    return ok ? n_raw + 1 : min(max(n_raw, 0), p.L_max);
+  }
+}
+
+template <bool APPEND>
+__device__ inline void complete_length(const DenseParams& p, int b, int j,
+                                       const LengthState& ls) {
+  if constexpr (APPEND) {
+    if (threadIdx.x == 0 && ls.unit_prev == p.P_max - 1) {
+      p.ws_ucnt[(size_t)b * p.n_kv + j] = 0;
+      if (atomicAdd(p.ws_bcnt + b, 1) == p.n_kv - 1) {
+        p.ws_bcnt[b] = 0;
+        if (ls.ok) p.seq_lens_rw[b] = ls.n_raw + 1;
+      }
+    }
+  }
+}
+
 __device__ inline void decode_unit(const DenseParams& p, int& b, int& j,
                                    int& split) {
   int wg = blockIdx.x;
@@ -261,6 +328,26 @@ __device__ inline void load_chunk(Chunk& c, int cs, int end, int n,
   }
 }
 
+// Fused append: the chunk holding the new token's slot takes that row from
+// k_new/v_new (the cache copy is being written concurrently).  Lane (r, g)
+// holds K rows pi(a, r) at columns kk*32 + g*8 and V rows g*8 + e at columns
+// r*8, so it copies the matching 16-byte pieces of the new rows.
+__device__ inline void patch_new_row(Chunk& c, int cs, int slot, const u32x4* kn,
+                                     const u32x4* vn, int r, int g) {
+  const int pos = slot - cs;
+  if (pos < 0 || pos >= kDenseChunk) return;
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    if ((r >> 2) * 8 + a * 4 + (r & 3) == pos) {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) c.k[a][kk] = kn[kk * 4 + g];
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    if (g * 8 + e == pos) c.v[e] = vn[r];
+}
+
 struct WaveState {
   float m;        // running max (log2 units), same in the 4 lanes of a head
   float l;        // this lane's share of the running sum
@@ -324,16 +411,18 @@ __device__ inline void compute_chunk(const Chunk& c, int cs, int end,
   }
 }
 
-template <bool TOPK>
-__global__ __launch_bounds__(256) void dense_mfma_kernel(DenseParams p) {
+template <bool TOPK, bool APPEND>
+__global__ __launch_bounds__(256, 2) void dense_mfma_kernel(DenseParams p) {
   __shared__ MergeLds<128> L;
   int b, j, split;
   decode_unit(p, b, j, split);
-  const int n = min(max(p.seq_lens[b], 0), p.L_max);
+  LengthState ls;
+  const int n = attended_length<APPEND, 128, uint16_t, false>(p, b, j, split, ls);
   const int count = TOPK ? p.K : n;
   const int start = split * p.S;
   if (start >= count) {
     if (split == 0) write_empty<uint16_t, 128>(p, b, j);
+    complete_length<APPEND>(p, b, j, ls);
     return;
   }
   const int end = min(count, start + p.S);
@@ -372,19 +461,30 @@ __global__ __launch_bounds__(256) void dense_mfma_kernel(DenseParams p) {
   bool bad = false;
   int cs = start + wave * kDenseChunk;
   constexpr int kStride = kDenseChunk * 4;
+  // fused append: slot of the new row (or -1), and its source rows
+  const int new_slot = (APPEND && ls.ok) ? ls.n_raw : -1;
+  const u32x4* kn = reinterpret_cast<const u32x4*>(p.k_new) + unit * 16;
+  const u32x4* vn = reinterpret_cast<const u32x4*>(p.v_new) + unit * 16;
   if (cs < end) {
     Chunk A, Bc;
     load_chunk<TOPK>(A, cs, end, n, kr, vr, ir, r, g, bad);
+    if constexpr (APPEND) patch_new_row(A, cs, new_slot, kn, vn, r, g);
     while (true) {
       int cn = cs + kStride;
       bool more = cn < end;
-      if (more) load_chunk<TOPK>(Bc, cn, end, n, kr, vr, ir, r, g, bad);
+      if (more) {
+        load_chunk<TOPK>(Bc, cn, end, n, kr, vr, ir, r, g, bad);
+        if constexpr (APPEND) patch_new_row(Bc, cn, new_slot, kn, vn, r, g);
+      }
       compute_chunk<TOPK>(A, cs, end, qop, p.scale_log2, g, st);
       if (!more) break;
       cs = cn;
       cn = cs + kStride;
       more = cn < end;
-      if (more) load_chunk<TOPK>(A, cn, end, n, kr, vr, ir, r, g, bad);
+      if (more) {
+        load_chunk<TOPK>(A, cn, end, n, kr, vr, ir, r, g, bad);
+        if constexpr (APPEND) patch_new_row(A, cn, new_slot, kn, vn, r, g);
+      }
       compute_chunk<TOPK>(Bc, cs, end, qop, p.scale_log2, g, st);
       if (!more) break;
       cs = cn;
@@ -404,6 +504,7 @@ __global__ __launch_bounds__(256) void dense_mfma_kernel(DenseParams p) {
   for (int m = 0; m < 8; ++m)
 #pragma unroll
     for (int i = 0; i < 4; ++i) L.o[wave][r][(4 * g + i) * 8 + m] = st.acc[m][i];
+  complete_length<APPEND>(p, b, j, ls);
   __syncthreads();
   finish_split<uint16_t, 128>(p, b, j, split, nsplit, L);
 }
@@ -438,17 +539,19 @@ __device__ inline void load8(const uint16_t* p, float (&x)[8]) {
   }
 }
 
-template <typename T, int D, bool TOPK>
+template <typename T, int D, bool TOPK, bool APPEND>
 __global__ __launch_bounds__(256) void dense_generic_kernel(DenseParams p) {
   __shared__ MergeLds<D> L;
   __shared__ float sq[kMaxGroup][D];
   int b, j, split;
   decode_unit(p, b, j, split);
-  const int n = min(max(p.seq_lens[b], 0), p.L_max);
+  LengthState ls;
+  const int n = attended_length<APPEND, D, T>(p, b, j, split, ls);
   const int count = TOPK ? p.K : n;
   const int start = split * p.S;
   if (start >= count) {
     if (split == 0) write_empty<T, D>(p, b, j);
+    complete_length<APPEND>(p, b, j, ls);
     return;
   }
   const int end = min(count, start + p.S);
@@ -552,6 +655,7 @@ __global__ __launch_bounds__(256) void dense_generic_kernel(DenseParams p) {
 #pragma unroll
     for (int u = 0; u < U; ++u) L.o[wave][h][lane + 64 * u] = o[h][u];
   }
+  complete_length<APPEND>(p, b, j, ls);
   __syncthreads();
   finish_split<T, D>(p, b, j, split, nsplit, L);
 }
@@ -563,31 +667,35 @@ static dim3 dense_grid(const DenseParams& p) {
   return dim3((unsigned)((size_t)p.B * p.n_kv * p.P_max));
 }
 
-hipError_t launch_dense_mfma(const DenseParams& p, bool topk, hipStream_t s) {
+hipError_t launch_dense_mfma(const DenseParams& p, bool topk, bool append, hipStream_t s) {
   if (topk)
-    hipLaunchKernelGGL(dense_mfma_kernel<true>, dense_grid(p), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((dense_mfma_kernel<true, false>), dense_grid(p), dim3(256), 0, s, p);
+  else if (append)
+    hipLaunchKernelGGL((dense_mfma_kernel<false, true>), dense_grid(p), dim3(256), 0, s, p);
   else
-    hipLaunchKernelGGL(dense_mfma_kernel<false>, dense_grid(p), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((dense_mfma_kernel<false, false>), dense_grid(p), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
 template <typename T, int D>
-static void launch_generic_t(const DenseParams& p, bool topk, hipStream_t s) {
+static void launch_generic_t(const DenseParams& p, bool topk, bool append, hipStream_t s) {
   if (topk)
-    hipLaunchKernelGGL((dense_generic_kernel<T, D, true>), dense_grid(p), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((dense_generic_kernel<T, D, true, false>), dense_grid(p), dim3(256), 0, s, p);
+  else if (append)
+    hipLaunchKernelGGL((dense_generic_kernel<T, D, false, true>), dense_grid(p), dim3(256), 0, s, p);
   else
-    hipLaunchKernelGGL((dense_generic_kernel<T, D, false>), dense_grid(p), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((dense_generic_kernel<T, D, false, false>), dense_grid(p), dim3(256), 0, s, p);
 }
 
 hipError_t launch_dense_generic(const DenseParams& p, int dtype, bool topk,
-                                hipStream_t s) {
+                                bool append, hipStream_t s) {
   const bool bf = dtype == 1;
   if (p.d == 64) {
-    if (bf) launch_generic_t<uint16_t, 64>(p, topk, s);
-    else launch_generic_t<float, 64>(p, topk, s);
+    if (bf) launch_generic_t<uint16_t, 64>(p, topk, append, s);
+    else launch_generic_t<float, 64>(p, topk, append, s);
   } else {
-    if (bf) launch_generic_t<uint16_t, 128>(p, topk, s);
-    else launch_generic_t<float, 128>(p, topk, s);
+    if (bf) launch_generic_t<uint16_t, 128>(p, topk, append, s);
+    else launch_generic_t<float, 128>(p, topk, append, s);
   }
   return hipGetLastError();
 }

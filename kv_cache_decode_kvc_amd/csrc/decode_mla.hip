@@ -31,8 +31,10 @@
 //          column 256h + r*8 + m.
 //
 // Latent tiles go HBM -> LDS directly (buffer_load ... lds), three chunks
-// deep, with chunk k of row rho stored at k ^ (rho & 7) so that both read
-// patterns avoid bank conflicts.  Rows at or past the sequence length read
+// deep, with 16-byte chunk k of row rho stored at k ^ ((rho >> 1) & 7).  The
+// row stride (1152 B) puts consecutive rows half a bank set apart on the
+// 64-bank LDS, so this key gives 16 distinct bank groups to the 16 lanes an
+// LDS cycle serves in both read patterns.  Rows at or past the sequence length read
 // as zeros (buffer range check) and are masked.  Splits of one sequence are
 // merged by log-sum-exp by the last workgroup to finish.
 
@@ -136,30 +138,35 @@ __global__ __launch_bounds__(256, 1) void mla_kernel(MlaParams p) {
       (const char*)p.ckv + (size_t)b * p.L_max * kRowB, (uint32_t)n * kRowB);
 
   // Load k of this lane fills LDS byte blk*1024 + lane*16 of a stage: row
-  // rho, physical chunk pc, which holds logical chunk pc ^ (rho & 7).
+  // rho, physical chunk pc, which holds logical chunk pc ^ ((rho >> 1) & 7).
   uint32_t goff[kLoadsPerWave];
 #pragma unroll
   for (int k = 0; k < kLoadsPerWave; ++k) {
     const int byte = (wave * kLoadsPerWave + k) * 1024 + lane * 16;
     const int rho = byte / kRowB;
     const int pc = (byte - rho * kRowB) >> 4;
-    goff[k] = (uint32_t)(rho * kRowB + ((pc ^ (rho & 7)) << 4));
+    goff[k] = (uint32_t)(rho * kRowB + ((pc ^ ((rho >> 1) & 7)) << 4));
   }
   // LDS read bases.  Scores: row r, logical chunk q = 2kk + g, stored at
-  // 8*(q/8) + ((q & 7) ^ (r & 7)).  This wave's k-steps are kk = 18h + k;
-  // writing k = 4a + u and x = 2h + u gives kk & 3 = x & 3 and
+  // 8*(q/8) + ((q & 7) ^ f) with f = (r >> 1) & 7.  This wave's k-steps are
+  // kk = 18h + k; writing k = 4a + u and x = 2h + u gives kk & 3 = x & 3 and
   // kk >> 2 = 4h + a + (x >> 2), so four per-wave bases plus a*128 cover
-  // every k-step.  Values: row rho = 8*(2ks + jj/4) + 4g + (jj & 3) has
-  // rho & 7 = 4g + (jj & 3); this half's chunk 32h + r sits at
-  // 32h + (r ^ (4g + (jj & 3))): four bases plus constants.
-  uint32_t wqk[4], pv_base[4];
+  // every k-step.  Values: row rho = 8*(2ks + jj/4) + 4g + (jj & 3) has key
+  // f = (4*(jj/4) + 2g + ((jj >> 1) & 1)) & 7 (ks drops out), and this half's
+  // chunk 32h + r sits at 32h + (r ^ f): eight bases (one per jj) plus
+  // 16*1152*ks.
+  uint32_t wqk[4], pv_base[8];
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
     const int x = 2 * half + v;
-    wqk[v] = (uint32_t)(r * kRowB + (((2 * (x & 3) + g) ^ (r & 7)) << 4) +
+    wqk[v] = (uint32_t)(r * kRowB + (((2 * (x & 3) + g) ^ ((r >> 1) & 7)) << 4) +
                         (4 * half + (x >> 2)) * 128);
-    const int y = 4 * g + v;
-    pv_base[v] = (uint32_t)(y * kRowB + ((r ^ y) << 4) + half * 512);
+  }
+#pragma unroll
+  for (int jj = 0; jj < 8; ++jj) {
+    const int rho0 = 8 * (jj >> 2) + 4 * g + (jj & 3);
+    const int f = (rho0 >> 1) & 7;
+    pv_base[jj] = (uint32_t)(rho0 * kRowB + ((r ^ f) << 4) + half * 512);
   }
 
   bf16x8 qop[kKHalf];
@@ -196,12 +203,16 @@ __global__ __launch_bounds__(256, 1) void mla_kernel(MlaParams p) {
     // This chunk's LDS bases, materialised once per chunk so that every read
     // below is base + constant (the constant goes in the instruction).
     const uint32_t toff = (uint32_t)((c % kStages) * kTileB);
-    uint32_t qb[4], pb[4];
+    uint32_t qb[4], pb[8];
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       qb[v] = toff + wqk[v];
-      pb[v] = toff + pv_base[v];
-      asm volatile("" : "+v"(qb[v]), "+v"(pb[v]));
+      asm volatile("" : "+v"(qb[v]));
+    }
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      pb[jj] = toff + pv_base[jj];
+      asm volatile("" : "+v"(pb[jj]));
     }
 
     // this half's score contribution; LDS reads run four k-steps ahead
@@ -222,7 +233,7 @@ __global__ __launch_bounds__(256, 1) void mla_kernel(MlaParams p) {
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj)
-        vr[ks][jj] = lds_load16(smem, pb[jj & 3] + (8 * (2 * ks + (jj >> 2))) * kRowB);
+        vr[ks][jj] = lds_load16(smem, pb[jj] + 16 * ks * kRowB);
 
     // add the other half's contribution
 #pragma unroll

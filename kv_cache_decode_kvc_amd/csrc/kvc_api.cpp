@@ -74,7 +74,7 @@ struct DenseCheck {
 };
 
 DenseCheck check_dense_shape(int B, int n_h, int n_kv, int L_max, int d,
-                             int dtype, int K, bool topk) {
+                             int dtype, int K, bool topk, bool fused = false) {
   DenseCheck c{KVC_OK, 0, 1, {}};
   if (!good_dtype(dtype)) { c.status = KVC_ERR_BAD_DTYPE; return c; }
   if (B < 0 || n_h < 1 || n_kv < 1 || L_max < 1 || d < 1) {
@@ -92,7 +92,7 @@ DenseCheck check_dense_shape(int B, int n_h, int n_kv, int L_max, int d,
   c.S = policy_split(topk ? KVC_KIND_TOPK : KVC_KIND_DENSE, B, units, n_max);
   c.P_max = splits_for(n_max, c.S);
   if (units * c.P_max >= kMaxOffset) { c.status = KVC_ERR_BAD_SHAPE; return c; }
-  c.ws = ws_layout((size_t)units, (size_t)B, (size_t)n_h, (size_t)c.P_max, (size_t)d);
+  c.ws = ws_layout((size_t)units, (size_t)B, (size_t)n_h, (size_t)c.P_max, (size_t)d, fused);
   if (c.ws.total >= (size_t)kMaxOffset) { c.status = KVC_ERR_UNSUPPORTED; return c; }
   return c;
 }
@@ -107,15 +107,19 @@ int check_workspace(const WsLayout& ws, void* workspace, size_t ws_bytes) {
 
 int launch_status(hipError_t e) { return e == hipSuccess ? KVC_OK : KVC_ERR_HIP; }
 
-void fill_ws(DenseParams& p, const WsLayout& ws, void* workspace) {
-  if (ws.total == 0) {
-    p.ws_cnt = nullptr; p.ws_lse = nullptr; p.ws_o = nullptr;
-    return;
-  }
+void fill_ws(DenseParams& p, const WsLayout& ws, void* workspace, size_t P_max,
+             bool fused) {
+  p.ws_cnt = nullptr; p.ws_lse = nullptr; p.ws_o = nullptr; p.ws_bcnt = nullptr;
   char* base = static_cast<char*>(workspace);
-  p.ws_cnt = reinterpret_cast<int32_t*>(base + ws.cnt_off);
-  p.ws_lse = reinterpret_cast<float*>(base + ws.lse_off);
-  p.ws_o = reinterpret_cast<float*>(base + ws.o_off);
+  if (P_max > 1) {
+    p.ws_cnt = reinterpret_cast<int32_t*>(base + ws.cnt_off);
+    p.ws_lse = reinterpret_cast<float*>(base + ws.lse_off);
+    p.ws_o = reinterpret_cast<float*>(base + ws.o_off);
+  }
+  if (fused) {
+    p.ws_bcnt = reinterpret_cast<int32_t*>(base + ws.bcnt_off);
+    p.ws_ucnt = p.ws_bcnt + p.B;
+  }
 }
 
 struct MlaCheck {
@@ -214,31 +218,56 @@ static int dense_common(const void* q, const void* k_cache, const void* v_cache,
                         void* out, float* lse, int B, int n_h, int n_kv,
                         int L_max, int d, float scale, int dtype, int32_t* flag,
                         void* workspace, size_t ws_bytes, void* stream,
-                        bool topk) {
-  const DenseCheck c = check_dense_shape(B, n_h, n_kv, L_max, d, dtype, K, topk);
+                        bool topk, const void* k_new = nullptr,
+                        const void* v_new = nullptr, bool fused = false) {
+  const DenseCheck c = check_dense_shape(B, n_h, n_kv, L_max, d, dtype, K, topk, fused);
   if (c.status != KVC_OK) return c.status;
   if (!isfinite(scale)) return KVC_ERR_BAD_ARG;
-  if (!q || !k_cache || !v_cache || !seq_lens || !out || (topk && !idx))
+  if (!q || !k_cache || !v_cache || !seq_lens || !out || (topk && !idx) ||
+      (fused && (!k_new || !v_new)))
     return KVC_ERR_NULL_PTR;
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
       !aligned(out, 16) || !aligned(seq_lens, 4) || (lse && !aligned(lse, 4)) ||
-      (idx && !aligned(idx, 16)) || (flag && !aligned(flag, 4)))
+      (idx && !aligned(idx, 16)) || (flag && !aligned(flag, 4)) ||
+      (fused && (!aligned(k_new, 16) || !aligned(v_new, 16))))
     return KVC_ERR_MISALIGNED;
   if (B == 0) return KVC_OK;
   const int ws_status = check_workspace(c.ws, workspace, ws_bytes);
   if (ws_status != KVC_OK) return ws_status;
 
   DenseParams p{};
-  p.q = q; p.k = k_cache; p.v = v_cache; p.seq_lens = seq_lens;
+  p.q = q;
+  p.k = const_cast<void*>(k_cache);
+  p.v = const_cast<void*>(v_cache);
+  p.k_new = k_new; p.v_new = v_new;
+  p.seq_lens = seq_lens;
+  p.seq_lens_rw = fused ? const_cast<int32_t*>(seq_lens) : nullptr;
   p.idx = topk ? idx : nullptr; p.out = out; p.lse = lse;
-  p.flag = topk ? flag : nullptr;
-  fill_ws(p, c.ws, workspace);
+  p.flag = (topk || fused) ? flag : nullptr;
   p.B = B; p.n_h = n_h; p.n_kv = n_kv; p.G = n_h / n_kv; p.L_max = L_max;
+  fill_ws(p, c.ws, workspace, (size_t)c.P_max, fused);
   p.d = d; p.K = topk ? K : 0; p.S = c.S; p.P_max = (int)c.P_max;
   p.scale_log2 = scale * 1.4426950408889634f;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (dtype == KVC_BF16 && d == 128) return launch_status(launch_dense_mfma(p, topk, s));
-  return launch_status(launch_dense_generic(p, dtype, topk, s));
+  if (dtype == KVC_BF16 && d == 128) return launch_status(launch_dense_mfma(p, topk, fused, s));
+  return launch_status(launch_dense_generic(p, dtype, topk, fused, s));
+}
+
+size_t kvc_append_decode_attn_workspace_size(int B, int n_h, int n_kv, int L_max,
+                                             int d, int dtype) {
+  const DenseCheck c = check_dense_shape(B, n_h, n_kv, L_max, d, dtype, 0, false, true);
+  return c.status == KVC_OK ? c.ws.total : 0;
+}
+
+int kvc_append_decode_attn(const void* q, void* k_cache, void* v_cache,
+                           int32_t* seq_lens, const void* k_new,
+                           const void* v_new, void* out, float* lse, int B,
+                           int n_h, int n_kv, int L_max, int d, float scale,
+                           int dtype, int32_t* flag, void* workspace,
+                           size_t ws_bytes, void* stream) {
+  return dense_common(q, k_cache, v_cache, seq_lens, nullptr, 0, out, lse, B,
+                      n_h, n_kv, L_max, d, scale, dtype, flag, workspace,
+                      ws_bytes, stream, false, k_new, v_new, true);
 }
 
 int kvc_decode_attn(const void* q, const void* k_cache, const void* v_cache,

@@ -42,8 +42,13 @@ struct AppendParams {
 // Dense and top-k decode.  Workspace pointers are null when P_max == 1.
 struct DenseParams {
   const void* q;
-  const void* k;
-  const void* v;
+  void* k;                // written only by the fused append-and-attend call
+  void* v;
+  const void* k_new;      // fused call: the new token's rows [B, n_kv, d]
+  const void* v_new;
+  int32_t* seq_lens_rw;   // fused call: lengths to bump (same array as seq_lens)
+  int32_t* ws_bcnt;       // fused call: [B] per-sequence arrival counters
+  int32_t* ws_ucnt;       // fused call: [B * n_kv] per-unit arrival counters
   const int32_t* seq_lens;
   const int32_t* idx;     // top-k only
   void* out;
@@ -74,27 +79,37 @@ struct MlaParams {
 };
 
 struct WsLayout {
-  size_t cnt_off, lse_off, o_off, total;
+  size_t cnt_off, lse_off, o_off, bcnt_off, total;
 };
 
 inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Workspace: [tickets per unit][partial lse][partial outputs] when a
+// sequence can need several splits, then (fused append-and-attend only) one
+// arrival counter per sequence followed by one per unit.
 inline WsLayout ws_layout(size_t units, size_t B, size_t n_h, size_t P_max,
-                          size_t d) {
+                          size_t d, bool fused = false) {
   WsLayout w{};
-  if (P_max <= 1) return w;
-  w.cnt_off = 0;
-  w.lse_off = round_up(units * sizeof(int32_t), 256);
-  w.o_off = w.lse_off + round_up(B * n_h * P_max * sizeof(float), 256);
-  w.total = w.o_off + B * n_h * P_max * d * sizeof(float);
+  size_t end = 0;
+  if (P_max > 1) {
+    w.cnt_off = 0;
+    w.lse_off = round_up(units * sizeof(int32_t), 256);
+    w.o_off = w.lse_off + round_up(B * n_h * P_max * sizeof(float), 256);
+    end = round_up(w.o_off + B * n_h * P_max * d * sizeof(float), 256);
+  }
+  if (fused) {
+    w.bcnt_off = end;
+    end += round_up((B + units) * sizeof(int32_t), 256);
+  }
+  w.total = end;
   return w;
 }
 
 // Kernel launchers (defined in the .hip sources).
 hipError_t launch_append(const AppendParams& p, hipStream_t s);
-hipError_t launch_dense_mfma(const DenseParams& p, bool topk, hipStream_t s);
+hipError_t launch_dense_mfma(const DenseParams& p, bool topk, bool append, hipStream_t s);
 hipError_t launch_dense_generic(const DenseParams& p, int dtype, bool topk,
-                                hipStream_t s);
+                                bool append, hipStream_t s);
 hipError_t launch_mla(const MlaParams& p, hipStream_t s);
 hipError_t launch_stream_read(const void* src, size_t bytes, float* sink,
                               hipStream_t s);

@@ -157,3 +157,22 @@ def test_diag_validation(L):
     assert L.kvc_stream_read(A16, 8, A16, NULL) == -6
     assert L.kvc_copy(A16, A8, 16, NULL) == -6
     assert L.kvc_copy(A16, A16, 0, NULL) == 0
+
+
+def test_fused_validation(L):
+    def fz(**kw):
+        a = dict(q=A16, k=A16, v=A16, sl=A4, kn=A16, vn=A16, out=A16, lse=NULL, B=2, n_h=8,
+                 n_kv=2, L_max=64, d=128, scale=0.1, dt=kvc.KVC_BF16, flag=NULL, ws=A16,
+                 wsb=1 << 30, stream=NULL)
+        a.update(kw)
+        return L.kvc_append_decode_attn(a["q"], a["k"], a["v"], a["sl"], a["kn"], a["vn"],
+                                        a["out"], a["lse"], a["B"], a["n_h"], a["n_kv"],
+                                        a["L_max"], a["d"], a["scale"], a["dt"], a["flag"],
+                                        a["ws"], a["wsb"], a["stream"])
+    assert fz(kn=NULL) == -1
+    assert fz(vn=A8) == -6
+    assert fz(ws=NULL) == -1              # always needs its arrival counters
+    assert fz(wsb=16) == -5
+    assert fz(n_h=6, n_kv=4) == -2
+    assert fz(B=0) == 0
+    assert L.kvc_append_decode_attn_workspace_size(1, 8, 2, 64, 128, kvc.KVC_BF16) > 0

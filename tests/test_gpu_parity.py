@@ -353,3 +353,75 @@ def test_copy_and_stream_read():
     kvc.kvc_stream_read(src, sink)
     torch.cuda.synchronize()
     assert torch.equal(dst, src)
+
+
+# ------------------------------------------------- fused append + attend
+FUSED_CASES = [
+    # (n_h, n_kv, d, dtype, pre-append lengths, L_max, split)
+    (32, 32, 128, "bf16", [4096], 4097, 0),                      # MHA layer, C2 shape
+    (64, 8, 128, "bf16", [0, 31, 255, 256, 1000, 2047, 2048], 2048, 0),   # incl. full cache
+    (64, 8, 128, "bf16", [0, 31, 255, 256, 1000, 2047], 2048, 256),
+    (16, 1, 128, "bf16", [511, 3], 512, 0),
+    (8, 2, 64, "bf16", [0, 129, 599, 600], 600, 0),              # generic kernel
+    (16, 4, 128, "f32", [0, 999, 64], 1000, 0),                  # generic kernel f32
+]
+
+
+@pytest.mark.parametrize("n_h,n_kv,d,dtype,pre,L_max,split", FUSED_CASES)
+def test_fused_append_decode(n_h, n_kv, d, dtype, pre, L_max, split):
+    """One launch = kvc_append then kvc_decode_attn: cache bytes and lengths
+    bit-exact, outputs within tolerance, full cache flagged and untouched."""
+    B = len(pre)
+    case = syn.dense_case(B, n_h, n_kv, d, L_max, pre, dtype, cfg_id=101)
+    scale = 1 / math.sqrt(d)
+    kc, vc, sl = dev(case["k_cache"]), dev(case["v_cache"]), dev(case["seq_lens"])
+    q, kn, vn = dev(case["q"]), dev(case["k_new"]), dev(case["v_new"])
+    out = torch.empty_like(q)
+    lse = torch.empty(B, n_h, dtype=torch.float32, device="cuda")
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    kvc.kvc_set_split_override(split)
+    code = kvc._dtype_code(q)
+    ws = kvc.workspace(kvc.kvc_append_decode_attn_workspace_size(B, n_h, n_kv, L_max, d, code))
+    kvc.kvc_append_decode_attn(q, kc, vc, sl, kn, vn, out, lse, scale=scale, flag=flag, workspace=ws)
+    torch.cuda.synchronize()
+    o_ref, l_ref, sl_ref, kc_ref, vc_ref, f_ref = oracle_dense_step(case, scale)
+    assert host(sl).tolist() == sl_ref.tolist()
+    assert int(host(flag)[0]) == f_ref
+    assert np.array_equal(host(kc).view(np.uint8), kc_ref.view(np.uint8))
+    assert np.array_equal(host(vc).view(np.uint8), vc_ref.view(np.uint8))
+    compare(host_f64(out), o_ref, tol_for(dtype), f"fused {n_h}/{n_kv} d{d} {dtype}")
+    compare_lse(host(lse), l_ref, lse_tol(dtype))
+    # counters: per-unit tickets at the front (when splits exist), one
+    # arrival counter per sequence in the last 256-byte-rounded block
+    tail = -(-4 * (B + B * n_kv) // 256) * 256
+    w32 = ws.view(torch.int32)
+    assert int(w32[-tail // 4:].abs().sum()) == 0, "arrival counters not reset"
+    if ws.numel() > tail:
+        assert int(w32[:B * n_kv].abs().sum()) == 0, "tickets not reset"
+
+
+def test_fused_graph_replay_and_repeat():
+    """Repeated fused steps (one appended token each) match the oracle's
+    append/decode loop, also when replayed from a captured graph."""
+    n_h, n_kv, d, L_max = 64, 8, 128, 1200
+    pre = [1000, 3, 600]
+    B = len(pre)
+    case = syn.dense_case(B, n_h, n_kv, d, L_max, pre, "bf16", cfg_id=102)
+    kc, vc, sl = dev(case["k_cache"]), dev(case["v_cache"]), dev(case["seq_lens"])
+    q, kn, vn = dev(case["q"]), dev(case["k_new"]), dev(case["v_new"])
+    out = torch.empty_like(q)
+    ws = kvc.workspace(kvc.kvc_append_decode_attn_workspace_size(B, n_h, n_kv, L_max, d, 1))
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=s):
+        kvc.kvc_append_decode_attn(q, kc, vc, sl, kn, vn, out, workspace=ws)
+    kc_o, vc_o, sl_o = case["k_cache"].copy(), case["v_cache"].copy(), case["seq_lens"].copy()
+    for step in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        oracle.append(kc_o, vc_o, sl_o, case["k_new"], case["v_new"])
+        o_ref, _ = oracle.decode(case["q"], kc_o, vc_o, sl_o, 1 / math.sqrt(d))
+        assert host(sl).tolist() == sl_o.tolist()
+        compare(host_f64(out), o_ref, 2e-2, f"fused replay {step}")
+    assert np.array_equal(host(kc), kc_o)
