@@ -374,6 +374,21 @@ def read_ceiling(torch, kvc, nbytes=4 << 30, reps=10):
     return gbs
 
 
+def measured_traffic(name):
+    """HBM bytes per launch of the workload's dominant kernel from the
+    committed counter runs (profiles/traffic.json), or None if the kernel
+    sources changed since those counters were taken."""
+    try:
+        from kv_cache_decode_kvc_amd.profile_summary import source_hash
+        with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
+            rec = json.load(f).get(name)
+        if not rec or rec["source_sha256"] != source_hash():
+            return None
+        return rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
+    except (OSError, ValueError, KeyError):
+        return None
+
+
 def blas_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -414,7 +429,8 @@ def main():
                    "us_per_layer_step": round(head["us_per_layer_step"], 3)},
         "roofline": {"bound": "hbm", "achieved": round(head["kernel_gbs"], 2),
                      "peak": PEAK_GBS, "unit": "GB/s",
-                     "frac": round(head["kernel_gbs"] / PEAK_GBS, 4), "traffic": None,
+                     "frac": round(head["kernel_gbs"] / PEAK_GBS, 4),
+                     "traffic": measured_traffic(args.config),
                      "kernel": head["kernel"], "kernel_us": round(head["kernel_us"], 3),
                      "algorithmic_bytes_per_launch": head["kernel_bytes"]},
     }
@@ -434,6 +450,7 @@ def main():
     for name in [x for x in args.others.split(",") if x in WORKLOADS and x != args.config]:
         w, r = measure(name, args, torch, kvc)
         also[name] = {k: (round(v, 3) if isinstance(v, float) else v) for k, v in r.items()}
+        also[name]["traffic"] = measured_traffic(name)
         del w
         torch.cuda.empty_cache()
     if also:
