@@ -21,10 +21,10 @@ constexpr int kMaxSplits = 256;
 // accumulators is rare.  The result is the same; only rounding differs.
 constexpr float kRescaleMargin = 8.0f;
 // MLA kernel: positions per step (also the split granularity); a workgroup
-// of 4 waves covers 64 heads, two waves sharing each 32 heads.
+// of 8 waves (two per SIMD) covers 64 heads, two waves sharing each 16.
 constexpr int kMlaChunk = 32;
-constexpr int kMlaHeadsPerWave = 32;
-constexpr int kMlaWaves = 4;
+constexpr int kMlaHeadsPerWave = 16;
+constexpr int kMlaWaves = 8;
 constexpr int kMlaHeadsPerWg = 64;
 constexpr int kMlaDc = 512;
 constexpr int kMlaDr = 64;
