@@ -27,6 +27,9 @@ COMMON = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     # packed fp32 instructions are kept out of the generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # single-lane atomics stay plain atomics: the wave-reduction rewrite
+    # consumes the result right away and so waits for the round trip
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-I", INCLUDE, "-I", CSRC,
 ]
 

@@ -205,7 +205,10 @@ struct LengthState {
 template <bool APPEND, int D, typename T, bool WAIT_WRITE = true>
 __device__ inline int attended_length(const DenseParams& p, int b, int j, int split,
                                       LengthState& ls) {
-  const int n_raw = *static_cast<const volatile int32_t*>(p.seq_lens + b);
+  // One read; the empty asm keeps the compiler from reading it again later
+  // (in the fused kernel the last workgroup of the sequence rewrites it).
+  int n_raw = p.seq_lens[b];
+  asm volatile("" : "+v"(n_raw));
   if constexpr (!APPEND) {
     return min(max(n_raw, 0), p.L_max);
   } else {

@@ -26,13 +26,19 @@ bool good_dtype(int dtype) { return dtype == KVC_F32 || dtype == KVC_BF16; }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Dense/top-k splits: at least 256 positions (two 32-position chunks per
-// wave, so each wave keeps a second chunk in flight), and no more than about
-// 18 workgroups per compute unit of a 256-CU MI355X.  Measured on MI355X:
-// the MHA 4096-token layer runs 1.5x faster at 256 than at 128 positions,
+// Dense/top-k splits.  A small problem (the whole step fits in about one
+// round of workgroups: two per compute unit of a 256-CU MI355X, the MFMA
+// kernel's occupancy) is cut into as many equal splits as fill that round,
+// so no workgroup starts late and the merge tail is paid once; a split keeps
+// at least one 32-position chunk per wave.  A large problem uses splits of at
+// least 256 positions (two chunks per wave, so each wave keeps a second chunk
+// in flight), doubled until there are no more than about 18 workgroups per
+// CU, and relies on the hardware to balance the rounds.  Measured on MI355X:
 // the 32-sequence GQA layer is fastest at 2048.
 constexpr int64_t kDenseTargetWgs = 4608;
 constexpr int64_t kDenseMinSplit = 256;
+constexpr int64_t kDenseRound = 512;
+constexpr int64_t kDenseMinSmallSplit = 128;
 constexpr int kCUs = 256;
 
 int policy_split(int kind, int64_t B, int64_t units, int64_t n_max) {
@@ -58,6 +64,11 @@ int policy_split(int kind, int64_t B, int64_t units, int64_t n_max) {
     return (int)(S > S_cap ? S : S_cap);
   }
   int64_t S = kDenseMinSplit;
+  if (units * ceil_div(n_max, S) <= kDenseRound + kDenseRound / 4) {
+    const int64_t P = units >= kDenseRound ? 1 : kDenseRound / units;
+    S = round_up((size_t)ceil_div(n_max, P), (size_t)gran);
+    if (S < kDenseMinSmallSplit) S = kDenseMinSmallSplit;
+  }
   while (units * ceil_div(n_max, S) > kDenseTargetWgs && S < ((int64_t)1 << 24))
     S *= 2;
   const int64_t S_cap = round_up((size_t)ceil_div(n_max, kMaxSplits), (size_t)gran);

@@ -9,9 +9,9 @@
 namespace kvc {
 
 // Positions one wave consumes per step of the MFMA dense kernel, and the
-// split granularity of dense / top-k decode (4 waves x 32 positions).
+// dense / top-k decode: positions per wave-chunk.
 constexpr int kDenseChunk = 32;
-constexpr int kDenseGran = 128;
+constexpr int kDenseGran = 32;     // split sizes are whole chunks
 constexpr int kMaxGroup = 16;        // query heads per KV head a kernel serves
 // Upper bound on the splits of one sequence (the merge stages their weights
 // in LDS); the split policy raises the split size to respect it.

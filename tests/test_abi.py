@@ -83,14 +83,19 @@ def test_dense_workspace_rules(L):
 def test_split_policy_and_override(L):
     S = kvc.kvc_split_positions(kvc.KVC_KIND_DENSE, 32, 256, 32768)
     assert S % 128 == 0 and 256 * -(-32768 // S) <= 4608
-    assert kvc.kvc_split_positions(kvc.KVC_KIND_DENSE, 1, 32, 4097) == 256
+    # small problem: one round of 512 workgroups -> 16 splits of 4097, rounded to 32
+    assert kvc.kvc_split_positions(kvc.KVC_KIND_DENSE, 1, 32, 4097) == 288
+    # top-k 2048 of 64 units: 8 splits of 256
+    assert kvc.kvc_split_positions(kvc.KVC_KIND_TOPK, 8, 64, 2048) == 256
+    # tiny problem: at least 128 positions per split
+    assert kvc.kvc_split_positions(kvc.KVC_KIND_DENSE, 1, 4, 300) == 128
     # at most 256 splits per sequence
     assert kvc.kvc_split_positions(kvc.KVC_KIND_DENSE, 1, 1, 1 << 20) >= (1 << 20) // 256
     Sm = kvc.kvc_split_positions(kvc.KVC_KIND_MLA, 64, 128, 8193)
     assert Sm % 32 == 0 and Sm >= 256
     try:
         kvc.kvc_set_split_override(300)
-        assert kvc.kvc_split_positions(kvc.KVC_KIND_DENSE, 1, 1, 1000) == 384
+        assert kvc.kvc_split_positions(kvc.KVC_KIND_DENSE, 1, 1, 1000) == 320
         assert kvc.kvc_split_positions(kvc.KVC_KIND_MLA, 1, 1, 1000) == 320
     finally:
         kvc.kvc_set_split_override(0)
