@@ -218,7 +218,7 @@ __device__ inline int attended_length(const DenseParams& p, int b, int j, int sp
     ls.unit_prev = 0;
     if (threadIdx.x == 0)
       ls.unit_prev = atomicAdd(p.ws_ucnt + (size_t)b * p.n_kv + j, 1);
-    if (ok && split == n_raw / p.S) {
+    if (ok && split == dense_num_splits(n_raw + 1, dense_split_size(n_raw + 1, p.S, p.P_max, p.even)) - 1) {
       constexpr int U = D * (int)sizeof(T) / 16;    // 16-byte pieces per row
       const size_t unit = (size_t)b * p.n_kv + j;
       const size_t dst = (unit * p.L_max + n_raw) * U;
@@ -422,14 +422,15 @@ __global__ __launch_bounds__(256, 2) void dense_mfma_kernel(DenseParams p) {
   LengthState ls;
   const int n = attended_length<APPEND, 128, uint16_t, false>(p, b, j, split, ls);
   const int count = TOPK ? p.K : n;
-  const int start = split * p.S;
-  if (start >= count) {
+  const int S = dense_split_size(count, p.S, p.P_max, p.even);
+  const int nsplit = dense_num_splits(count, S);
+  if (split >= nsplit || count == 0) {
     if (split == 0) write_empty<uint16_t, 128>(p, b, j);
     complete_length<APPEND>(p, b, j, ls);
     return;
   }
-  const int end = min(count, start + p.S);
-  const int nsplit = (count + p.S - 1) / p.S;
+  int start, end;
+  dense_split_range(count, S, split, start, end);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, g = lane >> 4;
@@ -551,14 +552,15 @@ __global__ __launch_bounds__(256) void dense_generic_kernel(DenseParams p) {
   LengthState ls;
   const int n = attended_length<APPEND, D, T>(p, b, j, split, ls);
   const int count = TOPK ? p.K : n;
-  const int start = split * p.S;
-  if (start >= count) {
+  const int S = dense_split_size(count, p.S, p.P_max, p.even);
+  const int nsplit = dense_num_splits(count, S);
+  if (split >= nsplit || count == 0) {
     if (split == 0) write_empty<T, D>(p, b, j);
     complete_length<APPEND>(p, b, j, ls);
     return;
   }
-  const int end = min(count, start + p.S);
-  const int nsplit = (count + p.S - 1) / p.S;
+  int start, end;
+  dense_split_range(count, S, split, start, end);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = p.G;
 

@@ -28,29 +28,41 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Dense/top-k splits.  A small problem (the whole step fits in about one
 // round of workgroups: two per compute unit of a 256-CU MI355X, the MFMA
-// kernel's occupancy) is cut into as many equal splits as fill that round,
-// so no workgroup starts late and the merge tail is paid once; a split keeps
-// at least one 32-position chunk per wave.  A large problem uses splits of at
-// least 256 positions (two chunks per wave, so each wave keeps a second chunk
-// in flight), doubled until there are no more than about 18 workgroups per
-// CU, and relies on the hardware to balance the rounds.  Measured on MI355X:
-// the 32-sequence GQA layer is fastest at 2048.
+// kernel's occupancy) runs in "even" mode: the grid has P = 512 / units
+// splits per (sequence, KV head) and each workgroup cuts its sequence's
+// actual length into at most P equal whole-chunk splits (at least 128
+// positions), so no workgroup starts late and the merge tail is paid once.
+// A large problem uses a fixed split of at least 256 positions (two chunks
+// per wave, so each wave keeps a second chunk in flight), doubled until there
+// are no more than about 18 workgroups per CU, and relies on the hardware to
+// balance the rounds.  Measured on MI355X: the 32-sequence GQA layer is
+// fastest at 2048.  The size of a small problem is judged from L_max (the
+// lengths live on the device).
 constexpr int64_t kDenseTargetWgs = 4608;
 constexpr int64_t kDenseMinSplit = 256;
 constexpr int64_t kDenseRound = 512;
-constexpr int64_t kDenseMinSmallSplit = 128;
+constexpr int64_t kDenseMinEvenSplit = 128;
 constexpr int kCUs = 256;
 
-int policy_split(int kind, int64_t B, int64_t units, int64_t n_max) {
+int64_t dense_splits(int64_t n, int64_t S) { return dense_num_splits((int)n, (int)S); }
+
+struct SplitPlan {
+  int S;        // fixed split, or the least split in even mode
+  int64_t P;    // grid splits per unit
+  int even;
+};
+
+SplitPlan plan_splits(int kind, int64_t units, int64_t n_max) {
   const int gran = kind == KVC_KIND_MLA ? kMlaChunk : kDenseGran;
+  if (n_max < 1) n_max = 1;
+  if (units < 1) units = 1;  // empty batch: any valid split will do
+  const int64_t S_cap = round_up((size_t)ceil_div(n_max, kMaxSplits), (size_t)gran);
   const int ov = g_split_override.load();
   if (ov > 0) {
     const int64_t S = round_up((size_t)ov, (size_t)gran);
-    const int64_t S_cap = round_up((size_t)ceil_div(n_max < 1 ? 1 : n_max, kMaxSplits), (size_t)gran);
-    return (int)(S > S_cap ? S : S_cap);
+    const int Sf = (int)(S > S_cap ? S : S_cap);
+    return {Sf, kind == KVC_KIND_MLA ? ceil_div(n_max, Sf) : dense_splits(n_max, Sf), 0};
   }
-  if (n_max < 1) n_max = 1;
-  if (units < 1) units = 1;  // empty batch: any valid split will do
   if (kind == KVC_KIND_MLA) {
     // A workgroup covers 64 heads and occupies a compute unit; aim for one
     // workgroup per CU.  Each split's partial output costs n_h * d_c floats,
@@ -60,33 +72,37 @@ int policy_split(int kind, int64_t B, int64_t units, int64_t n_max) {
     if (P < 1) P = 1;
     int64_t S = round_up((size_t)ceil_div(n_max, P), (size_t)gran);
     if (S < 256) S = 256;
-    const int64_t S_cap = round_up((size_t)ceil_div(n_max, kMaxSplits), (size_t)gran);
-    return (int)(S > S_cap ? S : S_cap);
+    const int Sf = (int)(S > S_cap ? S : S_cap);
+    return {Sf, ceil_div(n_max, Sf), 0};
+  }
+  if (units * dense_splits(n_max, kDenseMinSplit) <= kDenseRound + kDenseRound / 4) {
+    int64_t P = units >= kDenseRound ? 1 : kDenseRound / units;
+    if (P > kMaxSplits) P = kMaxSplits;
+    // no more splits than n_max has minimum-size pieces
+    const int64_t P_fill = dense_splits(n_max, kDenseMinEvenSplit);
+    if (P > P_fill) P = P_fill;
+    // the splits n_max takes; every shorter length fits in as many
+    P = dense_splits(n_max, dense_split_size((int)n_max, (int)kDenseMinEvenSplit, (int)P, 1));
+    return {(int)kDenseMinEvenSplit, P, 1};
   }
   int64_t S = kDenseMinSplit;
-  if (units * ceil_div(n_max, S) <= kDenseRound + kDenseRound / 4) {
-    const int64_t P = units >= kDenseRound ? 1 : kDenseRound / units;
-    S = round_up((size_t)ceil_div(n_max, P), (size_t)gran);
-    if (S < kDenseMinSmallSplit) S = kDenseMinSmallSplit;
-  }
-  while (units * ceil_div(n_max, S) > kDenseTargetWgs && S < ((int64_t)1 << 24))
+  while (units * dense_splits(n_max, S) > kDenseTargetWgs && S < ((int64_t)1 << 24))
     S *= 2;
-  const int64_t S_cap = round_up((size_t)ceil_div(n_max, kMaxSplits), (size_t)gran);
-  return (int)(S > S_cap ? S : S_cap);
+  const int Sf = (int)(S > S_cap ? S : S_cap);
+  return {Sf, dense_splits(n_max, Sf), 0};
 }
-
-int64_t splits_for(int64_t n_max, int S) { return n_max < 1 ? 1 : ceil_div(n_max, S); }
 
 struct DenseCheck {
   int status;
   int S;
   int64_t P_max;
+  int even;
   WsLayout ws;
 };
 
 DenseCheck check_dense_shape(int B, int n_h, int n_kv, int L_max, int d,
                              int dtype, int K, bool topk, bool fused = false) {
-  DenseCheck c{KVC_OK, 0, 1, {}};
+  DenseCheck c{KVC_OK, 0, 1, 0, {}};
   if (!good_dtype(dtype)) { c.status = KVC_ERR_BAD_DTYPE; return c; }
   if (B < 0 || n_h < 1 || n_kv < 1 || L_max < 1 || d < 1) {
     c.status = KVC_ERR_BAD_SHAPE; return c;
@@ -100,8 +116,10 @@ DenseCheck check_dense_shape(int B, int n_h, int n_kv, int L_max, int d,
   if (n_h / n_kv > kMaxGroup) { c.status = KVC_ERR_UNSUPPORTED; return c; }
   const int64_t units = (int64_t)B * n_kv;
   const int64_t n_max = topk ? K : L_max;
-  c.S = policy_split(topk ? KVC_KIND_TOPK : KVC_KIND_DENSE, B, units, n_max);
-  c.P_max = splits_for(n_max, c.S);
+  const SplitPlan plan = plan_splits(topk ? KVC_KIND_TOPK : KVC_KIND_DENSE, units, n_max);
+  c.S = plan.S;
+  c.P_max = plan.P;
+  c.even = plan.even;
   if (units * c.P_max >= kMaxOffset) { c.status = KVC_ERR_BAD_SHAPE; return c; }
   c.ws = ws_layout((size_t)units, (size_t)B, (size_t)n_h, (size_t)c.P_max, (size_t)d, fused);
   if (c.ws.total >= (size_t)kMaxOffset) { c.status = KVC_ERR_UNSUPPORTED; return c; }
@@ -153,8 +171,9 @@ MlaCheck check_mla_shape(int B, int n_h, int L_max, int d_c, int d_r, int dtype)
       n_h % kMlaHeadsPerWg != 0) {
     c.status = KVC_ERR_UNSUPPORTED; return c;
   }
-  c.S = policy_split(KVC_KIND_MLA, B, (int64_t)B * (n_h / kMlaHeadsPerWg), L_max);
-  c.P_max = splits_for(L_max, c.S);
+  const SplitPlan plan = plan_splits(KVC_KIND_MLA, (int64_t)B * (n_h / kMlaHeadsPerWg), L_max);
+  c.S = plan.S;
+  c.P_max = plan.P;
   const int64_t groups = n_h / kMlaHeadsPerWg;
   if ((int64_t)B * groups * c.P_max >= kMaxOffset) { c.status = KVC_ERR_BAD_SHAPE; return c; }
   c.ws = ws_layout((size_t)B * groups, (size_t)B, (size_t)n_h, (size_t)c.P_max, (size_t)d_c);
@@ -190,7 +209,8 @@ int kvc_set_split_override(int positions) {
 int kvc_split_positions(int kind, int B, int units, int n_max) {
   if (kind < KVC_KIND_DENSE || kind > KVC_KIND_MLA || B < 1 || units < 1)
     return KVC_ERR_BAD_ARG;
-  return policy_split(kind, B, units, n_max);
+  const SplitPlan plan = plan_splits(kind, units, n_max);
+  return dense_split_size(n_max < 1 ? 1 : n_max, plan.S, (int)plan.P, plan.even);
 }
 
 int kvc_append(void* k_cache, void* v_cache, int32_t* seq_lens,
@@ -257,7 +277,7 @@ static int dense_common(const void* q, const void* k_cache, const void* v_cache,
   p.flag = (topk || fused) ? flag : nullptr;
   p.B = B; p.n_h = n_h; p.n_kv = n_kv; p.G = n_h / n_kv; p.L_max = L_max;
   fill_ws(p, c.ws, workspace, (size_t)c.P_max, fused);
-  p.d = d; p.K = topk ? K : 0; p.S = c.S; p.P_max = (int)c.P_max;
+  p.d = d; p.K = topk ? K : 0; p.S = c.S; p.P_max = (int)c.P_max; p.even = c.even;
   p.scale_log2 = scale * 1.4426950408889634f;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dtype == KVC_BF16 && d == 128) return launch_status(launch_dense_mfma(p, topk, fused, s));

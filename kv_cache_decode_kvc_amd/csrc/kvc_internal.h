@@ -59,8 +59,9 @@ struct DenseParams {
   float* ws_o;            // [B * n_h * P_max * d] normalised partial outputs
   int B, n_h, n_kv, G, L_max, d;
   int K;                  // top-k list length (0 for dense)
-  int S;                  // positions per split
+  int S;                  // positions per split (even mode: the least)
   int P_max;              // splits per (b, kv head) in the grid
+  int even;               // 1: spread each sequence over the P_max splits
   float scale_log2;       // scale * log2(e)
 };
 
@@ -83,6 +84,23 @@ struct WsLayout {
 };
 
 inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Dense / top-k split geometry: split s holds positions [s*S, min(n, (s+1)*S)).
+__host__ __device__ inline int dense_num_splits(int n, int S) {
+  return n <= 0 ? 1 : (n + S - 1) / S;
+}
+// Split size for a sequence of n positions.  Fixed mode: S.  Even mode: the
+// least whole-chunk size (not below S) that fits n into P splits.
+__host__ __device__ inline int dense_split_size(int n, int S, int P, int even) {
+  if (!even) return S;
+  int Sn = (n + P - 1) / P;
+  Sn = (Sn + 31) / 32 * 32;
+  return Sn > S ? Sn : S;
+}
+__host__ __device__ inline void dense_split_range(int n, int S, int split, int& start, int& end) {
+  start = split * S;
+  end = start + S < n ? start + S : n;
+}
 
 // Workspace: [tickets per unit][partial lse][partial outputs] when a
 // sequence can need several splits, then (fused append-and-attend only) one

@@ -83,8 +83,10 @@ def test_dense_workspace_rules(L):
 def test_split_policy_and_override(L):
     S = kvc.kvc_split_positions(kvc.KVC_KIND_DENSE, 32, 256, 32768)
     assert S % 128 == 0 and 256 * -(-32768 // S) <= 4608
-    # small problem: one round of 512 workgroups -> 16 splits of 4097, rounded to 32
+    # small problem: one round of 512 workgroups -> at most 16 splits of 4097,
+    # whole chunks: 288 (15 splits)
     assert kvc.kvc_split_positions(kvc.KVC_KIND_DENSE, 1, 32, 4097) == 288
+    assert kvc.kvc_split_positions(kvc.KVC_KIND_DENSE, 1, 32, 4096) == 256
     # top-k 2048 of 64 units: 8 splits of 256
     assert kvc.kvc_split_positions(kvc.KVC_KIND_TOPK, 8, 64, 2048) == 256
     # tiny problem: at least 128 positions per split
