@@ -64,10 +64,10 @@ SplitPlan plan_splits(int kind, int64_t units, int64_t n_max) {
     return {Sf, kind == KVC_KIND_MLA ? ceil_div(n_max, Sf) : dense_splits(n_max, Sf), 0};
   }
   if (kind == KVC_KIND_MLA) {
-    // A workgroup covers 64 heads and occupies a compute unit; aim for one
-    // workgroup per CU.  Each split's partial output costs n_h * d_c floats,
-    // so keep splits at least 256 positions long.  `units` counts
-    // (sequence, 64-head group) pairs.
+    // A workgroup covers 64 or 128 heads and occupies a compute unit; aim
+    // for one workgroup per CU.  Each split's partial output costs n_h * d_c
+    // floats, so keep splits at least 256 positions long.  `units` counts
+    // (sequence, head group) pairs.
     int64_t P = ceil_div(kCUs, units);
     if (P < 1) P = 1;
     int64_t S = round_up((size_t)ceil_div(n_max, P), (size_t)gran);
@@ -171,10 +171,10 @@ MlaCheck check_mla_shape(int B, int n_h, int L_max, int d_c, int d_r, int dtype)
       n_h % kMlaHeadsPerWg != 0) {
     c.status = KVC_ERR_UNSUPPORTED; return c;
   }
-  const SplitPlan plan = plan_splits(KVC_KIND_MLA, (int64_t)B * (n_h / kMlaHeadsPerWg), L_max);
+  const SplitPlan plan = plan_splits(KVC_KIND_MLA, (int64_t)B * (n_h / mla_heads_per_wg(n_h)), L_max);
   c.S = plan.S;
   c.P_max = plan.P;
-  const int64_t groups = n_h / kMlaHeadsPerWg;
+  const int64_t groups = n_h / mla_heads_per_wg(n_h);
   if ((int64_t)B * groups * c.P_max >= kMaxOffset) { c.status = KVC_ERR_BAD_SHAPE; return c; }
   c.ws = ws_layout((size_t)B * groups, (size_t)B, (size_t)n_h, (size_t)c.P_max, (size_t)d_c);
   if (c.ws.total >= (size_t)kMaxOffset) { c.status = KVC_ERR_UNSUPPORTED; return c; }

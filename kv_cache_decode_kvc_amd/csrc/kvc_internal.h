@@ -23,9 +23,10 @@ constexpr float kRescaleMargin = 8.0f;
 // MLA kernel: positions per step (also the split granularity); a workgroup
 // of 8 waves (two per SIMD) covers 64 heads, two waves sharing each 16.
 constexpr int kMlaChunk = 32;
-constexpr int kMlaHeadsPerWave = 16;
-constexpr int kMlaWaves = 8;
-constexpr int kMlaHeadsPerWg = 64;
+constexpr int kMlaHeadsPerWave = 32;
+constexpr int kMlaHeadsPerWg = 64;      // n_h must be a multiple of this
+// Heads one MLA workgroup covers: 128 (4 waves) when n_h allows, else 64.
+inline int mla_heads_per_wg(int n_h) { return n_h % 128 == 0 ? 128 : 64; }
 constexpr int kMlaDc = 512;
 constexpr int kMlaDr = 64;
 

@@ -285,7 +285,41 @@ def test_mla_parity(B, n_h, pre, L_max, split):
     compare(host_f64(out), o_ref, 2e-2, f"mla B{B} h{n_h} split{split}")
     compare_lse(host(lse), l_ref, lse_tol("bf16"))
     if ws is not None:
-        assert int(ws[:4 * B * (n_h // 64)].view(torch.int32).abs().sum()) == 0
+        groups = n_h // (128 if n_h % 128 == 0 else 64)
+        assert int(ws[:4 * B * groups].view(torch.int32).abs().sum()) == 0
+
+
+@pytest.mark.parametrize("n_h", [128, 64])
+@pytest.mark.parametrize("split", [0, 96])
+def test_mla_score_jump(n_h, split):
+    """Rows whose score lies far above every earlier score of the split (by
+    about 90 and about 1200 in log2 units): the weights must not overflow
+    and the result is the exact softmax, dominated by those rows."""
+    B, L_max, pre = 2, 400, [300, 390]
+    case = syn.mla_case(B, n_h, 512, 64, L_max, pre, "bf16", cfg_id=98)
+    ckv, qb = case["ckv"], case["q"]
+    qf = oracle.bf16_to_f64(qb).astype(np.float32)
+    ckv[0, 200:204, :512] = syn.bf16_bits(3.0 * qf[0, 5, :512])
+    ckv[0, 200:204, 512:] = syn.bf16_bits(np.zeros(64, np.float32))
+    ckv[1, 350:352, :512] = syn.bf16_bits(40.0 * qf[1, 7, :512])
+    ckv[1, 350:352, 512:] = syn.bf16_bits(np.zeros(64, np.float32))
+    ckv_d, sl = dev(ckv), dev(case["seq_lens"])
+    q = dev(qb)
+    out = torch.empty(B, n_h, 512, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(B, n_h, dtype=torch.float32, device="cuda")
+    kvc.kvc_set_split_override(split)
+    ws = kvc.workspace(kvc.kvc_decode_attn_mla_workspace_size(B, n_h, L_max, 512, 64, 1))
+    kvc.kvc_decode_attn_mla(q, ckv_d, sl, out, lse, scale=1 / 24, workspace=ws)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.decode_mla(qb, ckv, case["seq_lens"], 512, 64, 1 / 24)
+    assert l_ref[0, 5] > 50 and l_ref[1, 7] > 500   # the jumps are real (natural log units)
+    got = host_f64(out)
+    assert np.isfinite(got).all()
+    # the dominated heads' outputs are 3x and 40x a query row: bf16 rounding
+    # of the output is relative, so scale the 2e-2 contract by max(1, |o|)
+    mag = np.maximum(1.0, np.abs(o_ref))
+    compare(got / mag, o_ref / mag, 2e-2, f"mla jump h{n_h} split{split}")
+    compare_lse(host(lse), l_ref, 4e-3 * max(1.0, float(np.abs(l_ref).max()) / 100))
 
 
 # ------------------------------------------------------------------ causal
