@@ -24,17 +24,17 @@
 //          16(i / 8) + 8g + i % 8, i.e. the B operand of the value product.
 //  weights softmax numerators 2^(s - m_ref) in log2 units against a fixed
 //          per-head reference (see the pass loop below).
-//  values  O^T[c][h] += C^T[c][t] P^T[t][h]: 16 column tiles x 2 k-steps.
-//          The A operand (8 positions of one column per lane) comes straight
-//          from LDS transposed by ds_read_b64_tr_b16: in each 16-lane group,
-//          lane i receives element i % 4 of the 8-byte pieces addressed by
-//          lanes i / 4, 4 + i / 4, 8 + i / 4 and 12 + i / 4.
+//  values  O^T[c][h] += C^T[c][t] P^T[t][h]: 16 column tiles x 2 k-steps;
+//          lane (r, g) reads rows 16 s + 8g + 0..7 x 16 B at columns
+//          256cb + 8r and transposes 8 x 8 bf16 in registers (v_perm), so
+//          tile (cb, m) row r is column 256cb + 8r + m.  (The transposing LDS
+//          read has no alias information for the compiler, which then waits
+//          for every tile copy in flight before it; plain reads do not.)
 //
-// Latent tiles go HBM -> LDS directly (buffer_load ... lds), four stages (two
-// tiles in flight while two are read), with 16-byte piece k of row rho stored
+// Latent tiles go HBM -> LDS directly (buffer_load ... lds), three stages (two
+// tiles in flight while one is read), with 16-byte piece k of row rho stored
 // at k ^ key(rho), key = bit-reverse of (rho >> 1) & 7: conflict-free for
-// both the 16-byte score reads and the 8-byte transposed reads on the 64-bank
-// LDS.  Rows at or past the sequence length read as zeros (buffer range
+// the 16-byte score and value reads on the 64-bank LDS.  Rows at or past the sequence length read as zeros (buffer range
 // check) and are masked.  Splits of one sequence are merged by log-sum-exp by
 // the last workgroup to finish.
 
@@ -48,17 +48,23 @@ namespace {
 constexpr int kD = kMlaDc + kMlaDr;          // 576
 constexpr int kRowB = kD * 2;                // 1152 bytes per row
 constexpr int kTileB = kMlaChunk * kRowB;    // 36864 bytes per chunk
-constexpr int kStages = 4;
+constexpr int kStages = 3;
 constexpr int kKSteps = kD / 16;             // 36
 constexpr int kColTiles = kMlaDc / 32;       // 16
-constexpr size_t kMlaLds = (size_t)kStages * kTileB;
+// The last kQPark query k-steps wait in LDS (per wave and lane, 1 KB per
+// k-step), which keeps the wave within the register file.
+constexpr int kQPark = 12;
+constexpr int kQRegs = kKSteps - kQPark;
+constexpr size_t kParkOff = (size_t)kStages * kTileB;
+constexpr size_t kMlaLds = kParkOff + 4 * kQPark * 1024;
 // Weights may reach 2^kMlaRefMargin against the reference (bf16 and fp32
 // hold that with room to spare: 8193 * 2^64 * |c| stays far below 2^128).
 constexpr float kMlaRefMargin = 64.0f;
+// LDS reads in flight ahead of the MFMA that consumes them (hides the LDS
+// latency behind earlier MFMAs of the same wave).
+constexpr int kQkAhead = 4;
 
 typedef __attribute__((address_space(3))) void lds_void;
-typedef short v4s __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4s lds_v4s;
 
 __device__ constexpr int swz_key(int row) {
   const int x = (row >> 1) & 7;
@@ -90,9 +96,6 @@ __device__ inline u32x4 lds_load16(const char* base, uint32_t off) {
   return *reinterpret_cast<const u32x4*>(base + off);
 }
 
-__device__ inline v4s lds_load_tr(const char* base, uint32_t off) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(base + off));
-}
 
 // s_waitcnt vmcnt(N) for N < 64 (gfx9 encoding: vmcnt bits 3:0 and 15:14;
 // expcnt and lgkmcnt left at maximum).
@@ -123,11 +126,6 @@ __device__ inline bool any_vote(const int* v) {
   return x != 0;
 }
 
-__device__ inline bf16x8 cat_tr(v4s lo, v4s hi) {
-  typedef short v8s __attribute__((ext_vector_type(8)));
-  const v8s v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  return __builtin_bit_cast(bf16x8, v);
-}
 
 }  // namespace
 
@@ -187,35 +185,33 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_kernel(MlaParams p) {
     for (int m = 0; m < 4; ++m)
       wqk[m] = (uint32_t)(row * kRowB + (((2 * m + g) ^ swz_key(row)) << 4));
   }
-  // Values, k-step s, half t, column tile ct: 16-lane group q16 = lane / 16,
-  // L = lane % 16 addresses row 16s + 8g + 4t + L / 4, columns
-  // 32ct + 16(q16 % 2) + 4(L % 4) .. +4, i.e. logical piece
-  // 4ct + 2(q16 % 2) + (L / 2) % 2, half L % 2.  The key does not depend on
-  // s; base by (t, ct % 2), plus 16s rows and 128(ct / 2).
-  uint32_t wpv[2][2];
-  {
-    const int q16 = lane >> 4, L = lane & 15;
+  // Values, k-step s2, column block cb: lane (r, g) reads rows
+  // 16 s2 + 8g + jj (jj = 0..7), logical piece 32cb + r (columns
+  // 256cb + 8r .. +8), stored at 32cb + 8(r / 8) + ((r % 8) ^ key(row)).  The
+  // key depends on (g, jj / 2) only: base by jj / 2, plus (jj % 2) rows,
+  // 16 s2 rows and 512 cb.
+  uint32_t wpv[4];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int row = 8 * g + 4 * t + (L >> 2);
-      const int key = swz_key(row);
-#pragma unroll
-      for (int cp = 0; cp < 2; ++cp)
-        wpv[t][cp] = (uint32_t)(row * kRowB +
-                                (((4 * cp + 2 * (q16 & 1) + ((L >> 1) & 1)) ^ key) << 4) +
-                                8 * (L & 1));
-    }
+  for (int q4 = 0; q4 < 4; ++q4) {
+    const int row = 8 * g + 2 * q4;
+    wpv[q4] = (uint32_t)(row * kRowB + ((8 * (r >> 3) + ((r & 7) ^ swz_key(row))) << 4));
   }
 
-  bf16x8 qop[kKSteps];
+  bf16x8 qop[kQRegs];
+  const uint32_t qpark = (uint32_t)(kParkOff + (wave * kQPark * 64 + lane) * 16);
   {
     const uint16_t* qrow = (const uint16_t*)p.q + bh * kD;
 #pragma unroll
-    for (int k = 0; k < kKSteps; ++k)
+    for (int k = 0; k < kQRegs; ++k)
       qop[k] = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow + k * 16 + g * 8));
+#pragma unroll
+    for (int k = kQRegs; k < kKSteps; ++k)
+      *reinterpret_cast<u32x4*>(smem + qpark + (k - kQRegs) * 1024) =
+          *reinterpret_cast<const u32x4*>(qrow + k * 16 + g * 8);
   }
 
-  // scores of one chunk (stage offset toff)
+  // Scores of one chunk (stage offset toff).  The LDS reads run kQkAhead
+  // k-steps ahead of the MFMAs; the scheduling barriers keep that order.
   auto scores = [&](uint32_t toff) {
     uint32_t qb[4];
 #pragma unroll
@@ -226,10 +222,23 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_kernel(MlaParams p) {
     f32x16 s;
 #pragma unroll
     for (int i = 0; i < 16; ++i) s[i] = 0.f;
+    // A: latent rows; Bq: parked query k-steps (k >= kQRegs)
+    u32x4 A[kQkAhead], Bq[kQkAhead];
+#pragma unroll
+    for (int k = 0; k < kQkAhead; ++k) {
+      A[k] = lds_load16(smem, qb[k & 3] + (k >> 2) * 128);
+      if (k >= kQRegs) Bq[k] = lds_load16(smem, qpark + (k - kQRegs) * 1024);
+    }
 #pragma unroll
     for (int k = 0; k < kKSteps; ++k) {
-      const u32x4 a = lds_load16(smem, qb[k & 3] + (k >> 2) * 128);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), qop[k], s, 0, 0, 0);
+      const bf16x8 bop = k < kQRegs ? qop[k < kQRegs ? k : 0] : as_bf16x8(Bq[k % kQkAhead]);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(A[k % kQkAhead]), bop, s, 0, 0, 0);
+      const int kn = k + kQkAhead;
+      if (kn < kKSteps) {
+        A[k % kQkAhead] = lds_load16(smem, qb[kn & 3] + (kn >> 2) * 128);
+        if (kn >= kQRegs) Bq[k % kQkAhead] = lds_load16(smem, qpark + (kn - kQRegs) * 1024);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
     return s;
   };
@@ -255,31 +264,28 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_kernel(MlaParams p) {
     issue_tile<kLpt>(smem, cr, start, blk0, lane);
     if (nchunks > 1) issue_tile<kLpt>(smem + kTileB, cr, start + kMlaChunk, blk0, lane);
     if (nchunks > 2) issue_tile<kLpt>(smem + 2 * kTileB, cr, start + 2 * kMlaChunk, blk0, lane);
+    // (tile k >= 3 is issued at the top of chunk k - 2, into the stage of
+    // chunk k - 3)
 
     float m_seen = m_ref;     // largest score of this head in this pass
     bool restart = false;
     for (int c = 0; c < nchunks; ++c) {
       const int cs = start + c * kMlaChunk;
-      // Tile c landed (tiles c + 1, c + 2 may still be in flight); every
-      // wave is done with stage (c + 3) % 4, last read for chunk c - 1, and
-      // has cast its vote on chunk c - 1.
-      if (c + 2 < nchunks) wait_vmcnt<2 * kLpt>();
+      // Tile c landed (tiles issued after it: c + 1, and c + 2 on the first
+      // chunk, may still be in flight); every wave is done with the stage of
+      // chunk c - 1 and has cast its vote on it.
+      if (c == 0 && nchunks > 2) wait_vmcnt<2 * kLpt>();
       else if (c + 1 < nchunks) wait_vmcnt<kLpt>();
       else wait_vmcnt<0>();
       lds_barrier();
       if (c > 0 && !scan && !scanned) {
         if (any_vote<NW>(s_vote[(c - 1) & 1])) { restart = true; break; }
       }
-      if (c + 3 < nchunks)
-        issue_tile<kLpt>(smem + ((c + 3) % kStages) * kTileB, cr, cs + 3 * kMlaChunk, blk0, lane);
+      if (c >= 1 && c + 2 < nchunks)
+        issue_tile<kLpt>(smem + ((c + 2) % kStages) * kTileB, cr, cs + 2 * kMlaChunk, blk0, lane);
       const uint32_t toff = (uint32_t)((c % kStages) * kTileB);
 
       const f32x16 S = scores(toff);
-#pragma unroll
-      for (int k = 0; k < kKSteps; ++k) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-      }
 
       // weights of this lane's 16 positions of head r
       float sv[16];
@@ -314,29 +320,36 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_kernel(MlaParams p) {
       }
       l_run += psum;
 
-      // weighted sum of the latents of chunk c
-      uint32_t pb[2][2];
+      // weighted sum of the latents of chunk c: per column block cb and
+      // k-step s2, 8 row reads (16 B each) and an 8 x 8 register transpose
+      // give the A operands of 8 MFMAs (tiles cb * 8 + m)
+      uint32_t pb[4];
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int cp = 0; cp < 2; ++cp) {
-          pb[t][cp] = toff + wpv[t][cp];
-          asm volatile("" : "+v"(pb[t][cp]));
-        }
+      for (int q4 = 0; q4 < 4; ++q4) {
+        pb[q4] = toff + wpv[q4];
+        asm volatile("" : "+v"(pb[q4]));
+      }
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
 #pragma unroll
-        for (int ct = 0; ct < kColTiles; ++ct) {
-          const uint32_t o = s2 * 16 * kRowB + (ct >> 1) * 128;
-          const v4s lo = lds_load_tr(smem, pb[0][ct & 1] + o);
-          const v4s hi = lds_load_tr(smem, pb[1][ct & 1] + o);
-          acc[ct] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cat_tr(lo, hi), pop[s2], acc[ct], 0, 0, 0);
-        }
-      }
+        for (int cb = 0; cb < 2; ++cb) {
+          u32x4 vr[8];
 #pragma unroll
-      for (int k = 0; k < 2 * kColTiles; ++k) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // LDS reads
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+          for (int jj = 0; jj < 8; ++jj)
+            vr[jj] = lds_load16(smem, pb[jj >> 1] + (jj & 1) * kRowB + s2 * 16 * kRowB + cb * 512);
+#pragma unroll
+          for (int m = 0; m < 8; ++m) {
+            const uint32_t sel = (m & 1) ? 0x07060302u : 0x05040100u;
+            const int dw = m >> 1;
+            u32x4 a;
+            a[0] = __builtin_amdgcn_perm(vr[1][dw], vr[0][dw], sel);
+            a[1] = __builtin_amdgcn_perm(vr[3][dw], vr[2][dw], sel);
+            a[2] = __builtin_amdgcn_perm(vr[5][dw], vr[4][dw], sel);
+            a[3] = __builtin_amdgcn_perm(vr[7][dw], vr[6][dw], sel);
+            acc[cb * 8 + m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), pop[s2],
+                                                                       acc[cb * 8 + m], 0, 0, 0);
+          }
+        }
       }
     }
     if (scan) {
@@ -358,8 +371,8 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_kernel(MlaParams p) {
     lds_barrier();
   }
 
-  // This split's result for head h: lane (r, g) holds columns
-  // 32ct + 8a + 4g + e in acc[ct][4a + e].
+  // This split's result for head h: lane (r, g) holds column
+  // 256cb + 8(8a + 4g + e) + m in acc[cb * 8 + m][4a + e].
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const float lse2 = l_tot > 0.f ? m_ref + __log2f(l_tot) : kNegInf;
@@ -367,12 +380,15 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_kernel(MlaParams p) {
   if (nsplit == 1) {
     uint16_t* o = (uint16_t*)p.out + bh * kMlaDc;
 #pragma unroll
-    for (int ct = 0; ct < kColTiles; ++ct)
+    for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const uint2 v = {pack_bf16x2(acc[ct][4 * a] * inv, acc[ct][4 * a + 1] * inv),
-                         pack_bf16x2(acc[ct][4 * a + 2] * inv, acc[ct][4 * a + 3] * inv)};
-        *reinterpret_cast<uint2*>(o + 32 * ct + 8 * a + 4 * g) = v;
+      for (int i = 0; i < 16; ++i) {
+        const int col = 256 * cb + 8 * (8 * (i >> 2) + 4 * g + (i & 3));
+        u32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          v[e] = pack_bf16x2(acc[cb * 8 + 2 * e][i] * inv, acc[cb * 8 + 2 * e + 1][i] * inv);
+        *reinterpret_cast<u32x4*>(o + col) = v;
       }
     if (p.lse && g == 0) p.lse[bh] = lse2 * kLn2;
     return;
@@ -380,72 +396,85 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_kernel(MlaParams p) {
 
   // Several splits: publish this one with device-coherent stores; the last
   // workgroup of the (sequence, head group) to take a ticket merges them.
+  // A split's partial block is in register order: slot k of lane l of wave w
+  // (k = 4 * tile + quad, 64 slots of 4 floats) is at ((w * 64 + k) * 64 + l)
+  // * 4 floats, so every store and load moves 1 KB contiguous per wave.
   const __amdgpu_buffer_rsrc_t wo = make_rsrc(p.ws_o, kWsRecords);
   const __amdgpu_buffer_rsrc_t wl = make_rsrc(p.ws_lse, kWsRecords);
+  const size_t unit_hg = (size_t)b * groups + hg;
+  constexpr size_t kBlock = (size_t)NW * 64 * 256;     // floats per split block
+  const uint32_t lane_off = (uint32_t)((wave * 64 * 64 + lane) * 16);
   {
-    const size_t row = (bh * p.P_max + split) * kMlaDc;
+    const uint32_t blk = (uint32_t)((unit_hg * p.P_max + split) * kBlock * 4);
 #pragma unroll
-    for (int ct = 0; ct < kColTiles; ++ct)
+    for (int t = 0; t < kColTiles; ++t)
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const f32x4 v = {acc[ct][4 * a] * inv, acc[ct][4 * a + 1] * inv,
-                         acc[ct][4 * a + 2] * inv, acc[ct][4 * a + 3] * inv};
-        store_coherent(wo, (uint32_t)((row + 32 * ct + 8 * a + 4 * g) * 4), v);
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4 v = {acc[t][4 * q4] * inv, acc[t][4 * q4 + 1] * inv,
+                         acc[t][4 * q4 + 2] * inv, acc[t][4 * q4 + 3] * inv};
+        store_coherent(wo, blk + lane_off + (uint32_t)((4 * t + q4) * 64 * 16), v);
       }
-    if (g == 0) store_coherent(wl, (uint32_t)((bh * p.P_max + split) * 4), lse2);
+    if (g == 0)
+      store_coherent(wl, (uint32_t)(((unit_hg * p.P_max + split) * kHpw + wave * 32 + r) * 4), lse2);
   }
   wait_vm_all();
   __syncthreads();
-  int32_t* ticket = p.ws_cnt + (size_t)b * groups + hg;
+  int32_t* ticket = p.ws_cnt + unit_hg;
   if (tid == 0) s_last = (atomicAdd(ticket, 1) == nsplit - 1);
   __syncthreads();
   if (!s_last) return;
 
-  // Last split to finish: merge every split of head h (its own included)
-  // from the workspace, 4 column tiles at a time with all their loads in
+  // Last split to finish: every lane combines the same slots of all the
+  // splits' blocks (its own included) by log-sum-exp weights, 8 slots (one
+  // column block cb, quad q4) at a time with the loads of up to 4 splits in
   // flight together.
-  const size_t base = bh * p.P_max;
+  const size_t lse_base = unit_hg * p.P_max * kHpw + wave * 32 + r;
   float M = kNegInf;
-  for (int s2 = 0; s2 < nsplit; ++s2) M = fmaxf(M, load_coherent1(wl, (uint32_t)((base + s2) * 4)));
+  for (int s2 = 0; s2 < nsplit; ++s2)
+    M = fmaxf(M, load_coherent1(wl, (uint32_t)((lse_base + (size_t)s2 * kHpw) * 4)));
   const float Mu = (M == kNegInf) ? 0.f : M;
   float Z = 0.f;
   for (int s2 = 0; s2 < nsplit; ++s2) {
-    const float ls = load_coherent1(wl, (uint32_t)((base + s2) * 4));
+    const float ls = load_coherent1(wl, (uint32_t)((lse_base + (size_t)s2 * kHpw) * 4));
     Z += ls == kNegInf ? 0.f : __builtin_amdgcn_exp2f(ls - Mu);
   }
   const float zi = Z > 0.f ? 1.f / Z : 0.f;
-  uint16_t* o = (uint16_t*)p.out + bh * kMlaDc;
-#pragma unroll 1
-  for (int c0 = 0; c0 < kColTiles; c0 += 4) {
-    f32x4 sum[4][4];
+  uint16_t* orow = (uint16_t*)p.out + bh * kMlaDc;
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct)
+  for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
-      for (int a = 0; a < 4; ++a) sum[ct][a] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int s2 = 0; s2 < nsplit; ++s2) {
-      const float ls = load_coherent1(wl, (uint32_t)((base + s2) * 4));
-      const float w = (ls == kNegInf ? 0.f : __builtin_amdgcn_exp2f(ls - Mu)) * zi;
-      const size_t row = (base + s2) * kMlaDc;
-      f32x4 v[4][4];
+    for (int q4 = 0; q4 < 4; ++q4) {
+      f32x4 sum[8];
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct)
+      for (int m = 0; m < 8; ++m) sum[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int s0 = 0; s0 < nsplit; s0 += 4) {
+        f32x4 v[4][8];
+        float w[4];
 #pragma unroll
-        for (int a = 0; a < 4; ++a)
-          v[ct][a] = load_coherent4(wo, (uint32_t)((row + 32 * (c0 + ct) + 8 * a + 4 * g) * 4));
+        for (int u = 0; u < 4; ++u) {
+          const int su = min(s0 + u, nsplit - 1);
+          const float ls = load_coherent1(wl, (uint32_t)((lse_base + (size_t)su * kHpw) * 4));
+          w[u] = (s0 + u >= nsplit || ls == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(ls - Mu);
+          const uint32_t blk = (uint32_t)((unit_hg * p.P_max + su) * kBlock * 4) + lane_off;
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct)
+          for (int m = 0; m < 8; ++m)
+            v[u][m] = load_coherent4(wo, blk + (uint32_t)((4 * (cb * 8 + m) + q4) * 64 * 16));
+        }
 #pragma unroll
-        for (int a = 0; a < 4; ++a) sum[ct][a] += w * v[ct][a];
-    }
+        for (int u = 0; u < 4; ++u)
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const uint2 v = {pack_bf16x2(sum[ct][a][0], sum[ct][a][1]),
-                         pack_bf16x2(sum[ct][a][2], sum[ct][a][3])};
-        *reinterpret_cast<uint2*>(o + 32 * (c0 + ct) + 8 * a + 4 * g) = v;
+          for (int m = 0; m < 8; ++m) sum[m] += w[u] * v[u][m];
       }
-  }
+      // slot (cb*8 + m, q4) element e is column 256cb + 8(8 q4 + 4g + e) + m
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        u32x4 o;
+#pragma unroll
+        for (int mm = 0; mm < 4; ++mm)
+          o[mm] = pack_bf16x2(sum[2 * mm][e] * zi, sum[2 * mm + 1][e] * zi);
+        *reinterpret_cast<u32x4*>(orow + 256 * cb + 8 * (8 * q4 + 4 * g + e)) = o;
+      }
+    }
   if (p.lse && g == 0) p.lse[bh] = Z > 0.f ? (M + __log2f(Z)) * kLn2 : kNegInf;
   if (tid == 0) *ticket = 0;
 }
