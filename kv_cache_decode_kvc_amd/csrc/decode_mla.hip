@@ -289,31 +289,35 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_kernel(MlaParams p) {
 
       // weights of this lane's 16 positions of head r
       float sv[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sv[i] = S[i] * scale_log2;
+      if (cs + kMlaChunk > end) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (cs + 16 * (i >> 3) + 8 * g + (i & 7) >= end) sv[i] = kNegInf;
+      }
       float mx = kNegInf;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int pos = cs + 16 * (i >> 3) + 8 * g + (i & 7);
-        sv[i] = pos < end ? S[i] * scale_log2 : kNegInf;
-        mx = fmaxf(mx, sv[i]);
-      }
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sv[i]);
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       m_seen = fmaxf(m_seen, mx);
       if (scan) continue;
       if (m_ref == kNegInf) m_ref = mx;       // first valid chunk (nothing accumulated yet)
       const bool over = mx > m_ref + kMlaRefMargin;
       const int vote = __any(over) ? 1 : 0;
-      if (lane == 0) s_vote[c & 1][wave] = vote;
+      s_vote[c & 1][wave] = vote;
       const float m_use = (m_ref == kNegInf) ? 0.f : m_ref;
       bf16x8 pop[2];
+      const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
       float psum = 0.f;
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
         uint32_t pp[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          pp[e] = pack_bf16x2(__builtin_amdgcn_exp2f(fminf(sv[8 * s2 + 2 * e] - m_use, kMlaRefMargin)),
-                              __builtin_amdgcn_exp2f(fminf(sv[8 * s2 + 2 * e + 1] - m_use, kMlaRefMargin)));
-          psum += bf16_lo(pp[e]) + bf16_hi(pp[e]);
+          pp[e] = pack_bf16x2(__builtin_amdgcn_exp2f(sv[8 * s2 + 2 * e] - m_use),
+                              __builtin_amdgcn_exp2f(sv[8 * s2 + 2 * e + 1] - m_use));
+          psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pp[e]), ones, psum, false);
         }
         const u32x4 pv = {pp[0], pp[1], pp[2], pp[3]};
         pop[s2] = as_bf16x8(pv);
