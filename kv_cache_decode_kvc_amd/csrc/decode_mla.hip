@@ -303,6 +303,9 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_kernel(MlaParams p) {
       m_seen = fmaxf(m_seen, mx);
       if (scan) continue;
       if (m_ref == kNegInf) m_ref = mx;       // first valid chunk (nothing accumulated yet)
+      // (every lane writes the wave's vote; a score this far above the
+      // reference may overflow the weights below, and the vote discards the
+      // pass)
       const bool over = mx > m_ref + kMlaRefMargin;
       const int vote = __any(over) ? 1 : 0;
       s_vote[c & 1][wave] = vote;
@@ -322,7 +325,7 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_kernel(MlaParams p) {
         const u32x4 pv = {pp[0], pp[1], pp[2], pp[3]};
         pop[s2] = as_bf16x8(pv);
       }
-      l_run += psum;
+      l_run += psum;      // the rounded weights' sum (bf16 dot with ones)
 
       // weighted sum of the latents of chunk c: per column block cb and
       // k-step s2, 8 row reads (16 B each) and an 8 x 8 register transpose
