@@ -27,6 +27,14 @@ What it computes, and where the pages say so:
 * Podcast transcript (my-weird-prompts 640482), DeepSeek Sparse Attention
   passage: a top-k subset of stored positions is read; attention runs over
   those positions only.
+* "KV cache" guide, "Fewer bits per number", and the podcast's KV
+  quantization passage: the cache may be stored at lower precision, FP8
+  being the common choice, one byte per number.  Reading (the pages name no
+  layout): OCP FP8 E4M3 in its finite variant (the format whose largest
+  value, 448, the DeepSeek FP4 section multiplies by 6), one float scale
+  per tensor (keys, values); a stored number is code value x scale, and a
+  new row is quantised as x * (1 / scale) in float32, rounded to nearest
+  even and saturated to +-448.
 * Podcast transcript, decode walk-through: each new token attends to the
   cache plus its own new pair, and its key and value are appended.  The
   oracle appends first and then attends over [0, seq_len), which is the
@@ -270,3 +278,86 @@ def merge_partials(os_, lses):
     Z = w.sum()
     o = sum(wi * np.asarray(oi, dtype=np.float64) for wi, oi in zip(w, os_)) / Z
     return o, M + math.log(Z)
+
+
+# --------------------------------------------------------------------------
+# FP8 E4M3 storage (guide "Fewer bits per number"; podcast KV quantization)
+# --------------------------------------------------------------------------
+FP8_E4M3_MAX = 448.0
+
+
+def fp8_e4m3_to_f64(codes: np.ndarray) -> np.ndarray:
+    """E4M3 bit patterns (uint8) -> float64, exactly.
+
+    Bit fields s eeee mmm, exponent bias 7.  e = 0: subnormal m * 2^-9;
+    e = 15 with m = 7: NaN (the finite variant has no infinities); otherwise
+    (1 + m/8) * 2^(e-7).
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where((c >> 7) & 1, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = c & 7
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    val = sign * mag
+    return np.where((e == 15) & (m == 7), np.nan, val)
+
+
+_FP8_POS = None
+
+
+def _fp8_positive_values():
+    """Values of the finite non-negative codes 0x00..0x7E (increasing)."""
+    global _FP8_POS
+    if _FP8_POS is None:
+        _FP8_POS = fp8_e4m3_to_f64(np.arange(0x7F, dtype=np.uint8))
+    return _FP8_POS
+
+
+def f64_to_fp8_e4m3(x: np.ndarray) -> np.ndarray:
+    """Round to the nearest E4M3 value, ties to the even code, saturating
+    to +-448; NaN -> 0x7F.  Sign is kept for zero."""
+    x = np.asarray(x, dtype=np.float64)
+    vals = _fp8_positive_values()
+    a = np.minimum(np.abs(x), FP8_E4M3_MAX)
+    hi = np.clip(np.searchsorted(vals, a, side="left"), 0, 0x7E)
+    lo = np.maximum(hi - 1, 0)
+    d_lo = a - vals[lo]
+    d_hi = vals[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo)
+    code = np.where(a == vals[hi], hi, code)
+    out = code.astype(np.uint8) | np.where(np.signbit(x), 0x80, 0).astype(np.uint8)
+    return np.where(np.isnan(x), np.uint8(0x7F), out).astype(np.uint8)
+
+
+def quantize_fp8(x_raw, scale: float) -> np.ndarray:
+    """Storage-form values -> E4M3 codes: float32(x) * float32(1/scale),
+    then f64_to_fp8_e4m3 (the product is exact in float64)."""
+    inv = np.float32(1.0) / np.float32(scale)
+    y = to_f64(x_raw).astype(np.float32) * inv
+    return f64_to_fp8_e4m3(y.astype(np.float64))
+
+
+def append_fp8(k_cache8, v_cache8, seq_lens, k_new, v_new, k_scale, v_scale) -> int:
+    """append() for an E4M3 cache: the new rows are quantised first."""
+    return append(k_cache8, v_cache8, seq_lens, quantize_fp8(k_new, k_scale),
+                  quantize_fp8(v_new, v_scale))
+
+
+def decode_fp8(q, k_cache8, v_cache8, seq_lens, scale: float, k_scale: float,
+               v_scale: float):
+    """decode() over an E4M3 cache: stored keys are code value * k_scale,
+    stored values code value * v_scale."""
+    B, n_h, d = q.shape
+    n_kv = k_cache8.shape[1]
+    G = n_h // n_kv
+    o = np.zeros((B, n_h, v_cache8.shape[3]))
+    lse = np.full((B, n_h), -math.inf)
+    for b in range(B):
+        n = int(seq_lens[b])
+        for j in range(n_kv):
+            K = fp8_e4m3_to_f64(k_cache8[b, j, :n]) * float(k_scale)
+            V = fp8_e4m3_to_f64(v_cache8[b, j, :n]) * float(v_scale)
+            for i in range(j * G, (j + 1) * G):
+                o[b, i], lse[b, i] = _attend(to_f64(q[b, i]), K, V, scale)
+    return o, lse

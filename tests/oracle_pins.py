@@ -395,6 +395,126 @@ def pin_bf16_decoding(orc):
     assert math.copysign(1.0, got[5]) == -1.0
 
 
+# ---------------------------------------------------------------- FP8 E4M3
+# Code values from the format's bit fields (sign, 4-bit exponent with bias 7,
+# 3-bit mantissa; exponent 0 subnormal; 0x7F/0xFF NaN), and the page's
+# figure for its largest value.
+_FP8_KNOWN = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6,
+              0x30: 0.5, 0x38: 1.0, 0x39: 1.125, 0x3A: 1.25, 0x3C: 1.5, 0x3F: 1.875,
+              0x40: 2.0, 0x44: 3.0, 0x4C: 6.0, 0x7D: 416.0, 0x7E: 448.0,
+              0x80: -0.0, 0xB8: -1.0, 0xC0: -2.0, 0xFE: -448.0}
+
+
+def pin_fp8_page_max(orc):
+    """The DeepSeek article's headroom bound: the block format tops out at
+    448 x 6 = 2688, 448 being the largest E4M3 value."""
+    g = golden()["fp8_e4m3_max"]
+    assert g["e4m3_max"] * g["e2m1_max"] == g["product"]
+    assert orc.FP8_E4M3_MAX == g["e4m3_max"]
+    assert float(orc.fp8_e4m3_to_f64(np.array([0x7E], np.uint8))[0]) == g["e4m3_max"]
+    # nothing finite above it
+    allv = orc.fp8_e4m3_to_f64(np.arange(256, dtype=np.uint8))
+    assert np.nanmax(np.abs(allv)) == g["e4m3_max"]
+
+
+def pin_fp8_codes(orc):
+    """Known code values; NaN codes; 127 finite non-negative values,
+    strictly increasing with the code."""
+    codes = np.array(sorted(_FP8_KNOWN), dtype=np.uint8)
+    got = orc.fp8_e4m3_to_f64(codes)
+    for c, v in zip(codes.tolist(), got.tolist()):
+        assert v == _FP8_KNOWN[c], (hex(c), v)
+    assert math.copysign(1.0, float(orc.fp8_e4m3_to_f64(np.array([0x80], np.uint8))[0])) == -1.0
+    assert np.isnan(orc.fp8_e4m3_to_f64(np.array([0x7F, 0xFF], np.uint8))).all()
+    pos = orc.fp8_e4m3_to_f64(np.arange(0x7F, dtype=np.uint8))
+    assert np.all(np.diff(pos) > 0)
+    # negative codes mirror positive ones
+    neg = orc.fp8_e4m3_to_f64(np.arange(0x80, 0xFF, dtype=np.uint8))
+    assert np.array_equal(-pos[1:], neg[1:])
+
+
+def pin_fp8_roundtrip(orc):
+    """Every finite code encodes back to itself."""
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    back = orc.f64_to_fp8_e4m3(orc.fp8_e4m3_to_f64(codes))
+    assert np.array_equal(back, codes)
+
+
+def _nearest_even_code(x, table):
+    """Scalar brute force over (code, value) pairs: nearest value, ties to
+    the even code, saturating at the largest magnitude."""
+    a = min(abs(x), 448.0)
+    best = None
+    for c, v in table:
+        dist = abs(a - v)
+        key = (dist, c % 2)
+        if best is None or key < best[0]:
+            best = (key, c)
+    c = best[1]
+    return c | (0x80 if math.copysign(1.0, x) < 0 else 0)
+
+
+def pin_fp8_rounding(orc):
+    """Round to nearest, ties to even, saturate: worked ties, the clamp,
+    and a scalar brute force over random float32 values."""
+    cases = {1.0625: 0x38, 1.1875: 0x3A, 2.0 ** -10: 0x00, 3 * 2.0 ** -10: 0x02,
+             1e6: 0x7E, -1e6: 0xFE, 464.0: 0x7E, 447.0: 0x7E, 432.0: 0x7E,
+             431.0: 0x7D, 0.0: 0x00}
+    xs = np.array(list(cases), dtype=np.float64)
+    got = orc.f64_to_fp8_e4m3(xs)
+    for x, c in zip(xs.tolist(), got.tolist()):
+        assert c == cases[x], (x, hex(c))
+    assert orc.f64_to_fp8_e4m3(np.array([-0.0])).tolist() == [0x80]
+    rng = np.random.default_rng(7)
+    ys = (rng.standard_normal(400) * np.exp2(rng.integers(-12, 10, 400))).astype(np.float32).astype(np.float64)
+    got = orc.f64_to_fp8_e4m3(ys)
+    full = [(c, float(2.0 ** -9 * (c & 7)) if (c >> 3) == 0 else (1 + (c & 7) / 8) * 2.0 ** ((c >> 3) - 7))
+            for c in range(0x7F)]
+    for y, c in zip(ys.tolist(), got.tolist()):
+        assert c == _nearest_even_code(y, full), (y, hex(c))
+
+
+def pin_fp8_quantize_scale(orc):
+    """A stored code times the scale gives the number back: 3.0 stored with
+    scale 2 is code 1.5 (0x3C), with scale 0.5 it is code 6.0 (0x4C)."""
+    x = syn.bf16_bits(np.array([3.0, -3.0], np.float32))
+    assert orc.quantize_fp8(x, 2.0).tolist() == [0x3C, 0xBC]
+    assert orc.quantize_fp8(x, 0.5).tolist() == [0x4C, 0xCC]
+    # float32 inputs too
+    assert orc.quantize_fp8(np.array([448.0 * 4], np.float32), 4.0).tolist() == [0x7E]
+
+
+def pin_fp8_decode(orc):
+    """decode_fp8 equals scalar brute-force attention over values taken
+    from known codes (times the scales); append_fp8 stores quantised rows
+    at the length slot."""
+    rng = np.random.default_rng(11)
+    known = np.array([c for c in _FP8_KNOWN if c not in (0x80,)], dtype=np.uint8)
+    B, n_h, n_kv, d, L = 1, 4, 2, 8, 6
+    kc = rng.choice(known, size=(B, n_kv, L, d)).astype(np.uint8)
+    vc = rng.choice(known, size=(B, n_kv, L, d)).astype(np.uint8)
+    q = rng.standard_normal((B, n_h, d)).astype(np.float32)
+    lens = np.array([5], np.int32)
+    ks, vs = 0.25, 1.5
+    o, l = orc.decode_fp8(q, kc, vc, lens, 0.3, ks, vs)
+    for i in range(n_h):
+        j = i // (n_h // n_kv)
+        Kf = [[_FP8_KNOWN[int(c)] * ks for c in row] for row in kc[0, j, :5]]
+        Vf = [[_FP8_KNOWN[int(c)] * vs for c in row] for row in vc[0, j, :5]]
+        bo, bl = brute_attend(q[0, i], Kf, Vf, 0.3)
+        assert np.allclose(o[0, i], bo, rtol=1e-12, atol=1e-12)
+        assert abs(l[0, i] - bl) < 1e-12
+    k8 = np.zeros((1, 1, 4, 2), np.uint8)
+    v8 = np.zeros((1, 1, 4, 2), np.uint8)
+    sl = np.array([2], np.int32)
+    kn = syn.bf16_bits(np.array([[[1.0, -2.0]]], np.float32))
+    vn = syn.bf16_bits(np.array([[[3.0, 0.5]]], np.float32))
+    f = orc.append_fp8(k8, v8, sl, kn, vn, 1.0, 0.5)
+    assert f == 0 and int(sl[0]) == 3
+    assert k8[0, 0, 2].tolist() == [0x38, 0xC0] and v8[0, 0, 2].tolist() == [0x4C, 0x38]
+    assert not k8[0, 0, [0, 1, 3]].any()
+
+
 ALL_PINS = [
     pin_size_llama2, pin_size_matches_storage, pin_causal_equals_recompute,
     pin_full_causal_bruteforce, pin_decode_bruteforce, pin_single_position,
@@ -402,4 +522,6 @@ ALL_PINS = [
     pin_saturation, pin_scale_is_multiplicative, pin_permutation,
     pin_split_merge, pin_gqa_head_mapping, pin_mla_reduces_to_dense,
     pin_mla_rope_matters, pin_topk, pin_append, pin_bf16_decoding,
+    pin_fp8_page_max, pin_fp8_codes, pin_fp8_roundtrip, pin_fp8_rounding,
+    pin_fp8_quantize_scale, pin_fp8_decode,
 ]

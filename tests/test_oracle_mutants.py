@@ -175,6 +175,61 @@ def mutants():
         return sum(np.asarray(o) for o in os_) / len(os_), max(lses)
     m.merge_partials = merge_unweighted
     out["merge_ignores_lse"] = m
+
+    # FP8 E4M3 slips
+    def fp8_decode_variant(bias=7, sub=2.0 ** -9):
+        def dec(codes):
+            c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+            sign = np.where((c >> 7) & 1, -1.0, 1.0)
+            e, mm = (c >> 3) & 15, c & 7
+            mag = np.where(e == 0, mm * sub, (1.0 + mm / 8.0) * np.exp2(e - float(bias)))
+            return np.where((e == 15) & (mm == 7), np.nan, sign * mag)
+        return dec
+    m = _copy()
+    m.fp8_e4m3_to_f64 = fp8_decode_variant(bias=8)
+    out["fp8_exponent_bias_8"] = m
+    m = _copy()
+    m.fp8_e4m3_to_f64 = fp8_decode_variant(sub=2.0 ** -10)
+    out["fp8_subnormal_scale"] = m
+
+    def fp8_encode_variant(ties_up=False, saturate=True):
+        def enc(x):
+            x = np.asarray(x, dtype=np.float64)
+            vals = K.fp8_e4m3_to_f64(np.arange(0x7F, dtype=np.uint8))
+            a = np.abs(x)
+            over = a > 448.0
+            a = np.minimum(a, 448.0)
+            hi = np.clip(np.searchsorted(vals, a), 0, 0x7E)
+            lo = np.maximum(hi - 1, 0)
+            d_lo, d_hi = a - vals[lo], vals[hi] - a
+            pick = (d_hi < d_lo) | ((d_hi == d_lo) & (True if ties_up else (hi % 2 == 0)))
+            code = np.where(a == vals[hi], hi, np.where(pick, hi, lo)).astype(np.uint8)
+            code = code | np.where(np.signbit(x), 0x80, 0).astype(np.uint8)
+            if not saturate:
+                code = np.where(over, np.uint8(0x7F), code)
+            return code.astype(np.uint8)
+        return enc
+    m = _copy()
+    m.f64_to_fp8_e4m3 = fp8_encode_variant(ties_up=True)
+    out["fp8_ties_away_from_zero"] = m
+    m = _copy()
+    m.f64_to_fp8_e4m3 = fp8_encode_variant(saturate=False)
+    out["fp8_overflow_to_nan"] = m
+
+    m = _copy()
+
+    def quantize_multiplies(x, scale):
+        y = K.to_f64(x).astype(np.float32) * np.float32(scale)
+        return K.f64_to_fp8_e4m3(y.astype(np.float64))
+    m.quantize_fp8 = quantize_multiplies
+    out["fp8_quantize_multiplies_scale"] = m
+
+    m = _copy()
+
+    def decode_fp8_no_vscale(q, kc, vc, sl, scale, ks, vs):
+        return K.decode_fp8(q, kc, vc, sl, scale, ks, 1.0)
+    m.decode_fp8 = decode_fp8_no_vscale
+    out["fp8_decode_ignores_value_scale"] = m
     return out
 
 
