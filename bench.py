@@ -16,7 +16,7 @@ GB/s over the algorithmic bytes of a step (cache read + q read + out write +
 new k/v read and written + lengths).  `roofline` is the dense decode kernel
 alone, timed with HIP events over back-to-back launches of one step's
 layers.  `also` carries the same figures for the GQA, MLA and top-k
-workloads.  `cpu_baseline` is the fp64 oracle on the same inputs (copied to
+workloads, and for the GQA workload over FP8 E4M3 caches (C3F8).  `cpu_baseline` is the fp64 oracle on the same inputs (copied to
 the host), on a time-bounded sample of layer-steps.
 """
 from __future__ import annotations
@@ -45,8 +45,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="C2", choices=["C2", "C3", "C4", "C5"])
-    ap.add_argument("--others", default="C3,C4,C5",
+    ap.add_argument("--config", default="C2", choices=["C2", "C3", "C4", "C5", "C3F8"])
+    ap.add_argument("--others", default="C3,C4,C5,C3F8",
                     help="also-measured workloads (comma list; 'none' for none)")
     ap.add_argument("--kernel-reps", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true")
@@ -279,8 +279,97 @@ class TopKWorkload:
                 f"indices of L={c.pre_len}, {self.layers} index sets over {self.nbuf} cache buffers")
 
 
+class Fp8DenseWorkload:
+    """The GQA layers of C3 over FP8 E4M3 caches (uint8 [B, n_kv, L_max, d],
+    one float32 scale per tensor).  A layer-step is kvc_append_fp8 then
+    kvc_decode_attn_fp8."""
+
+    kernel = "dense_mfma_kernel<false, false, true> (fp8 E4M3 cache)"
+    kernel_appends = False
+    K_SCALE = 1.0 / 64      # N(0,1) / (1/64) stays within +-448
+    V_SCALE = 1.0 / 64
+
+    def __init__(self, cfg, slack, torch, kvc):
+        self.cfg, self.torch, self.kvc = cfg, torch, kvc
+        B, n_h, n_kv, d = cfg.B, cfg.n_h, cfg.n_kv, cfg.d
+        self.pre = syn.pre_append_lens(cfg).astype(np.int64)
+        self.L_max = int(max(cfg.L_max, self.pre.max() + 1) + slack)
+        self.layers = cfg.layers
+        self.nbuf = cfg.distinct_buffers
+        dt = torch.bfloat16
+        codes = lambda i, t, sc: self._fp8_fill(
+            torch.empty(B, n_kv, self.L_max, d, dtype=torch.uint8, device="cuda"),
+            syn.device_seed(cfg.cfg_id, i, t), sc)
+        self.K = [codes(i, "k", self.K_SCALE) for i in range(self.nbuf)]
+        self.V = [codes(i, "v", self.V_SCALE) for i in range(self.nbuf)]
+        mk = lambda shape, l, t: syn.device_normal_(torch.empty(*shape, dtype=dt, device="cuda"),
+                                                    syn.device_seed(cfg.cfg_id, l, t))
+        self.q = [mk((B, n_h, d), l, "q") for l in range(self.layers)]
+        self.kn = [mk((B, n_kv, d), l, "k_new") for l in range(self.layers)]
+        self.vn = [mk((B, n_kv, d), l, "v_new") for l in range(self.layers)]
+        self.out = [torch.empty(B, n_h, d, dtype=dt, device="cuda") for _ in range(self.layers)]
+        pre_t = torch.tensor(self.pre, dtype=torch.int32)
+        self.sl = [pre_t.clone().cuda() for _ in range(self.layers)]
+        self.ws = kvc.workspace(kvc.kvc_decode_attn_fp8_workspace_size(B, n_h, n_kv, self.L_max, d))
+
+    def _fp8_fill(self, t, seed, scale, chunk=1 << 26):
+        """Synthetic cache contents: seeded N(0,1) / scale as E4M3 codes
+        (torch's float8_e4m3fn cast lays the data out; input set-up only)."""
+        torch = self.torch
+        flat = t.view(-1)
+        g = torch.Generator(device=t.device)
+        g.manual_seed(seed)
+        for s in range(0, flat.numel(), chunk):
+            e = min(flat.numel(), s + chunk)
+            x = torch.randn(e - s, generator=g, device=t.device, dtype=torch.float32) / scale
+            flat[s:e].copy_(x.to(torch.float8_e4m3fn).view(torch.uint8))
+            del x
+        return t
+
+    def step(self):
+        for l in range(self.layers):
+            b = l % self.nbuf
+            self.kvc.kvc_append_fp8(self.K[b], self.V[b], self.sl[l], self.kn[l], self.vn[l],
+                                    self.K_SCALE, self.V_SCALE)
+            self.kvc.kvc_decode_attn_fp8(self.q[l], self.K[b], self.V[b], self.sl[l], self.out[l],
+                                         self.K_SCALE, self.V_SCALE, None,
+                                         scale=self.cfg.scale, workspace=self.ws)
+
+    def decode_only(self):
+        for l in range(self.layers):
+            b = l % self.nbuf
+            self.kvc.kvc_decode_attn_fp8(self.q[l], self.K[b], self.V[b], self.sl[l], self.out[l],
+                                         self.K_SCALE, self.V_SCALE, None,
+                                         scale=self.cfg.scale, workspace=self.ws)
+
+    def kernel_only(self):
+        self.decode_only()
+
+    def lens_after(self, steps_done):
+        return np.minimum(self.pre + 1 + steps_done, self.L_max)
+
+    def kernel_bytes(self, n):
+        c = self.cfg
+        return int(2 * c.n_kv * c.d * 1 * n.sum() + c.B * c.n_h * c.d * (2 + 2) + 4 * c.B)
+
+    def launch_bytes(self, steps_done):
+        return self.kernel_bytes(self.lens_after(steps_done - 1))
+
+    def step_bytes(self, steps_done):
+        c = self.cfg
+        append = 2 * c.B * c.n_kv * c.d * (2 + 1) + 8 * c.B
+        return (self.kernel_bytes(self.lens_after(steps_done)) + append) * self.layers
+
+    def describe(self):
+        c = self.cfg
+        return (f"{c.name} over FP8 E4M3 caches: B={c.B} n_h={c.n_h} n_kv={c.n_kv} d={c.d}, "
+                f"seq_lens ~ U[{c.len_range[0]}, {c.len_range[1]}] (post-append), "
+                f"{self.layers} layers ({self.nbuf} distinct cache buffers), bf16 q/out")
+
+
 WORKLOADS = {"C2": (syn.C2, DenseWorkload), "C3": (syn.C3, DenseWorkload),
-             "C4": (syn.C4, MlaWorkload), "C5": (syn.C5, TopKWorkload)}
+             "C4": (syn.C4, MlaWorkload), "C5": (syn.C5, TopKWorkload),
+             "C3F8": (syn.C3, Fp8DenseWorkload)}
 
 
 # ---------------------------------------------------------------- timing

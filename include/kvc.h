@@ -149,6 +149,44 @@ int kvc_append_decode_attn(const void* q, void* k_cache, void* v_cache,
                            void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * FP8 E4M3 cache (guide, "Fewer bits per number": the byte width b is a plain
+ * multiplier of the cache size, and fp8 is the usual serving default; podcast
+ * transcript, KV quantization passage).  Each cached number is one byte, an
+ * OCP E4M3 code (finite-only variant: 4 exponent bits with bias 7, 3 mantissa
+ * bits, largest finite value 448, codes 0x7F and 0xFF are NaN), and one
+ * float32 scale per tensor: stored value = decode(code) * scale.
+ *
+ * kvc_append_fp8 - as kvc_append with dtype bf16 new rows and E4M3 caches.
+ * Each new number x becomes the code nearest to float32(x) * inv in float32
+ * arithmetic, where inv = (float)(1.0 / (double)scale), ties to the even
+ * code, magnitudes beyond 448 saturating to +-448 and NaN giving 0x7F.
+ *   k_cache, v_cache  [B, n_kv, L_max, d] uint8 (both required)
+ *   k_new, v_new      [B, n_kv, d] bf16;  d a multiple of 16.
+ *   k_scale, v_scale  finite and > 0, else KVC_ERR_BAD_ARG.
+ */
+int kvc_append_fp8(void* k_cache, void* v_cache, int32_t* seq_lens,
+                   const void* k_new, const void* v_new,
+                   int B, int n_kv, int L_max, int d,
+                   float k_scale, float v_scale, int32_t* flag, void* stream);
+
+/*
+ * kvc_decode_attn_fp8 - kvc_decode_attn over E4M3 caches written by
+ * kvc_append_fp8: keys are decode(code) * k_scale and values
+ * decode(code) * v_scale (the scales are folded into the score scale and the
+ * output; the codes are widened to bf16, which holds every E4M3 value
+ * exactly).  q and out are bf16, lse float32 or NULL.
+ *   q [B, n_h, d]   k_cache, v_cache [B, n_kv, L_max, d] uint8   d = 128;
+ *   n_h / n_kv <= 16.  Workspace rules as for kvc_decode_attn.
+ */
+size_t kvc_decode_attn_fp8_workspace_size(int B, int n_h, int n_kv, int L_max,
+                                          int d);
+int kvc_decode_attn_fp8(const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* seq_lens, void* out, float* lse,
+                        int B, int n_h, int n_kv, int L_max, int d, float scale,
+                        float k_scale, float v_scale, void* workspace,
+                        size_t ws_bytes, void* stream);
+
+/*
  * kvc_decode_attn_mla - decode attention over a latent (MLA) cache.
  * (Guide, "Caching a compressed latent" and the memory footnote.)
  *

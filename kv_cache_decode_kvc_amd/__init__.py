@@ -68,6 +68,10 @@ def lib() -> ctypes.CDLL:
         "kvc_decode_attn_topk_workspace_size": (_Z, [_I, _I, _I, _I, _I, _I]),
         "kvc_decode_attn_topk": (_I, [_P, _P, _P, _P, _P, _I, _P, _P, _I, _I,
                                       _I, _I, _I, _F, _I, _P, _P, _Z, _P]),
+        "kvc_append_fp8": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _F, _P, _P]),
+        "kvc_decode_attn_fp8_workspace_size": (_Z, [_I, _I, _I, _I, _I]),
+        "kvc_decode_attn_fp8": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
+                                     _F, _F, _F, _P, _Z, _P]),
         "kvc_status_string": (ctypes.c_char_p, [_I]),
         "kvc_set_split_override": (_I, [_I]),
         "kvc_split_positions": (_I, [_I, _I, _I, _I]),
@@ -237,6 +241,51 @@ def kvc_decode_attn_topk(q, k_cache, v_cache, seq_lens, idx, out, lse=None,
                                     _dtype_code(q), _ptr(flag), wp, wn,
                                     _stream(stream))
     _check(st, "kvc_decode_attn_topk")
+
+
+def _need_u8(t, what):
+    import torch
+    if t.dtype != torch.uint8:
+        raise TypeError(f"{what} must be uint8 (E4M3 codes), got {t.dtype}")
+
+
+def kvc_append_fp8(k_cache, v_cache, seq_lens, k_new, v_new, k_scale, v_scale,
+                   flag=None, stream=None):
+    """Quantise bf16 k_new/v_new [B, n_kv, d] to E4M3 codes (x / scale) at slot
+    seq_lens[b] of the uint8 caches [B, n_kv, L_max, d]; bump seq_lens."""
+    import torch
+    _need_u8(k_cache, "k_cache")
+    _need_u8(v_cache, "v_cache")
+    if k_new.dtype != torch.bfloat16 or v_new.dtype != torch.bfloat16:
+        raise TypeError("k_new/v_new must be bfloat16")
+    B, n_kv, L_max, d = k_cache.shape
+    st = lib().kvc_append_fp8(_ptr(k_cache), _ptr(v_cache), _ptr(seq_lens),
+                              _ptr(k_new), _ptr(v_new), B, n_kv, L_max, d,
+                              k_scale, v_scale, _ptr(flag), _stream(stream))
+    _check(st, "kvc_append_fp8")
+
+
+def kvc_decode_attn_fp8_workspace_size(B, n_h, n_kv, L_max, d) -> int:
+    return lib().kvc_decode_attn_fp8_workspace_size(B, n_h, n_kv, L_max, d)
+
+
+def kvc_decode_attn_fp8(q, k_cache, v_cache, seq_lens, out, k_scale, v_scale,
+                        lse=None, scale=None, workspace=None, stream=None):
+    """Dense decode over E4M3 caches (uint8 [B, n_kv, L_max, d]); q/out bf16."""
+    import torch
+    _need_u8(k_cache, "k_cache")
+    _need_u8(v_cache, "v_cache")
+    if q.dtype != torch.bfloat16 or out.dtype != torch.bfloat16:
+        raise TypeError("q/out must be bfloat16")
+    B, n_h, d = q.shape
+    _, n_kv, L_max, _ = k_cache.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    wp, wn = _ws(workspace)
+    st = lib().kvc_decode_attn_fp8(_ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                   _ptr(seq_lens), _ptr(out), _ptr(lse), B, n_h,
+                                   n_kv, L_max, d, scale, k_scale, v_scale, wp, wn,
+                                   _stream(stream))
+    _check(st, "kvc_decode_attn_fp8")
 
 
 def kvc_stream_read_sink_floats(nbytes: int) -> int:

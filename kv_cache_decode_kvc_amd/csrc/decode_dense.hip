@@ -66,7 +66,10 @@ __device__ inline void write_final(const DenseParams& p, size_t bh,
                                    const float* o, float lse2) {
   constexpr int CPT = D / 16;
   const int c0 = (threadIdx.x & 15) * CPT;
-  store_row<OutT, CPT>(reinterpret_cast<OutT*>(p.out) + bh * D + c0, o);
+  float os[CPT];
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) os[c] = o[c] * p.out_scale;
+  store_row<OutT, CPT>(reinterpret_cast<OutT*>(p.out) + bh * D + c0, os);
   if (p.lse && (threadIdx.x & 15) == 0) p.lse[bh] = lse2 * kLn2;
 }
 
@@ -414,8 +417,52 @@ __device__ inline void compute_chunk(const Chunk& c, int cs, int end,
   }
 }
 
-template <bool TOPK, bool APPEND>
+// FP8 E4M3 cache (d = 128, 128-byte rows): the same chunk, loaded as raw
+// codes and expanded to bf16 (exactly) just before its MFMAs.  The dot
+// product's column order is free as long as q uses the same one, so K k-step
+// kk, lane group g covers columns (kk/2)*64 + g*16 + (kk%2)*8 .. +7: one
+// 16-byte load per (row, kk/2).  V keeps the bf16 layout (8 bytes per row).
+struct ChunkF8 {
+  u32x4 k[2][2];
+  u32x2 v[8];
+};
+
+__device__ inline int fp8_q_col(int kk, int g) { return (kk >> 1) * 64 + g * 16 + (kk & 1) * 8; }
+
+__device__ inline void load_chunk(ChunkF8& c, int cs, __amdgpu_buffer_rsrc_t kr,
+                                  __amdgpu_buffer_rsrc_t vr, int r, int g) {
+  constexpr uint32_t kRow = 128;
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    const uint32_t row = cs + (r >> 2) * 8 + a * 4 + (r & 3);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) c.k[a][h] = buf_load16_stream(kr, row * kRow + h * 64 + g * 16);
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    c.v[e] = buf_load8_stream(vr, (uint32_t)(cs + g * 8 + e) * kRow + r * 8);
+}
+
+__device__ inline void expand_chunk(const ChunkF8& f, Chunk& c) {
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const u32x4 w = f.k[a][kk >> 1];
+      const u32x2 h = (kk & 1) ? u32x2{w[2], w[3]} : u32x2{w[0], w[1]};
+      c.k[a][kk] = fp8x8_to_bf16x8(h);
+    }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) c.v[e] = fp8x8_to_bf16x8(f.v[e]);
+  c.vmask = 0xFF;
+}
+
+template <bool FP8> struct ChunkOf { using T = Chunk; };
+template <> struct ChunkOf<true> { using T = ChunkF8; };
+
+template <bool TOPK, bool APPEND, bool FP8 = false>
 __global__ __launch_bounds__(256, 2) void dense_mfma_kernel(DenseParams p) {
+  static_assert(!FP8 || (!TOPK && !APPEND), "FP8 caches: plain decode only");
   __shared__ MergeLds<128> L;
   int b, j, split;
   decode_unit(p, b, j, split);
@@ -435,11 +482,12 @@ __global__ __launch_bounds__(256, 2) void dense_mfma_kernel(DenseParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, g = lane >> 4;
   const size_t unit = (size_t)b * p.n_kv + j;
-  const size_t unit_bytes = (size_t)p.L_max * 256;
+  constexpr uint32_t kRowBytes = FP8 ? 128u : 256u;
+  const size_t unit_bytes = (size_t)p.L_max * kRowBytes;
   const __amdgpu_buffer_rsrc_t kr =
-      make_rsrc((const char*)p.k + unit * unit_bytes, (uint32_t)n * 256u);
+      make_rsrc((const char*)p.k + unit * unit_bytes, (uint32_t)n * kRowBytes);
   const __amdgpu_buffer_rsrc_t vr =
-      make_rsrc((const char*)p.v + unit * unit_bytes, (uint32_t)n * 256u);
+      make_rsrc((const char*)p.v + unit * unit_bytes, (uint32_t)n * kRowBytes);
   const __amdgpu_buffer_rsrc_t ir =
       TOPK ? make_rsrc(p.idx + unit * p.K, (uint32_t)p.K * 4u) : kr;
 
@@ -449,7 +497,7 @@ __global__ __launch_bounds__(256, 2) void dense_mfma_kernel(DenseParams p) {
         (const uint16_t*)p.q + ((size_t)b * p.n_h + j * p.G + r) * 128;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
-      qop[kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow + kk * 32 + g * 8));
+      qop[kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow + (FP8 ? fp8_q_col(kk, g) : kk * 32 + g * 8)));
   } else {
     const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
@@ -469,27 +517,38 @@ __global__ __launch_bounds__(256, 2) void dense_mfma_kernel(DenseParams p) {
   const int new_slot = (APPEND && ls.ok) ? ls.n_raw : -1;
   const u32x4* kn = reinterpret_cast<const u32x4*>(p.k_new) + unit * 16;
   const u32x4* vn = reinterpret_cast<const u32x4*>(p.v_new) + unit * 16;
+  using Raw = typename ChunkOf<FP8>::T;
+  auto load = [&](Raw& c, int at) {
+    if constexpr (FP8) {
+      load_chunk(c, at, kr, vr, r, g);
+    } else {
+      load_chunk<TOPK>(c, at, end, n, kr, vr, ir, r, g, bad);
+      if constexpr (APPEND) patch_new_row(c, at, new_slot, kn, vn, r, g);
+    }
+  };
+  auto compute = [&](const Raw& c, int at) {
+    if constexpr (FP8) {
+      Chunk x;
+      expand_chunk(c, x);
+      compute_chunk<false>(x, at, end, qop, p.scale_log2, g, st);
+    } else {
+      compute_chunk<TOPK>(c, at, end, qop, p.scale_log2, g, st);
+    }
+  };
   if (cs < end) {
-    Chunk A, Bc;
-    load_chunk<TOPK>(A, cs, end, n, kr, vr, ir, r, g, bad);
-    if constexpr (APPEND) patch_new_row(A, cs, new_slot, kn, vn, r, g);
+    Raw A, Bc;
+    load(A, cs);
     while (true) {
       int cn = cs + kStride;
       bool more = cn < end;
-      if (more) {
-        load_chunk<TOPK>(Bc, cn, end, n, kr, vr, ir, r, g, bad);
-        if constexpr (APPEND) patch_new_row(Bc, cn, new_slot, kn, vn, r, g);
-      }
-      compute_chunk<TOPK>(A, cs, end, qop, p.scale_log2, g, st);
+      if (more) load(Bc, cn);
+      compute(A, cs);
       if (!more) break;
       cs = cn;
       cn = cs + kStride;
       more = cn < end;
-      if (more) {
-        load_chunk<TOPK>(A, cn, end, n, kr, vr, ir, r, g, bad);
-        if constexpr (APPEND) patch_new_row(A, cn, new_slot, kn, vn, r, g);
-      }
-      compute_chunk<TOPK>(Bc, cs, end, qop, p.scale_log2, g, st);
+      if (more) load(A, cn);
+      compute(Bc, cs);
       if (!more) break;
       cs = cn;
     }
@@ -679,6 +738,11 @@ hipError_t launch_dense_mfma(const DenseParams& p, bool topk, bool append, hipSt
     hipLaunchKernelGGL((dense_mfma_kernel<false, true>), dense_grid(p), dim3(256), 0, s, p);
   else
     hipLaunchKernelGGL((dense_mfma_kernel<false, false>), dense_grid(p), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_dense_fp8(const DenseParams& p, hipStream_t s) {
+  hipLaunchKernelGGL((dense_mfma_kernel<false, false, true>), dense_grid(p), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

@@ -227,8 +227,27 @@ int kvc_append(void* k_cache, void* v_cache, int32_t* seq_lens,
     return KVC_ERR_MISALIGNED;
   if (B == 0) return KVC_OK;
   AppendParams p{k_cache, v_cache, seq_lens, k_new, v_new, flag,
-                 B, n_kv, L_max, d, elem_bytes(dtype)};
+                 B, n_kv, L_max, d, elem_bytes(dtype), 1.f, 1.f};
   return launch_status(launch_append(p, static_cast<hipStream_t>(stream)));
+}
+
+int kvc_append_fp8(void* k_cache, void* v_cache, int32_t* seq_lens,
+                   const void* k_new, const void* v_new, int B, int n_kv,
+                   int L_max, int d, float k_scale, float v_scale,
+                   int32_t* flag, void* stream) {
+  if (B < 0 || n_kv < 1 || L_max < 1 || d < 1) return KVC_ERR_BAD_SHAPE;
+  if (d % 16 != 0 || (int64_t)n_kv * d >= kMaxOffset) return KVC_ERR_BAD_SHAPE;
+  if (!(isfinite(k_scale) && isfinite(v_scale) && k_scale > 0.f && v_scale > 0.f))
+    return KVC_ERR_BAD_ARG;
+  if (!k_cache || !v_cache || !seq_lens || !k_new || !v_new) return KVC_ERR_NULL_PTR;
+  if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(k_new, 16) ||
+      !aligned(v_new, 16) || !aligned(seq_lens, 4) || (flag && !aligned(flag, 4)))
+    return KVC_ERR_MISALIGNED;
+  if (B == 0) return KVC_OK;
+  AppendParams p{k_cache, v_cache, seq_lens, k_new, v_new, flag,
+                 B, n_kv, L_max, d, 1,
+                 (float)(1.0 / (double)k_scale), (float)(1.0 / (double)v_scale)};
+  return launch_status(launch_append_fp8(p, static_cast<hipStream_t>(stream)));
 }
 
 size_t kvc_decode_attn_workspace_size(int B, int n_h, int n_kv, int L_max,
@@ -250,10 +269,15 @@ static int dense_common(const void* q, const void* k_cache, const void* v_cache,
                         int L_max, int d, float scale, int dtype, int32_t* flag,
                         void* workspace, size_t ws_bytes, void* stream,
                         bool topk, const void* k_new = nullptr,
-                        const void* v_new = nullptr, bool fused = false) {
+                        const void* v_new = nullptr, bool fused = false,
+                        bool fp8 = false, float k_scale = 1.f, float v_scale = 1.f) {
+  // FP8 caches: q and out are bf16; the shape rules are those of bf16 with
+  // d = 128 (checked by the caller).
   const DenseCheck c = check_dense_shape(B, n_h, n_kv, L_max, d, dtype, K, topk, fused);
   if (c.status != KVC_OK) return c.status;
   if (!isfinite(scale)) return KVC_ERR_BAD_ARG;
+  if (fp8 && !(isfinite(k_scale) && isfinite(v_scale) && k_scale > 0.f && v_scale > 0.f))
+    return KVC_ERR_BAD_ARG;
   if (!q || !k_cache || !v_cache || !seq_lens || !out || (topk && !idx) ||
       (fused && (!k_new || !v_new)))
     return KVC_ERR_NULL_PTR;
@@ -279,7 +303,13 @@ static int dense_common(const void* q, const void* k_cache, const void* v_cache,
   fill_ws(p, c.ws, workspace, (size_t)c.P_max, fused);
   p.d = d; p.K = topk ? K : 0; p.S = c.S; p.P_max = (int)c.P_max; p.even = c.even;
   p.scale_log2 = scale * 1.4426950408889634f;
+  p.out_scale = 1.f;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (fp8) {
+    p.scale_log2 *= k_scale;
+    p.out_scale = v_scale;
+    return launch_status(launch_dense_fp8(p, s));
+  }
   if (dtype == KVC_BF16 && d == 128) return launch_status(launch_dense_mfma(p, topk, fused, s));
   return launch_status(launch_dense_generic(p, dtype, topk, fused, s));
 }
@@ -319,6 +349,26 @@ int kvc_decode_attn_topk(const void* q, const void* k_cache,
   return dense_common(q, k_cache, v_cache, seq_lens, idx, K, out, lse, B, n_h,
                       n_kv, L_max, d, scale, dtype, flag, workspace, ws_bytes,
                       stream, true);
+}
+
+size_t kvc_decode_attn_fp8_workspace_size(int B, int n_h, int n_kv, int L_max,
+                                          int d) {
+  if (d != 128) return 0;
+  const DenseCheck c = check_dense_shape(B, n_h, n_kv, L_max, d, KVC_BF16, 0, false);
+  return c.status == KVC_OK ? c.ws.total : 0;
+}
+
+int kvc_decode_attn_fp8(const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* seq_lens, void* out, float* lse, int B,
+                        int n_h, int n_kv, int L_max, int d, float scale,
+                        float k_scale, float v_scale, void* workspace,
+                        size_t ws_bytes, void* stream) {
+  if (B < 0 || n_h < 1 || n_kv < 1 || L_max < 1 || d < 1) return KVC_ERR_BAD_SHAPE;
+  if (d != 128) return KVC_ERR_UNSUPPORTED;
+  return dense_common(q, k_cache, v_cache, seq_lens, nullptr, 0, out, lse, B,
+                      n_h, n_kv, L_max, d, scale, KVC_BF16, nullptr, workspace,
+                      ws_bytes, stream, false, nullptr, nullptr, false, true,
+                      k_scale, v_scale);
 }
 
 size_t kvc_decode_attn_mla_workspace_size(int B, int n_h, int L_max, int d_c,

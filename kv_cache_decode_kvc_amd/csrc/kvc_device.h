@@ -11,6 +11,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // Buffer resource word 3 for gfx9-family raw buffers: 32-bit data format,
 // no swizzle.  Accesses at offsets >= num_records return zero, which is how
@@ -37,6 +38,11 @@ constexpr int kStream = 2;
 __device__ inline u32x4 buf_load16_stream(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4,
                             __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kStream));
+}
+
+__device__ inline u32x2 buf_load8_stream(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x2,
+                            __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kStream));
 }
 
 __device__ inline bf16x8 as_bf16x8(u32x4 x) {
@@ -101,6 +107,18 @@ __device__ inline void wait_vm_all() {
 }
 
 constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kFp8Max = 448.0f;   // largest finite E4M3 value
+
+// Eight E4M3 codes (bytes 0..7 of x) -> eight bf16 in the same order.  Every
+// E4M3 value is exact in bf16; the conversion's scale is 1.
+__device__ inline u32x4 fp8x8_to_bf16x8(u32x2 x) {
+  u32x4 r;
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[0], 1.0f, false));
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[0], 1.0f, true));
+  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[1], 1.0f, false));
+  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[1], 1.0f, true));
+  return r;
+}
 constexpr float kLn2 = 0.693147180559945309f;
 
 // exp2 of (x - m) where m may be -inf (then every x is -inf too): 0.

@@ -38,6 +38,7 @@ struct AppendParams {
   const void* v_new;      // may be null
   int32_t* flag;          // may be null
   int B, n_kv, L_max, d, elem_bytes;
+  float k_inv, v_inv;     // FP8 append: 1 / scale of the keys and values
 };
 
 // Dense and top-k decode.  Workspace pointers are null when P_max == 1.
@@ -63,7 +64,8 @@ struct DenseParams {
   int S;                  // positions per split (even mode: the least)
   int P_max;              // splits per (b, kv head) in the grid
   int even;               // 1: spread each sequence over the P_max splits
-  float scale_log2;       // scale * log2(e)
+  float scale_log2;       // scale * log2(e) (times the key scale for FP8 caches)
+  float out_scale;        // multiplies the output (the value scale for FP8 caches)
 };
 
 struct MlaParams {
@@ -126,6 +128,8 @@ inline WsLayout ws_layout(size_t units, size_t B, size_t n_h, size_t P_max,
 
 // Kernel launchers (defined in the .hip sources).
 hipError_t launch_append(const AppendParams& p, hipStream_t s);
+hipError_t launch_append_fp8(const AppendParams& p, hipStream_t s);
+hipError_t launch_dense_fp8(const DenseParams& p, hipStream_t s);
 hipError_t launch_dense_mfma(const DenseParams& p, bool topk, bool append, hipStream_t s);
 hipError_t launch_dense_generic(const DenseParams& p, int dtype, bool topk,
                                 bool append, hipStream_t s);

@@ -183,3 +183,42 @@ def test_fused_validation(L):
     assert fz(n_h=6, n_kv=4) == -2
     assert fz(B=0) == 0
     assert L.kvc_append_decode_attn_workspace_size(1, 8, 2, 64, 128, kvc.KVC_BF16) > 0
+
+
+def test_fp8_validation(L):
+    def ap(**kw):
+        a = dict(k=A16, v=A16, sl=A4, kn=A16, vn=A16, B=2, n_kv=2, L_max=8, d=128,
+                 ks=0.1, vs=0.1, flag=NULL, stream=NULL)
+        a.update(kw)
+        return L.kvc_append_fp8(a["k"], a["v"], a["sl"], a["kn"], a["vn"], a["B"], a["n_kv"],
+                                a["L_max"], a["d"], a["ks"], a["vs"], a["flag"], a["stream"])
+    assert ap(v=NULL) == -1           # both caches are required
+    assert ap(vn=NULL) == -1
+    assert ap(d=120) == -2            # rows are whole 16-byte pieces
+    assert ap(ks=0.0) == -8
+    assert ap(vs=float("inf")) == -8
+    assert ap(ks=-1.0) == -8
+    assert ap(k=A8) == -6
+    assert ap(B=0) == 0
+
+    def dc(**kw):
+        a = dict(q=A16, k=A16, v=A16, sl=A4, out=A16, lse=NULL, B=2, n_h=8, n_kv=2,
+                 L_max=64, d=128, scale=0.1, ks=0.1, vs=0.1, ws=A16, wsb=1 << 30,
+                 stream=NULL)
+        a.update(kw)
+        return L.kvc_decode_attn_fp8(a["q"], a["k"], a["v"], a["sl"], a["out"], a["lse"],
+                                     a["B"], a["n_h"], a["n_kv"], a["L_max"], a["d"],
+                                     a["scale"], a["ks"], a["vs"], a["ws"], a["wsb"],
+                                     a["stream"])
+    assert dc(k=NULL) == -1
+    assert dc(d=64) == -4
+    assert dc(n_h=7) == -2
+    assert dc(n_h=64, n_kv=2) == -4   # group of 32 heads
+    assert dc(scale=float("nan")) == -8
+    assert dc(ks=0.0) == -8
+    assert dc(vs=float("nan")) == -8
+    assert dc(out=A8) == -6
+    assert dc(B=0) == 0
+    assert L.kvc_decode_attn_fp8_workspace_size(32, 64, 8, 32768, 128) == \
+        L.kvc_decode_attn_workspace_size(32, 64, 8, 32768, 128, kvc.KVC_BF16)
+    assert L.kvc_decode_attn_fp8_workspace_size(32, 64, 8, 32768, 64) == 0
