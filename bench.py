@@ -58,7 +58,7 @@ class DenseWorkload:
     """MHA/GQA layers over [B, n_kv, L_max, d] caches (C2, C3).  Each layer
     runs the fused append-and-attend call (one kernel per layer-step)."""
 
-    kernel = "dense_mfma_kernel<false, true> (append + attend)"
+    kernel = "dense_mfma_kernel<false, true, false> (append + attend)"
     kernel_appends = True
 
     def __init__(self, cfg, slack, torch, kvc):
@@ -217,7 +217,7 @@ class MlaWorkload:
 class TopKWorkload:
     """Top-k sparse GQA over [B, n_kv, L_max, d] caches (C5)."""
 
-    kernel = "dense_mfma_kernel<true, false> (top-k)"
+    kernel = "dense_mfma_kernel<true, false, false> (top-k)"
     kernel_appends = False
 
     def __init__(self, cfg, slack, torch, kvc):

@@ -211,7 +211,7 @@ __device__ inline int attended_length(const DenseParams& p, int b, int j, int sp
   // One read; the empty asm keeps the compiler from reading it again later
   // (in the fused kernel the last workgroup of the sequence rewrites it).
   int n_raw = p.seq_lens[b];
-  asm volatile("" : "+v"(n_raw));
+  asm volatile("" : "+s"(n_raw));
   if constexpr (!APPEND) {
     return min(max(n_raw, 0), p.L_max);
   } else {
@@ -286,72 +286,97 @@ struct Chunk {
   uint32_t vmask;   // top-k: slot g*8+e valid
 };
 
-template <bool TOPK>
-__device__ inline void load_chunk(Chunk& c, int cs, int end, int n,
+// Loads are issued unconditionally; a chunk past the end of the split
+// (cs >= end) gets offsets beyond the buffer, which read zeros without
+// touching memory.  Keeping the loads out of branches lets the compiler
+// wait for exactly the chunk being computed while the next one is in flight.
+__device__ inline void load_chunk(Chunk& c, int cs, int end,
                                   __amdgpu_buffer_rsrc_t kr,
-                                  __amdgpu_buffer_rsrc_t vr,
-                                  __amdgpu_buffer_rsrc_t ir, int r, int g,
-                                  bool& bad) {
+                                  __amdgpu_buffer_rsrc_t vr, int r, int g) {
   constexpr uint32_t kRow = 256;
-  if constexpr (!TOPK) {
+  {
+    const bool live = cs < end;
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
       const uint32_t row = cs + (r >> 2) * 8 + a * 4 + (r & 3);
+      const uint32_t kb = live ? row * kRow + g * 16 : kOobOffset;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
-        c.k[a][kk] = buf_load16_stream(kr, row * kRow + kk * 64 + g * 16);
+        c.k[a][kk] = buf_load16_stream(kr, kb + kk * 64);
     }
+    const uint32_t vb = live ? (uint32_t)(cs + g * 8) * kRow + r * 16 : kOobOffset;
 #pragma unroll
     for (int e = 0; e < 8; ++e)
-      c.v[e] = buf_load16_stream(vr, (uint32_t)(cs + g * 8 + e) * kRow + r * 16);
+      c.v[e] = buf_load16_stream(vr, vb + e * kRow);
     c.vmask = 0xFF;
-  } else {
-    // slots for the V rows: cs + g*8 + 0..7; for the K rows: cs + pi(a, r).
-    const u32x4 i0 = buf_load16(ir, (uint32_t)(cs + g * 8) * 4);
-    const u32x4 i1 = buf_load16(ir, (uint32_t)(cs + g * 8 + 4) * 4);
-    const uint32_t iv[8] = {i0[0], i0[1], i0[2], i0[3], i1[0], i1[1], i1[2], i1[3]};
-    uint32_t mask = 0;
+  }
+}
+
+// Top-k: the list entries a chunk needs, loaded one chunk ahead of the rows
+// they address (entries past K read as zero and are masked).  Lane (r, g)
+// takes the slots of its V rows, cs + g*8 + 0..7, and of its K rows,
+// cs + pi(a, r).
+struct ChunkIdx {
+  u32x4 v0, v1;
+  uint32_t k[2];
+};
+
+__device__ inline void load_idx(ChunkIdx& x, int cs, __amdgpu_buffer_rsrc_t ir, int r, int g) {
+  x.v0 = buf_load16(ir, (uint32_t)(cs + g * 8) * 4);
+  x.v1 = buf_load16(ir, (uint32_t)(cs + g * 8 + 4) * 4);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int slot = cs + g * 8 + e;
-      const bool in_list = slot < end;
-      const bool ok = iv[e] < (uint32_t)n;
-      if (in_list && !ok) bad = true;
-      const bool use = in_list && ok;
-      mask |= (use ? 1u : 0u) << e;
-      c.v[e] = buf_load16_stream(vr, use ? iv[e] * kRow + r * 16 : kOobOffset);
-    }
-    c.vmask = mask;
+  for (int a = 0; a < 2; ++a)
+    x.k[a] = __builtin_amdgcn_raw_buffer_load_b32(
+        ir, (uint32_t)(cs + (r >> 2) * 8 + a * 4 + (r & 3)) * 4, 0, 0);
+}
+
+__device__ inline void load_listed(Chunk& c, const ChunkIdx& x, int cs, int end, int n,
+                                   __amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr,
+                                   int r, int g, bool& bad) {
+  constexpr uint32_t kRow = 256;
+  const uint32_t iv[8] = {x.v0[0], x.v0[1], x.v0[2], x.v0[3], x.v1[0], x.v1[1], x.v1[2], x.v1[3]};
+  uint32_t mask = 0;
 #pragma unroll
-    for (int a = 0; a < 2; ++a) {
-      const int slot = cs + (r >> 2) * 8 + a * 4 + (r & 3);
-      const uint32_t t = __builtin_amdgcn_raw_buffer_load_b32(ir, (uint32_t)slot * 4, 0, 0);
-      const bool use = slot < end && t < (uint32_t)n;
+  for (int e = 0; e < 8; ++e) {
+    const bool in_list = cs + g * 8 + e < end;
+    const bool ok = iv[e] < (uint32_t)n;
+    if (in_list && !ok) bad = true;
+    const bool use = in_list && ok;
+    mask |= (use ? 1u : 0u) << e;
+    c.v[e] = buf_load16_stream(vr, use ? iv[e] * kRow + r * 16 : kOobOffset);
+  }
+  c.vmask = mask;
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-        c.k[a][kk] = buf_load16_stream(kr, use ? t * kRow + kk * 64 + g * 16 : kOobOffset);
-    }
+  for (int a = 0; a < 2; ++a) {
+    const int slot = cs + (r >> 2) * 8 + a * 4 + (r & 3);
+    const bool use = slot < end && x.k[a] < (uint32_t)n;
+    const uint32_t kb = use ? x.k[a] * kRow + g * 16 : kOobOffset;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) c.k[a][kk] = buf_load16_stream(kr, kb + kk * 64);
   }
 }
 
 // Fused append: the chunk holding the new token's slot takes that row from
 // k_new/v_new (the cache copy is being written concurrently).  Lane (r, g)
 // holds K rows pi(a, r) at columns kk*32 + g*8 and V rows g*8 + e at columns
-// r*8, so it copies the matching 16-byte pieces of the new rows.
-__device__ inline void patch_new_row(Chunk& c, int cs, int slot, const u32x4* kn,
-                                     const u32x4* vn, int r, int g) {
-  const int pos = slot - cs;
-  if (pos < 0 || pos >= kDenseChunk) return;
+// r*8; knr/vnr are its 16-byte pieces of the new rows (loaded once), swapped
+// in with selects so no load is waited on early.
+__device__ inline void patch_new_row(Chunk& c, int pos, const u32x4 (&knr)[4],
+                                     const u32x4& vnr, int r, int g) {
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
-    if ((r >> 2) * 8 + a * 4 + (r & 3) == pos) {
+    const bool mk = (r >> 2) * 8 + a * 4 + (r & 3) == pos;
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) c.k[a][kk] = kn[kk * 4 + g];
-    }
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) c.k[a][kk][w] = mk ? knr[kk][w] : c.k[a][kk][w];
   }
 #pragma unroll
-  for (int e = 0; e < 8; ++e)
-    if (g * 8 + e == pos) c.v[e] = vn[r];
+  for (int e = 0; e < 8; ++e) {
+    const bool mv = g * 8 + e == pos;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) c.v[e][w] = mv ? vnr[w] : c.v[e][w];
+  }
 }
 
 struct WaveState {
@@ -429,18 +454,20 @@ struct ChunkF8 {
 
 __device__ inline int fp8_q_col(int kk, int g) { return (kk >> 1) * 64 + g * 16 + (kk & 1) * 8; }
 
-__device__ inline void load_chunk(ChunkF8& c, int cs, __amdgpu_buffer_rsrc_t kr,
+__device__ inline void load_chunk(ChunkF8& c, int cs, int end, __amdgpu_buffer_rsrc_t kr,
                                   __amdgpu_buffer_rsrc_t vr, int r, int g) {
   constexpr uint32_t kRow = 128;
+  const bool live = cs < end;
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
     const uint32_t row = cs + (r >> 2) * 8 + a * 4 + (r & 3);
+    const uint32_t kb = live ? row * kRow + g * 16 : kOobOffset;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) c.k[a][h] = buf_load16_stream(kr, row * kRow + h * 64 + g * 16);
+    for (int h = 0; h < 2; ++h) c.k[a][h] = buf_load16_stream(kr, kb + h * 64);
   }
+  const uint32_t vb = live ? (uint32_t)(cs + g * 8) * kRow + r * 8 : kOobOffset;
 #pragma unroll
-  for (int e = 0; e < 8; ++e)
-    c.v[e] = buf_load8_stream(vr, (uint32_t)(cs + g * 8 + e) * kRow + r * 8);
+  for (int e = 0; e < 8; ++e) c.v[e] = buf_load8_stream(vr, vb + e * kRow);
 }
 
 __device__ inline void expand_chunk(const ChunkF8& f, Chunk& c) {
@@ -479,7 +506,8 @@ __global__ __launch_bounds__(256, 2) void dense_mfma_kernel(DenseParams p) {
   int start, end;
   dense_split_range(count, S, split, start, end);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, g = lane >> 4;
   const size_t unit = (size_t)b * p.n_kv + j;
   constexpr uint32_t kRowBytes = FP8 ? 128u : 256u;
@@ -515,42 +543,66 @@ __global__ __launch_bounds__(256, 2) void dense_mfma_kernel(DenseParams p) {
   constexpr int kStride = kDenseChunk * 4;
   // fused append: slot of the new row (or -1), and its source rows
   const int new_slot = (APPEND && ls.ok) ? ls.n_raw : -1;
-  const u32x4* kn = reinterpret_cast<const u32x4*>(p.k_new) + unit * 16;
-  const u32x4* vn = reinterpret_cast<const u32x4*>(p.v_new) + unit * 16;
+  u32x4 knr[4], vnr;
+  if constexpr (APPEND) {
+    const u32x4* kn = reinterpret_cast<const u32x4*>(p.k_new) + unit * 16;
+    const u32x4* vn = reinterpret_cast<const u32x4*>(p.v_new) + unit * 16;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) knr[kk] = kn[kk * 4 + g];
+    vnr = vn[r];
+  }
   using Raw = typename ChunkOf<FP8>::T;
-  auto load = [&](Raw& c, int at) {
-    if constexpr (FP8) {
-      load_chunk(c, at, kr, vr, r, g);
-    } else {
-      load_chunk<TOPK>(c, at, end, n, kr, vr, ir, r, g, bad);
-      if constexpr (APPEND) patch_new_row(c, at, new_slot, kn, vn, r, g);
-    }
-  };
-  auto compute = [&](const Raw& c, int at) {
+  auto load = [&](Raw& c, int at) { load_chunk(c, at, end, kr, vr, r, g); };
+  auto compute = [&](Raw& c, int at) {
     if constexpr (FP8) {
       Chunk x;
       expand_chunk(c, x);
       compute_chunk<false>(x, at, end, qop, p.scale_log2, g, st);
     } else {
+      // the chunk holding the new slot takes that row from k_new/v_new
+      if constexpr (APPEND)
+        if (new_slot >= at && new_slot < at + kDenseChunk)
+          patch_new_row(c, new_slot - at, knr, vnr, r, g);
       compute_chunk<TOPK>(c, at, end, qop, p.scale_log2, g, st);
     }
   };
-  if (cs < end) {
+  if constexpr (TOPK) {
+    if (cs < end) {
+      // list entries two chunks ahead, rows one chunk ahead
+      Chunk A, Bc;
+      ChunkIdx I0, I1;
+      load_idx(I0, cs, ir, r, g);
+      load_idx(I1, cs + kStride, ir, r, g);
+      load_listed(A, I0, cs, end, n, kr, vr, r, g, bad);
+      while (true) {
+        load_idx(I0, cs + 2 * kStride, ir, r, g);
+        load_listed(Bc, I1, cs + kStride, end, n, kr, vr, r, g, bad);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(A, cs);
+        cs += kStride;
+        if (cs >= end) break;
+        load_idx(I1, cs + 2 * kStride, ir, r, g);
+        load_listed(A, I0, cs + kStride, end, n, kr, vr, r, g, bad);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(Bc, cs);
+        cs += kStride;
+        if (cs >= end) break;
+      }
+    }
+  } else if (cs < end) {
     Raw A, Bc;
     load(A, cs);
     while (true) {
-      int cn = cs + kStride;
-      bool more = cn < end;
-      if (more) load(Bc, cn);
+      load(Bc, cs + kStride);
+      __builtin_amdgcn_sched_barrier(0);   // the next chunk's loads go out first
       compute(A, cs);
-      if (!more) break;
-      cs = cn;
-      cn = cs + kStride;
-      more = cn < end;
-      if (more) load(A, cn);
+      cs += kStride;
+      if (cs >= end) break;
+      load(A, cs + kStride);
+      __builtin_amdgcn_sched_barrier(0);
       compute(Bc, cs);
-      if (!more) break;
-      cs = cn;
+      cs += kStride;
+      if (cs >= end) break;
     }
   }
   if constexpr (TOPK) {

@@ -26,10 +26,11 @@ COPY_BYTES = 1 << 30
 
 # dominant kernel of each bench workload (substring of the demangled name)
 DOMINANT = {
-    "C2": "dense_mfma_kernel<false, true>",
-    "C3": "dense_mfma_kernel<false, true>",
+    "C2": "dense_mfma_kernel<false, true, false>",
+    "C3": "dense_mfma_kernel<false, true, false>",
     "C4": "mla_kernel",
-    "C5": "dense_mfma_kernel<true, false>",
+    "C5": "dense_mfma_kernel<true, false, false>",
+    "C3F8": "dense_mfma_kernel<false, false, true>",
 }
 
 

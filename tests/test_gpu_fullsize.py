@@ -1,0 +1,206 @@
+"""Parity at the benchmark's full sizes (MI355X).
+
+Each test builds one layer of a benchmark workload at its real shape on the
+device (seeded N(0,1), the same generators and split policy the benchmark
+uses), runs the calls the benchmark times, and checks a sample of the
+outputs against the fp64 oracle on host copies of just the rows those
+outputs depend on.  Appended rows and lengths are checked bit for bit.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import kvc_synth as syn
+import oracle
+from gpu_helpers import compare, compare_lse, host
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+import kv_cache_decode_kvc_amd as kvc  # noqa: E402
+
+
+@pytest.fixture(autouse=True)
+def _gpu_only():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU (run with -m 'not gpu' elsewhere)")
+    kvc.kvc_set_split_override(0)
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def normal(shape, cfg_id, layer, tensor):
+    t = torch.empty(*shape, dtype=torch.bfloat16, device="cuda")
+    return syn.device_normal_(t, syn.device_seed(cfg_id, layer, tensor))
+
+
+def bits(t):
+    """bf16 device tensor -> host uint16 bit patterns."""
+    return host(t.contiguous())
+
+
+def sample_units(pre, n_kv, count, seed):
+    """(b, j) pairs: the longest and shortest sequences plus a seeded draw."""
+    rng = np.random.default_rng(seed)
+    bs = {int(np.argmax(pre)), int(np.argmin(pre))}
+    bs |= set(int(x) for x in rng.choice(len(pre), size=min(count, len(pre)), replace=False))
+    return [(b, int(rng.integers(n_kv))) for b in sorted(bs)]
+
+
+def check_dense_units(cfg, pre, q, K, V, out, lse, units, what):
+    G = cfg.n_h // cfg.n_kv
+    for b, j in units:
+        n = int(pre[b]) + 1
+        kb = bits(K[b, j, :n])[None, None]
+        vb = bits(V[b, j, :n])[None, None]
+        qb = bits(q[b, j * G:(j + 1) * G])[None]
+        o_ref, l_ref = oracle.decode(qb, kb, vb, np.array([n], np.int32), cfg.scale)
+        got = oracle.to_f64(bits(out[b, j * G:(j + 1) * G]))
+        compare(got, o_ref[0], 2e-2, f"{what} b={b} j={j} n={n}")
+        compare_lse(host(lse[b, j * G:(j + 1) * G]), l_ref[0], 4e-3)
+
+
+def test_fullsize_mha_layer():
+    """32-head MHA layer, 4096 cached + 1 appended, fused append + attend."""
+    c = syn.C2
+    _fused_dense(c, units=[(0, j) for j in range(c.n_kv)])
+
+
+def test_fullsize_gqa_layer():
+    """GQA layer, B = 32, lengths U[1024, 32768], fused append + attend."""
+    c = syn.C3
+    pre = syn.pre_append_lens(c)
+    _fused_dense(c, units=sample_units(pre, c.n_kv, 4, 31))
+
+
+def _fused_dense(c, units):
+    pre = syn.pre_append_lens(c)
+    L_max = int(max(c.L_max, pre.max() + 1))
+    K = normal((c.B, c.n_kv, L_max, c.d), c.cfg_id, 0, "k")
+    V = normal((c.B, c.n_kv, L_max, c.d), c.cfg_id, 0, "v")
+    q = normal((c.B, c.n_h, c.d), c.cfg_id, 0, "q")
+    kn = normal((c.B, c.n_kv, c.d), c.cfg_id, 0, "k_new")
+    vn = normal((c.B, c.n_kv, c.d), c.cfg_id, 0, "v_new")
+    sl = torch.tensor(pre, dtype=torch.int32, device="cuda")
+    out = torch.empty_like(q)
+    lse = torch.empty(c.B, c.n_h, dtype=torch.float32, device="cuda")
+    ws = kvc.workspace(kvc.kvc_append_decode_attn_workspace_size(c.B, c.n_h, c.n_kv, L_max, c.d,
+                                                                 kvc.KVC_BF16))
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    kvc.kvc_append_decode_attn(q, K, V, sl, kn, vn, out, lse, scale=c.scale, flag=flag,
+                               workspace=ws)
+    torch.cuda.synchronize()
+    assert host(sl).tolist() == (pre + 1).tolist()
+    assert int(host(flag)[0]) == 0
+    for b, j in units:
+        assert np.array_equal(bits(K[b, j, pre[b]]), bits(kn[b, j]))
+        assert np.array_equal(bits(V[b, j, pre[b]]), bits(vn[b, j]))
+    check_dense_units(c, pre, q, K, V, out, lse, units, c.name)
+
+
+def test_fullsize_gqa_layer_fp8():
+    """The GQA layer over E4M3 caches: append_fp8 then decode_fp8."""
+    c = syn.C3
+    pre = syn.pre_append_lens(c)
+    L_max = int(max(c.L_max, pre.max() + 1))
+    ks, vs = 1.0 / 64, 1.0 / 64
+    G = c.n_h // c.n_kv
+
+    def codes(tensor, scale):
+        t = torch.empty(c.B, c.n_kv, L_max, c.d, dtype=torch.uint8, device="cuda")
+        flat = t.view(-1)
+        g = torch.Generator(device="cuda")
+        g.manual_seed(syn.device_seed(c.cfg_id, 0, tensor))
+        step = 1 << 26
+        for s in range(0, flat.numel(), step):
+            e = min(flat.numel(), s + step)
+            x = torch.randn(e - s, generator=g, device="cuda", dtype=torch.float32) / scale
+            flat[s:e].copy_(x.to(torch.float8_e4m3fn).view(torch.uint8))
+        return t
+
+    K8, V8 = codes("k", ks), codes("v", vs)
+    q = normal((c.B, c.n_h, c.d), c.cfg_id, 0, "q")
+    kn = normal((c.B, c.n_kv, c.d), c.cfg_id, 0, "k_new")
+    vn = normal((c.B, c.n_kv, c.d), c.cfg_id, 0, "v_new")
+    sl = torch.tensor(pre, dtype=torch.int32, device="cuda")
+    out = torch.empty_like(q)
+    lse = torch.empty(c.B, c.n_h, dtype=torch.float32, device="cuda")
+    ws = kvc.workspace(kvc.kvc_decode_attn_fp8_workspace_size(c.B, c.n_h, c.n_kv, L_max, c.d))
+    kvc.kvc_append_fp8(K8, V8, sl, kn, vn, ks, vs)
+    kvc.kvc_decode_attn_fp8(q, K8, V8, sl, out, ks, vs, lse, scale=c.scale, workspace=ws)
+    torch.cuda.synchronize()
+    assert host(sl).tolist() == (pre + 1).tolist()
+    for b, j in sample_units(pre, c.n_kv, 4, 33):
+        n = int(pre[b]) + 1
+        assert np.array_equal(host(K8[b, j, pre[b]]), oracle.quantize_fp8(bits(kn[b, j]), ks))
+        assert np.array_equal(host(V8[b, j, pre[b]]), oracle.quantize_fp8(bits(vn[b, j]), vs))
+        o_ref, l_ref = oracle.decode_fp8(bits(q[b, j * G:(j + 1) * G])[None],
+                                         host(K8[b, j, :n])[None, None],
+                                         host(V8[b, j, :n])[None, None],
+                                         np.array([n], np.int32), c.scale, ks, vs)
+        got = oracle.to_f64(bits(out[b, j * G:(j + 1) * G]))
+        compare(got, o_ref[0], 2e-2, f"fp8 b={b} j={j} n={n}")
+        compare_lse(host(lse[b, j * G:(j + 1) * G]), l_ref[0], 4e-3)
+
+
+def test_fullsize_mla_layer():
+    """Latent-cache layer: B = 64, 128 heads, 8192 cached + 1 appended."""
+    c = syn.C4
+    D = c.d_c + c.d_r
+    L_max = c.L_max
+    C = normal((c.B, L_max, D), c.cfg_id, 0, "ckv")
+    q = normal((c.B, c.n_h, D), c.cfg_id, 0, "q")
+    cn = normal((c.B, D), c.cfg_id, 0, "ckv_new")
+    pre = np.full(c.B, c.pre_len, dtype=np.int32)
+    sl = torch.tensor(pre, dtype=torch.int32, device="cuda")
+    out = torch.empty(c.B, c.n_h, c.d_c, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(c.B, c.n_h, dtype=torch.float32, device="cuda")
+    ws = kvc.workspace(kvc.kvc_decode_attn_mla_workspace_size(c.B, c.n_h, L_max, c.d_c, c.d_r,
+                                                              kvc.KVC_BF16))
+    kvc.kvc_append(C, None, sl, cn, None)
+    kvc.kvc_decode_attn_mla(q, C, sl, out, lse, scale=c.scale, workspace=ws)
+    torch.cuda.synchronize()
+    assert host(sl).tolist() == (pre + 1).tolist()
+    for b in (0, 37, 63):
+        assert np.array_equal(bits(C[b, c.pre_len]), bits(cn[b]))
+        o_ref, l_ref = oracle.decode_mla(bits(q[b])[None], bits(C[b])[None],
+                                         np.array([c.pre_len + 1], np.int32), c.d_c, c.d_r, c.scale)
+        compare(oracle.to_f64(bits(out[b])), o_ref[0], 2e-2, f"mla b={b}")
+        compare_lse(host(lse[b]), l_ref[0], 4e-3)
+
+
+def test_fullsize_topk_layer():
+    """Top-k layer: B = 8, 2048 listed positions of 131072 per KV head."""
+    c = syn.C5
+    L_max = c.L_max
+    K = normal((c.B, c.n_kv, L_max, c.d), c.cfg_id, 0, "k")
+    V = normal((c.B, c.n_kv, L_max, c.d), c.cfg_id, 0, "v")
+    q = normal((c.B, c.n_h, c.d), c.cfg_id, 0, "q")
+    kn = normal((c.B, c.n_kv, c.d), c.cfg_id, 0, "k_new")
+    vn = normal((c.B, c.n_kv, c.d), c.cfg_id, 0, "v_new")
+    idx_h = syn.topk_indices(c.cfg_id, 0, c.B, c.n_kv, c.K, c.pre_len, index_set=0)
+    idx = torch.from_numpy(idx_h).cuda()
+    pre = np.full(c.B, c.pre_len, dtype=np.int32)
+    sl = torch.tensor(pre, dtype=torch.int32, device="cuda")
+    out = torch.empty_like(q)
+    lse = torch.empty(c.B, c.n_h, dtype=torch.float32, device="cuda")
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ws = kvc.workspace(kvc.kvc_decode_attn_topk_workspace_size(c.B, c.n_h, c.n_kv, c.K, c.d,
+                                                               kvc.KVC_BF16))
+    kvc.kvc_append(K, V, sl, kn, vn)
+    kvc.kvc_decode_attn_topk(q, K, V, sl, idx, out, lse, scale=c.scale, flag=flag, workspace=ws)
+    torch.cuda.synchronize()
+    assert int(host(flag)[0]) == 0
+    G = c.n_h // c.n_kv
+    for b, j in [(0, 0), (3, 5), (7, 7)]:
+        n = c.pre_len + 1
+        kb = bits(K[b, j, :n])[None, None]
+        vb = bits(V[b, j, :n])[None, None]
+        qb = bits(q[b, j * G:(j + 1) * G])[None]
+        o_ref, l_ref, f_ref = oracle.decode_topk(qb, kb, vb, np.array([n], np.int32),
+                                                 idx_h[b:b + 1, j:j + 1], c.scale)
+        assert f_ref == 0
+        compare(oracle.to_f64(bits(out[b, j * G:(j + 1) * G])), o_ref[0], 2e-2, f"topk b={b} j={j}")
+        compare_lse(host(lse[b, j * G:(j + 1) * G]), l_ref[0], 4e-3)
