@@ -35,8 +35,9 @@
 // tiles in flight while one is read), with 16-byte piece k of row rho stored
 // at k ^ key(rho), key = bit-reverse of (rho >> 1) & 7: conflict-free for
 // the 16-byte score and value reads on the 64-bank LDS.  Rows at or past the sequence length read as zeros (buffer range
-// check) and are masked.  Splits of one sequence are merged by log-sum-exp by
-// the last workgroup to finish.
+// check) and are masked.  Splits of one sequence publish normalised partials
+// and a second kernel, spread over every compute unit, merges them by
+// log-sum-exp.
 
 #include "kvc_device.h"
 #include "kvc_internal.h"
@@ -92,6 +93,17 @@ __device__ inline void issue_tile(char* stage, __amdgpu_buffer_rsrc_t cr, int cs
   }
 }
 
+// One 1-KB block of a tile (block index blk of the 36).
+__device__ inline void issue_block(char* stage, __amdgpu_buffer_rsrc_t cr, int cs,
+                                   int blk, int lane) {
+  const int byte = blk * 1024 + lane * 16;
+  const int rho = byte / kRowB;
+  const int pc = (byte - rho * kRowB) >> 4;
+  const uint32_t goff = (uint32_t)(rho * kRowB + ((pc ^ swz_key(rho)) << 4));
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      cr, (lds_void*)(stage + blk * 1024), 16, goff, cs * kRowB, 0, kStream);
+}
+
 __device__ inline u32x4 lds_load16(const char* base, uint32_t off) {
   return *reinterpret_cast<const u32x4*>(base + off);
 }
@@ -127,13 +139,20 @@ __device__ inline bool any_vote(const int* v) {
 }
 
 
+template <int NW>
+__device__ inline bool any_vote4(u32x4 v) {
+  uint32_t x = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) x |= v[w];
+  return x != 0;
+}
+
 }  // namespace
 
 template <int NW>
 __global__ __launch_bounds__(NW * 64, 1) void mla_kernel(MlaParams p) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  __shared__ int s_last;
-  __shared__ int s_vote[2][4];         // per chunk parity: wave needs a restart
+  __shared__ __attribute__((aligned(16))) int s_vote[2][4];         // per chunk parity: wave needs a restart
   constexpr int kHpw = 32 * NW;        // heads per workgroup
   constexpr int kLpt = 36 / NW;        // 1-KB blocks each wave copies per tile
 
@@ -149,7 +168,8 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_kernel(MlaParams p) {
   if (u >= units) return;
   const int b = u / p.P_max, split = u % p.P_max;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 31, g = lane >> 5;
   const int h = hg * kHpw + wave * 32 + r;
   const size_t bh = (size_t)b * p.n_h + h;
@@ -197,6 +217,15 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_kernel(MlaParams p) {
     wpv[q4] = (uint32_t)(row * kRowB + ((8 * (r >> 3) + ((r & 7) ^ swz_key(row))) << 4));
   }
 
+  // The first tile copies go out before the query loads, so the two
+  // latencies overlap.
+  auto issue_first = [&]() {
+    issue_tile<kLpt>(smem, cr, start, blk0, lane);
+    if (nchunks > 1) issue_tile<kLpt>(smem + kTileB, cr, start + kMlaChunk, blk0, lane);
+    if (nchunks > 2) issue_tile<kLpt>(smem + 2 * kTileB, cr, start + 2 * kMlaChunk, blk0, lane);
+  };
+  issue_first();
+
   bf16x8 qop[kQRegs];
   const uint32_t qpark = (uint32_t)(kParkOff + (wave * kQPark * 64 + lane) * 16);
   {
@@ -212,7 +241,10 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_kernel(MlaParams p) {
 
   // Scores of one chunk (stage offset toff).  The LDS reads run kQkAhead
   // k-steps ahead of the MFMAs; the scheduling barriers keep that order.
-  auto scores = [&](uint32_t toff) {
+  // The copy of a later tile (when dma) is issued one block every NW
+  // k-steps (kLpt = 36 / NW blocks per wave): each block occupies the address unit for a while, and spread
+  // out its issue hides behind the MFMAs instead of stalling the wave.
+  auto scores = [&](uint32_t toff, bool dma, char* dstage, int dcs) {
     uint32_t qb[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
@@ -233,6 +265,7 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_kernel(MlaParams p) {
     for (int k = 0; k < kKSteps; ++k) {
       const bf16x8 bop = k < kQRegs ? qop[k < kQRegs ? k : 0] : as_bf16x8(Bq[k % kQkAhead]);
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(A[k % kQkAhead]), bop, s, 0, 0, 0);
+      if (k % NW == 1 && dma) issue_block(dstage, cr, dcs, blk0 + k / NW, lane);
       const int kn = k + kQkAhead;
       if (kn < kKSteps) {
         A[k % kQkAhead] = lds_load16(smem, qb[kn & 3] + (kn >> 2) * 128);
@@ -254,16 +287,15 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_kernel(MlaParams p) {
   // the split once for each head's largest score (scores only), and
   // accumulate again against that without further votes: at most three
   // passes.
-  bool scan = false, scanned = false;
+  bool scan = false, scanned = false, first_pass = true;
   for (;;) {
 #pragma unroll
     for (int m = 0; m < kColTiles; ++m)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[m][i] = 0.f;
     l_run = 0.f;
-    issue_tile<kLpt>(smem, cr, start, blk0, lane);
-    if (nchunks > 1) issue_tile<kLpt>(smem + kTileB, cr, start + kMlaChunk, blk0, lane);
-    if (nchunks > 2) issue_tile<kLpt>(smem + 2 * kTileB, cr, start + 2 * kMlaChunk, blk0, lane);
+    if (!first_pass) issue_first();
+    first_pass = false;
     // (tile k >= 3 is issued at the top of chunk k - 2, into the stage of
     // chunk k - 3)
 
@@ -278,14 +310,28 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_kernel(MlaParams p) {
       else if (c + 1 < nchunks) wait_vmcnt<kLpt>();
       else wait_vmcnt<0>();
       lds_barrier();
-      if (c > 0 && !scan && !scanned) {
-        if (any_vote<NW>(s_vote[(c - 1) & 1])) { restart = true; break; }
-      }
-      if (c >= 1 && c + 2 < nchunks)
-        issue_tile<kLpt>(smem + ((c + 2) % kStages) * kTileB, cr, cs + 2 * kMlaChunk, blk0, lane);
+      // (the votes on chunk c - 1 are read here and tested after this
+      // chunk's scores, so the read's latency hides behind the MFMAs)
+      const u32x4 vw = *reinterpret_cast<const u32x4*>(s_vote[(c - 1) & 1]);
       const uint32_t toff = (uint32_t)((c % kStages) * kTileB);
+      const f32x16 S = scores(toff, c >= 1 && c + 2 < nchunks,
+                              smem + ((c + 2) % kStages) * kTileB, cs + 2 * kMlaChunk);
+      if (c > 0 && !scan && !scanned && any_vote4<NW>(vw)) { restart = true; break; }
 
-      const f32x16 S = scores(toff);
+      // value rows of the first column block, read ahead of the softmax
+      uint32_t pb[4];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        pb[q4] = toff + wpv[q4];
+        asm volatile("" : "+v"(pb[q4]));
+      }
+      auto pv_read = [&](u32x4 (&vr)[8], int s2, int cb) {
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj)
+          vr[jj] = lds_load16(smem, pb[jj >> 1] + (jj & 1) * kRowB + s2 * 16 * kRowB + cb * 512);
+      };
+      u32x4 va[8], vb[8];
+      pv_read(va, 0, 0);
 
       // weights of this lane's 16 positions of head r
       float sv[16];
@@ -296,13 +342,21 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_kernel(MlaParams p) {
         for (int i = 0; i < 16; ++i)
           if (cs + 16 * (i >> 3) + 8 * g + (i & 7) >= end) sv[i] = kNegInf;
       }
+      // This lane's max over its 16 positions.  The two lanes of a head
+      // (g = 0, 1) agree on the reference only through the first valid
+      // chunk's exchange; afterwards each tests its own half against it, so
+      // no cross-lane (LDS-pipe) operation sits in the steady-state loop.
       float mx = kNegInf;
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sv[i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
       m_seen = fmaxf(m_seen, mx);
       if (scan) continue;
-      if (m_ref == kNegInf) m_ref = mx;       // first valid chunk (nothing accumulated yet)
+      if (__builtin_amdgcn_readfirstlane(__float_as_int(m_ref)) == __float_as_int(kNegInf)) {
+        // first valid chunk (nothing accumulated yet); the empty asm keeps
+        // the exchange inside this branch
+        asm volatile("" ::: "memory");
+        m_ref = fmaxf(mx, __shfl_xor(mx, 32));
+      }
       // (every lane writes the wave's vote; a score this far above the
       // reference may overflow the weights below, and the vote discards the
       // pass)
@@ -329,40 +383,37 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_kernel(MlaParams p) {
 
       // weighted sum of the latents of chunk c: per column block cb and
       // k-step s2, 8 row reads (16 B each) and an 8 x 8 register transpose
-      // give the A operands of 8 MFMAs (tiles cb * 8 + m)
-      uint32_t pb[4];
+      // give the A operands of 8 MFMAs (tiles cb * 8 + m).  The reads of the
+      // next (s2, cb) group go out before the current group's MFMAs.
+      auto pv_mma = [&](const u32x4 (&vr)[8], int s2, int cb) {
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        pb[q4] = toff + wpv[q4];
-        asm volatile("" : "+v"(pb[q4]));
-      }
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb) {
-          u32x4 vr[8];
-#pragma unroll
-          for (int jj = 0; jj < 8; ++jj)
-            vr[jj] = lds_load16(smem, pb[jj >> 1] + (jj & 1) * kRowB + s2 * 16 * kRowB + cb * 512);
-#pragma unroll
-          for (int m = 0; m < 8; ++m) {
-            const uint32_t sel = (m & 1) ? 0x07060302u : 0x05040100u;
-            const int dw = m >> 1;
-            u32x4 a;
-            a[0] = __builtin_amdgcn_perm(vr[1][dw], vr[0][dw], sel);
-            a[1] = __builtin_amdgcn_perm(vr[3][dw], vr[2][dw], sel);
-            a[2] = __builtin_amdgcn_perm(vr[5][dw], vr[4][dw], sel);
-            a[3] = __builtin_amdgcn_perm(vr[7][dw], vr[6][dw], sel);
-            acc[cb * 8 + m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), pop[s2],
-                                                                       acc[cb * 8 + m], 0, 0, 0);
-          }
+        for (int m = 0; m < 8; ++m) {
+          const uint32_t sel = (m & 1) ? 0x07060302u : 0x05040100u;
+          const int dw = m >> 1;
+          u32x4 a;
+          a[0] = __builtin_amdgcn_perm(vr[1][dw], vr[0][dw], sel);
+          a[1] = __builtin_amdgcn_perm(vr[3][dw], vr[2][dw], sel);
+          a[2] = __builtin_amdgcn_perm(vr[5][dw], vr[4][dw], sel);
+          a[3] = __builtin_amdgcn_perm(vr[7][dw], vr[6][dw], sel);
+          acc[cb * 8 + m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), pop[s2],
+                                                                     acc[cb * 8 + m], 0, 0, 0);
         }
-      }
+      };
+      pv_read(vb, 0, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      pv_mma(va, 0, 0);
+      pv_read(va, 1, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      pv_mma(vb, 0, 1);
+      pv_read(vb, 1, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      pv_mma(va, 1, 0);
+      pv_mma(vb, 1, 1);
     }
     if (scan) {
       scan = false;
       scanned = true;
-      m_ref = m_seen;
+      m_ref = fmaxf(m_seen, __shfl_xor(m_seen, 32));
     } else {
       if (!restart && !scanned) {
         // votes on the last chunk
@@ -401,89 +452,105 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_kernel(MlaParams p) {
     return;
   }
 
-  // Several splits: publish this one with device-coherent stores; the last
-  // workgroup of the (sequence, head group) to take a ticket merges them.
-  // A split's partial block is in register order: slot k of lane l of wave w
-  // (k = 4 * tile + quad, 64 slots of 4 floats) is at ((w * 64 + k) * 64 + l)
-  // * 4 floats, so every store and load moves 1 KB contiguous per wave.
-  const __amdgpu_buffer_rsrc_t wo = make_rsrc(p.ws_o, kWsRecords);
-  const __amdgpu_buffer_rsrc_t wl = make_rsrc(p.ws_lse, kWsRecords);
-  const size_t unit_hg = (size_t)b * groups + hg;
-  constexpr size_t kBlock = (size_t)NW * 64 * 256;     // floats per split block
-  const uint32_t lane_off = (uint32_t)((wave * 64 * 64 + lane) * 16);
+  // Several splits: publish this one; mla_merge_kernel (launched next on
+  // the same stream, so the kernel boundary makes the stores visible to every
+  // XCD) combines them.  A split's partial block is in register order: slot k
+  // of lane l of wave w (k = 4 * tile + quad, 64 slots of 4 floats) is at
+  // ((w * 64 + k) * 64 + l) * 4 floats, so every store moves 1 KB contiguous
+  // per wave.
   {
-    const uint32_t blk = (uint32_t)((unit_hg * p.P_max + split) * kBlock * 4);
+    const size_t unit_hg = (size_t)b * groups + hg;
+    constexpr size_t kBlock = (size_t)NW * 64 * 256;     // floats per split block
+    f32x4* blk = reinterpret_cast<f32x4*>(p.ws_o + (unit_hg * p.P_max + split) * kBlock) +
+                 wave * 64 * 64 + lane;
 #pragma unroll
     for (int t = 0; t < kColTiles; ++t)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const f32x4 v = {acc[t][4 * q4] * inv, acc[t][4 * q4 + 1] * inv,
-                         acc[t][4 * q4 + 2] * inv, acc[t][4 * q4 + 3] * inv};
-        store_coherent(wo, blk + lane_off + (uint32_t)((4 * t + q4) * 64 * 16), v);
-      }
-    if (g == 0)
-      store_coherent(wl, (uint32_t)(((unit_hg * p.P_max + split) * kHpw + wave * 32 + r) * 4), lse2);
+      for (int q4 = 0; q4 < 4; ++q4)
+        blk[(4 * t + q4) * 64] = f32x4{acc[t][4 * q4] * inv, acc[t][4 * q4 + 1] * inv,
+                                       acc[t][4 * q4 + 2] * inv, acc[t][4 * q4 + 3] * inv};
+    if (g == 0) p.ws_lse[(unit_hg * p.P_max + split) * kHpw + wave * 32 + r] = lse2;
   }
-  wait_vm_all();
-  __syncthreads();
-  int32_t* ticket = p.ws_cnt + unit_hg;
-  if (tid == 0) s_last = (atomicAdd(ticket, 1) == nsplit - 1);
-  __syncthreads();
-  if (!s_last) return;
+}
 
-  // Last split to finish: every lane combines the same slots of all the
-  // splits' blocks (its own included) by log-sum-exp weights, 8 slots (one
-  // column block cb, quad q4) at a time with the loads of up to 4 splits in
-  // flight together.
-  const size_t lse_base = unit_hg * p.P_max * kHpw + wave * 32 + r;
+// Split merge: one workgroup (NW waves, the main kernel's lane layout) per
+// (sequence, head group, column block cb, quad q4).  Every lane combines the
+// same 8 slots (tiles cb*8 + m, quad q4) of all the splits' blocks by
+// log-sum-exp weights, with the loads of up to 4 splits in flight together.
+// Sequences that needed one split (or none) were finished by the main kernel.
+// (Register budget for two waves per SIMD, so that all 32 slot loads of a
+// batch stay in flight together.)
+template <int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 2)))
+void mla_merge_kernel(MlaParams p) {
+  constexpr int kHpw = 32 * NW;
+  constexpr size_t kBlock = (size_t)NW * 64 * 256;
+  const int groups = p.n_h / kHpw;
+  int id = blockIdx.x;
+  const int part = id & 7;
+  id >>= 3;
+  const int hg = id % groups, b = id / groups;
+  const int cb = part >> 2, q4 = part & 3;
+  const int n = min(max(p.seq_lens[b], 0), p.L_max);
+  const int nsplit = (n + p.S - 1) / p.S;
+  if (nsplit <= 1) return;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = lane & 31, g = lane >> 5;
+  const int h = hg * kHpw + wave * 32 + r;
+  const size_t bh = (size_t)b * p.n_h + h;
+  const size_t unit_hg = (size_t)b * groups + hg;
+
+  // Two round trips for 4 splits: the partial lse values (8 at a time, for
+  // the max), then each batch of 4 splits' slots with their lse.
+  const float* lse_p = p.ws_lse + unit_hg * p.P_max * kHpw + wave * 32 + r;
   float M = kNegInf;
-  for (int s2 = 0; s2 < nsplit; ++s2)
-    M = fmaxf(M, load_coherent1(wl, (uint32_t)((lse_base + (size_t)s2 * kHpw) * 4)));
+  for (int s0 = 0; s0 < nsplit; s0 += 8) {
+    float t[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) t[u] = lse_p[(size_t)min(s0 + u, nsplit - 1) * kHpw];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) M = fmaxf(M, t[u]);
+  }
   const float Mu = (M == kNegInf) ? 0.f : M;
+
+  const f32x4* base = reinterpret_cast<const f32x4*>(p.ws_o + unit_hg * p.P_max * kBlock) +
+                      wave * 64 * 64 + lane;
+  f32x4 sum[8];
+#pragma unroll
+  for (int m = 0; m < 8; ++m) sum[m] = f32x4{0.f, 0.f, 0.f, 0.f};
   float Z = 0.f;
-  for (int s2 = 0; s2 < nsplit; ++s2) {
-    const float ls = load_coherent1(wl, (uint32_t)((lse_base + (size_t)s2 * kHpw) * 4));
-    Z += ls == kNegInf ? 0.f : __builtin_amdgcn_exp2f(ls - Mu);
+  for (int s0 = 0; s0 < nsplit; s0 += 4) {
+    f32x4 v[4][8];
+    float ls[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int su = min(s0 + u, nsplit - 1);
+      ls[u] = lse_p[(size_t)su * kHpw];
+      const f32x4* blk = base + (size_t)su * (kBlock / 4);
+#pragma unroll
+      for (int m = 0; m < 8; ++m) v[u][m] = blk[(4 * (cb * 8 + m) + q4) * 64];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float w = (s0 + u >= nsplit || ls[u] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(ls[u] - Mu);
+      Z += w;
+#pragma unroll
+      for (int m = 0; m < 8; ++m) sum[m] += w * v[u][m];
+    }
   }
   const float zi = Z > 0.f ? 1.f / Z : 0.f;
+  // slot (cb*8 + m, q4) element e is column 256cb + 8(8 q4 + 4g + e) + m
   uint16_t* orow = (uint16_t*)p.out + bh * kMlaDc;
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb)
+  for (int e = 0; e < 4; ++e) {
+    u32x4 o;
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      f32x4 sum[8];
-#pragma unroll
-      for (int m = 0; m < 8; ++m) sum[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-      for (int s0 = 0; s0 < nsplit; s0 += 4) {
-        f32x4 v[4][8];
-        float w[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int su = min(s0 + u, nsplit - 1);
-          const float ls = load_coherent1(wl, (uint32_t)((lse_base + (size_t)su * kHpw) * 4));
-          w[u] = (s0 + u >= nsplit || ls == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(ls - Mu);
-          const uint32_t blk = (uint32_t)((unit_hg * p.P_max + su) * kBlock * 4) + lane_off;
-#pragma unroll
-          for (int m = 0; m < 8; ++m)
-            v[u][m] = load_coherent4(wo, blk + (uint32_t)((4 * (cb * 8 + m) + q4) * 64 * 16));
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-          for (int m = 0; m < 8; ++m) sum[m] += w[u] * v[u][m];
-      }
-      // slot (cb*8 + m, q4) element e is column 256cb + 8(8 q4 + 4g + e) + m
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        u32x4 o;
-#pragma unroll
-        for (int mm = 0; mm < 4; ++mm)
-          o[mm] = pack_bf16x2(sum[2 * mm][e] * zi, sum[2 * mm + 1][e] * zi);
-        *reinterpret_cast<u32x4*>(orow + 256 * cb + 8 * (8 * q4 + 4 * g + e)) = o;
-      }
-    }
-  if (p.lse && g == 0) p.lse[bh] = Z > 0.f ? (M + __log2f(Z)) * kLn2 : kNegInf;
-  if (tid == 0) *ticket = 0;
+    for (int mm = 0; mm < 4; ++mm)
+      o[mm] = pack_bf16x2(sum[2 * mm][e] * zi, sum[2 * mm + 1][e] * zi);
+    *reinterpret_cast<u32x4*>(orow + 256 * cb + 8 * (8 * q4 + 4 * g + e)) = o;
+  }
+  if (part == 0 && p.lse && g == 0) p.lse[bh] = Z > 0.f ? (M + __log2f(Z)) * kLn2 : kNegInf;
 }
 
 template <int NW>
@@ -499,6 +566,9 @@ static hipError_t launch_mla_t(const MlaParams& p, hipStream_t s) {
     attr_set = true;
   }
   hipLaunchKernelGGL(mla_kernel<NW>, dim3((unsigned)blocks), dim3(NW * 64), kMlaLds, s, p);
+  if (p.P_max > 1)
+    hipLaunchKernelGGL(mla_merge_kernel<NW>, dim3((unsigned)((size_t)p.B * groups * 8)),
+                       dim3(NW * 64), 0, s, p);
   return hipGetLastError();
 }
 
