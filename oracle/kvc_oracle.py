@@ -35,6 +35,12 @@ What it computes, and where the pages say so:
   per tensor (keys, values); a stored number is code value x scale, and a
   new row is quantised as x * (1 / scale) in float32, rounded to nearest
   even and saturated to +-448.
+* "890 bytes a token" (bemiagent), SWA bounded replay passage: with a
+  window W and a replayed segment starting at position s, a query at
+  position i attends to keys [max(s, i - W + 1), i].  For decode the query
+  is the newest position i = n - 1, so the keys are [max(s, n - W), n);
+  s = 0 when every position is present.  (The guide's "Keeping fewer
+  tokens" section describes the same bounded, most-recent window.)
 * Podcast transcript, decode walk-through: each new token attends to the
   cache plus its own new pair, and its key and value are appended.  The
   oracle appends first and then attends over [0, seq_len), which is the
@@ -162,6 +168,37 @@ def decode(q, k_cache, v_cache, seq_lens, scale: float):
         for j in range(n_kv):
             K = to_f64(k_cache[b, j, :n])
             V = to_f64(v_cache[b, j, :n])
+            for i in range(j * G, (j + 1) * G):
+                o[b, i], lse[b, i] = _attend(to_f64(q[b, i]), K, V, scale)
+    return o, lse
+
+
+# --------------------------------------------------------------------------
+# sliding-window decode (bounded replay's window rule)
+# --------------------------------------------------------------------------
+def window_range(n: int, window: int, start: int = 0):
+    """Positions the newest query (position n - 1) attends: [lo, n) with
+    lo = max(start, n - window), clamped to [0, n]."""
+    lo = min(max(start, n - window, 0), n)
+    return lo, n
+
+
+def decode_window(q, k_cache, v_cache, seq_lens, scale: float, window: int,
+                  win_start=None):
+    """decode() restricted to the window: head i of sequence b attends over
+    window_range(seq_lens[b], window, win_start[b]) (win_start None: 0)."""
+    assert window >= 1
+    B, n_h, d = q.shape
+    n_kv = k_cache.shape[1]
+    G = n_h // n_kv
+    o = np.zeros((B, n_h, v_cache.shape[3]))
+    lse = np.full((B, n_h), -math.inf)
+    for b in range(B):
+        st = 0 if win_start is None else int(win_start[b])
+        lo, n = window_range(int(seq_lens[b]), window, st)
+        for j in range(n_kv):
+            K = to_f64(k_cache[b, j, lo:n])
+            V = to_f64(v_cache[b, j, lo:n])
             for i in range(j * G, (j + 1) * G):
                 o[b, i], lse[b, i] = _attend(to_f64(q[b, i]), K, V, scale)
     return o, lse

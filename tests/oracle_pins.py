@@ -515,6 +515,70 @@ def pin_fp8_decode(orc):
     assert not k8[0, 0, [0, 1, 3]].any()
 
 
+# ---------------------------------------------------------- sliding window
+def _window_lo_from_page_rule(n, W, s):
+    """The page's rule for the query at position i = n - 1: keys from
+    max(s, i - W + 1) through i.  Written with i, as the page states it."""
+    i = n - 1
+    return min(max(s, i - W + 1, 0), n)
+
+
+def pin_window(orc):
+    """Bounded-replay window rule (DeepSeek article): brute force over the
+    page's [max(s, i - W + 1), i]; W >= n reduces to plain decode; W = 1
+    returns the newest value row; the window and the positions before it
+    merge (log-sum-exp) into the full decode; n_win = 128 attends exactly 128
+    positions (closed-form mean); an empty window gives zeros and -inf."""
+    g = golden()["swa_bounded_replay"]
+    assert g["layers"] * g["n_win"] == g["replay_tokens"]
+    rng = np.random.default_rng(21)
+    B, n_h, n_kv, d = 3, 4, 2, 8
+    lens = [1, 37, 90]
+    q, kc, vc, sl = _f64_case(rng, B, n_h, n_kv, d, lens, L_max=90)
+    for W, starts in ((1, None), (5, None), (33, [0, 10, 80]), (64, [0, 36, 0]), (200, None)):
+        o, lse = orc.decode_window(q, kc, vc, sl, 0.3, W, starts)
+        for b in range(B):
+            st = 0 if starts is None else starts[b]
+            lo = _window_lo_from_page_rule(lens[b], W, st)
+            for i in range(n_h):
+                j = i // (n_h // n_kv)
+                if lo == lens[b]:
+                    assert (o[b, i] == 0).all() and lse[b, i] == -math.inf
+                    continue
+                bo, bl = brute_attend(q[b, i], kc[b, j, lo:lens[b]], vc[b, j, lo:lens[b]], 0.3)
+                assert np.allclose(o[b, i], bo, rtol=1e-12, atol=1e-12), (W, b, i)
+                assert abs(lse[b, i] - bl) < 1e-12
+    ofull, lfull = orc.decode(q, kc, vc, sl, 0.3)
+    ow, lw = orc.decode_window(q, kc, vc, sl, 0.3, 10 ** 6)
+    np.testing.assert_allclose(ow, ofull, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lw, lfull, rtol=0, atol=1e-13)
+    o1, l1 = orc.decode_window(q, kc, vc, sl, 0.3, 1)
+    for b in range(B):
+        for i in range(n_h):
+            j = i // (n_h // n_kv)
+            np.testing.assert_allclose(o1[b, i], vc[b, j, lens[b] - 1], rtol=0, atol=1e-14)
+            s_last = 0.3 * math.fsum(float(x) * float(y) for x, y in zip(q[b, i], kc[b, j, lens[b] - 1]))
+            assert abs(l1[b, i] - s_last) < 1e-12
+    # window W plus the positions before it = everything (merge by lse)
+    W = 20
+    ow, lw = orc.decode_window(q, kc, vc, sl, 0.3, W)
+    n = lens[2]
+    oh, lh = orc.decode(q[2:3], kc[2:3], vc[2:3], np.array([n - W], np.int32), 0.3)
+    for i in range(n_h):
+        mo, ml = orc.merge_partials([oh[0, i], ow[2, i]], [lh[0, i], lw[2, i]])
+        np.testing.assert_allclose(mo, ofull[2, i], rtol=0, atol=1e-12)
+        assert abs(ml - lfull[2, i]) < 1e-12
+    # the page's window of 128: q = 0 weighs every attended position equally,
+    # and V[t] = t averages to the middle of [n - 128, n)
+    n = 300
+    qz = np.zeros((1, 2, 4), np.float32)
+    kz = rng.standard_normal((1, 1, n, 4)).astype(np.float32)
+    vt = np.repeat(np.arange(n, dtype=np.float32)[None, None, :, None], 4, axis=3)
+    o, lse = orc.decode_window(qz, kz, vt, np.array([n], np.int32), 0.5, g["n_win"])
+    np.testing.assert_allclose(o, (2 * n - g["n_win"] - 1) / 2, rtol=0, atol=1e-9)
+    np.testing.assert_allclose(lse, math.log(g["n_win"]), rtol=0, atol=1e-12)
+
+
 ALL_PINS = [
     pin_size_llama2, pin_size_matches_storage, pin_causal_equals_recompute,
     pin_full_causal_bruteforce, pin_decode_bruteforce, pin_single_position,
@@ -523,5 +587,5 @@ ALL_PINS = [
     pin_split_merge, pin_gqa_head_mapping, pin_mla_reduces_to_dense,
     pin_mla_rope_matters, pin_topk, pin_append, pin_bf16_decoding,
     pin_fp8_page_max, pin_fp8_codes, pin_fp8_roundtrip, pin_fp8_rounding,
-    pin_fp8_quantize_scale, pin_fp8_decode,
+    pin_fp8_quantize_scale, pin_fp8_decode, pin_window,
 ]

@@ -230,6 +230,36 @@ def mutants():
         return K.decode_fp8(q, kc, vc, sl, scale, ks, 1.0)
     m.decode_fp8 = decode_fp8_no_vscale
     out["fp8_decode_ignores_value_scale"] = m
+
+    # sliding window
+    def window_variant(lo_of):
+        def decode_window(q, kc, vc, sl, scale, window, win_start=None):
+            B, n_h, d = q.shape
+            n_kv = kc.shape[1]
+            G = n_h // n_kv
+            o = np.zeros((B, n_h, vc.shape[3]))
+            lse = np.full((B, n_h), -math.inf)
+            for b in range(B):
+                n = int(sl[b])
+                st = 0 if win_start is None else int(win_start[b])
+                lo = min(max(lo_of(n, window, st), 0), n)
+                hi = n if lo_of is not _front else min(window, n)
+                for i in range(n_h):
+                    j = i // G
+                    o[b, i], lse[b, i] = K._attend(K.to_f64(q[b, i]), K.to_f64(kc[b, j, lo:hi]),
+                                                   K.to_f64(vc[b, j, lo:hi]), scale)
+            return o, lse
+        return decode_window
+
+    def _front(n, W, st):
+        return 0
+    for name, lo_of in (("window_one_short", lambda n, W, st: max(st, n - W + 1)),
+                        ("window_one_long", lambda n, W, st: max(st, n - W - 1)),
+                        ("window_ignores_start", lambda n, W, st: n - W),
+                        ("window_from_front", _front)):
+        m = _copy()
+        m.decode_window = window_variant(lo_of)
+        out[name] = m
     return out
 
 
