@@ -16,7 +16,8 @@ GB/s over the algorithmic bytes of a step (cache read + q read + out write +
 new k/v read and written + lengths).  `roofline` is the dense decode kernel
 alone, timed with HIP events over back-to-back launches of one step's
 layers.  `also` carries the same figures for the GQA, MLA and top-k
-workloads, and for the GQA workload over FP8 E4M3 caches (C3F8).  `cpu_baseline` is the fp64 oracle on the same inputs (copied to
+workloads, for the GQA workload over FP8 E4M3 caches (C3F8) and for the GQA
+workload attending a sliding window of its newest 128 positions (C3W128).  `cpu_baseline` is the fp64 oracle on the same inputs (copied to
 the host), on a time-bounded sample of layer-steps.
 """
 from __future__ import annotations
@@ -45,8 +46,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="C2", choices=["C2", "C3", "C4", "C5", "C3F8"])
-    ap.add_argument("--others", default="C3,C4,C5,C3F8",
+    ap.add_argument("--config", default="C2", choices=["C2", "C3", "C4", "C5", "C3F8", "C3W128"])
+    ap.add_argument("--others", default="C3,C4,C5,C3F8,C3W128",
                     help="also-measured workloads (comma list; 'none' for none)")
     ap.add_argument("--kernel-reps", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true")
@@ -367,9 +368,58 @@ class Fp8DenseWorkload:
                 f"{self.layers} layers ({self.nbuf} distinct cache buffers), bf16 q/out")
 
 
+class WindowWorkload(DenseWorkload):
+    """The GQA layers of C3 attending only the newest WINDOW positions (the
+    DeepSeek article's n_win = 128).  A layer-step is kvc_append then
+    kvc_decode_attn_window."""
+
+    kernel = "dense_mfma_kernel<false, false, false> (window 128)"
+    kernel_appends = False
+    WINDOW = 128
+
+    def __init__(self, cfg, slack, torch, kvc):
+        super().__init__(cfg, slack, torch, kvc)
+        self.ws_win = kvc.workspace(kvc.kvc_decode_attn_window_workspace_size(
+            cfg.B, cfg.n_h, cfg.n_kv, self.L_max, cfg.d, kvc.KVC_BF16, self.WINDOW))
+
+    def step(self):
+        for l in range(self.layers):
+            b = l % self.nbuf
+            self.kvc.kvc_append(self.K[b], self.V[b], self.sl[l], self.kn[l], self.vn[l])
+            self.kvc.kvc_decode_attn_window(self.q[l], self.K[b], self.V[b], self.sl[l],
+                                            self.out[l], self.WINDOW, scale=self.cfg.scale,
+                                            workspace=self.ws_win)
+
+    def decode_only(self):
+        for l in range(self.layers):
+            b = l % self.nbuf
+            self.kvc.kvc_decode_attn_window(self.q[l], self.K[b], self.V[b], self.sl[l],
+                                            self.out[l], self.WINDOW, scale=self.cfg.scale,
+                                            workspace=self.ws_win)
+
+    def kernel_only(self):
+        self.decode_only()
+
+    def kernel_bytes(self, n):
+        c = self.cfg
+        return int(2 * c.n_kv * c.d * 2 * np.minimum(n, self.WINDOW).sum()
+                   + c.B * c.n_h * c.d * (2 + 2) + 4 * c.B)
+
+    def launch_bytes(self, steps_done):
+        return self.kernel_bytes(self.lens_after(steps_done - 1))
+
+    def step_bytes(self, steps_done):
+        c = self.cfg
+        per_layer = self.kernel_bytes(self.lens_after(steps_done)) + 4 * c.B * c.n_kv * c.d * 2 + 8 * c.B
+        return per_layer * self.layers
+
+    def describe(self):
+        return super().describe().replace(", seq_lens", f", window {self.WINDOW} of seq_lens")
+
+
 WORKLOADS = {"C2": (syn.C2, DenseWorkload), "C3": (syn.C3, DenseWorkload),
              "C4": (syn.C4, MlaWorkload), "C5": (syn.C5, TopKWorkload),
-             "C3F8": (syn.C3, Fp8DenseWorkload)}
+             "C3F8": (syn.C3, Fp8DenseWorkload), "C3W128": (syn.C3, WindowWorkload)}
 
 
 # ---------------------------------------------------------------- timing

@@ -149,6 +149,31 @@ int kvc_append_decode_attn(const void* q, void* k_cache, void* v_cache,
                            void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * kvc_decode_attn_window - kvc_decode_attn over a sliding window of the
+ * newest positions.  ("890 bytes a token", SWA bounded replay passage: for a
+ * replay starting at position s, the query at position i attends to keys
+ * [max(s, i - W + 1), i]; guide, "Keeping fewer tokens".)
+ *
+ * For each b with n = seq_lens[b] (the newest query is position n - 1):
+ *     lo = clamp(max(s_b, n - window), 0, n), s_b = win_start[b] or 0,
+ * and every head attends over [lo, n) exactly as kvc_decode_attn does over
+ * [0, n).  Positions below lo are never read.  lo == n gives a zero row and
+ * lse = -inf.
+ *   window      >= 1, else KVC_ERR_BAD_ARG.
+ *   win_start   [B] int32 device array or NULL (all 0).
+ *   Other arguments, dtypes, shapes and workspace rules as kvc_decode_attn
+ *   (the workspace query takes the window: a window shorter than L_max needs
+ *   less).
+ */
+size_t kvc_decode_attn_window_workspace_size(int B, int n_h, int n_kv, int L_max,
+                                             int d, int dtype, int window);
+int kvc_decode_attn_window(const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* seq_lens, const int32_t* win_start,
+                           int window, void* out, float* lse, int B, int n_h,
+                           int n_kv, int L_max, int d, float scale, int dtype,
+                           void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * FP8 E4M3 cache (guide, "Fewer bits per number": the byte width b is a plain
  * multiplier of the cache size, and fp8 is the usual serving default; podcast
  * transcript, KV quantization passage).  Each cached number is one byte, an

@@ -68,6 +68,9 @@ def lib() -> ctypes.CDLL:
         "kvc_decode_attn_topk_workspace_size": (_Z, [_I, _I, _I, _I, _I, _I]),
         "kvc_decode_attn_topk": (_I, [_P, _P, _P, _P, _P, _I, _P, _P, _I, _I,
                                       _I, _I, _I, _F, _I, _P, _P, _Z, _P]),
+        "kvc_decode_attn_window_workspace_size": (_Z, [_I, _I, _I, _I, _I, _I, _I]),
+        "kvc_decode_attn_window": (_I, [_P, _P, _P, _P, _P, _I, _P, _P, _I, _I, _I, _I, _I,
+                                        _F, _I, _P, _Z, _P]),
         "kvc_append_fp8": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _F, _P, _P]),
         "kvc_decode_attn_fp8_workspace_size": (_Z, [_I, _I, _I, _I, _I]),
         "kvc_decode_attn_fp8": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
@@ -241,6 +244,25 @@ def kvc_decode_attn_topk(q, k_cache, v_cache, seq_lens, idx, out, lse=None,
                                     _dtype_code(q), _ptr(flag), wp, wn,
                                     _stream(stream))
     _check(st, "kvc_decode_attn_topk")
+
+
+def kvc_decode_attn_window_workspace_size(B, n_h, n_kv, L_max, d, dtype, window) -> int:
+    return lib().kvc_decode_attn_window_workspace_size(B, n_h, n_kv, L_max, d, dtype, window)
+
+
+def kvc_decode_attn_window(q, k_cache, v_cache, seq_lens, out, window, win_start=None,
+                           lse=None, scale=None, workspace=None, stream=None):
+    """Dense decode over the newest `window` positions (from win_start[b] at
+    the earliest); shapes as kvc_decode_attn."""
+    B, n_h, d = q.shape
+    _, n_kv, L_max, _ = k_cache.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    wp, wn = _ws(workspace)
+    st = lib().kvc_decode_attn_window(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens),
+                                      _ptr(win_start), window, _ptr(out), _ptr(lse), B, n_h,
+                                      n_kv, L_max, d, scale, _dtype_code(q), wp, wn,
+                                      _stream(stream))
+    _check(st, "kvc_decode_attn_window")
 
 
 def _need_u8(t, what):

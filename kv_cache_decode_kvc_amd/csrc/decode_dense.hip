@@ -495,7 +495,8 @@ __global__ __launch_bounds__(256, 2) void dense_mfma_kernel(DenseParams p) {
   decode_unit(p, b, j, split);
   LengthState ls;
   const int n = attended_length<APPEND, 128, uint16_t, false>(p, b, j, split, ls);
-  const int count = TOPK ? p.K : n;
+  const int lo = TOPK ? 0 : window_low(p, b, n);    // window mode only (not fused)
+  const int count = TOPK ? p.K : n - lo;
   const int S = dense_split_size(count, p.S, p.P_max, p.even);
   const int nsplit = dense_num_splits(count, S);
   if (split >= nsplit || count == 0) {
@@ -505,6 +506,8 @@ __global__ __launch_bounds__(256, 2) void dense_mfma_kernel(DenseParams p) {
   }
   int start, end;
   dense_split_range(count, S, split, start, end);
+  start += lo;
+  end += lo;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -662,7 +665,8 @@ __global__ __launch_bounds__(256) void dense_generic_kernel(DenseParams p) {
   decode_unit(p, b, j, split);
   LengthState ls;
   const int n = attended_length<APPEND, D, T>(p, b, j, split, ls);
-  const int count = TOPK ? p.K : n;
+  const int lo = TOPK ? 0 : window_low(p, b, n);    // window mode only (not fused)
+  const int count = TOPK ? p.K : n - lo;
   const int S = dense_split_size(count, p.S, p.P_max, p.even);
   const int nsplit = dense_num_splits(count, S);
   if (split >= nsplit || count == 0) {
@@ -672,6 +676,8 @@ __global__ __launch_bounds__(256) void dense_generic_kernel(DenseParams p) {
   }
   int start, end;
   dense_split_range(count, S, split, start, end);
+  start += lo;
+  end += lo;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = p.G;
 

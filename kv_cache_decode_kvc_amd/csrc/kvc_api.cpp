@@ -100,8 +100,11 @@ struct DenseCheck {
   WsLayout ws;
 };
 
+// window > 0: at most `window` positions are attended, which is what the
+// split plan and the workspace are sized for.
 DenseCheck check_dense_shape(int B, int n_h, int n_kv, int L_max, int d,
-                             int dtype, int K, bool topk, bool fused = false) {
+                             int dtype, int K, bool topk, bool fused = false,
+                             int window = 0) {
   DenseCheck c{KVC_OK, 0, 1, 0, {}};
   if (!good_dtype(dtype)) { c.status = KVC_ERR_BAD_DTYPE; return c; }
   if (B < 0 || n_h < 1 || n_kv < 1 || L_max < 1 || d < 1) {
@@ -115,7 +118,7 @@ DenseCheck check_dense_shape(int B, int n_h, int n_kv, int L_max, int d,
   if (d != 64 && d != 128) { c.status = KVC_ERR_UNSUPPORTED; return c; }
   if (n_h / n_kv > kMaxGroup) { c.status = KVC_ERR_UNSUPPORTED; return c; }
   const int64_t units = (int64_t)B * n_kv;
-  const int64_t n_max = topk ? K : L_max;
+  const int64_t n_max = topk ? K : (window > 0 && window < L_max ? window : L_max);
   const SplitPlan plan = plan_splits(topk ? KVC_KIND_TOPK : KVC_KIND_DENSE, units, n_max);
   c.S = plan.S;
   c.P_max = plan.P;
@@ -270,10 +273,11 @@ static int dense_common(const void* q, const void* k_cache, const void* v_cache,
                         void* workspace, size_t ws_bytes, void* stream,
                         bool topk, const void* k_new = nullptr,
                         const void* v_new = nullptr, bool fused = false,
-                        bool fp8 = false, float k_scale = 1.f, float v_scale = 1.f) {
+                        bool fp8 = false, float k_scale = 1.f, float v_scale = 1.f,
+                        int window = 0, const int32_t* win_start = nullptr) {
   // FP8 caches: q and out are bf16; the shape rules are those of bf16 with
   // d = 128 (checked by the caller).
-  const DenseCheck c = check_dense_shape(B, n_h, n_kv, L_max, d, dtype, K, topk, fused);
+  const DenseCheck c = check_dense_shape(B, n_h, n_kv, L_max, d, dtype, K, topk, fused, window);
   if (c.status != KVC_OK) return c.status;
   if (!isfinite(scale)) return KVC_ERR_BAD_ARG;
   if (fp8 && !(isfinite(k_scale) && isfinite(v_scale) && k_scale > 0.f && v_scale > 0.f))
@@ -284,7 +288,8 @@ static int dense_common(const void* q, const void* k_cache, const void* v_cache,
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
       !aligned(out, 16) || !aligned(seq_lens, 4) || (lse && !aligned(lse, 4)) ||
       (idx && !aligned(idx, 16)) || (flag && !aligned(flag, 4)) ||
-      (fused && (!aligned(k_new, 16) || !aligned(v_new, 16))))
+      (fused && (!aligned(k_new, 16) || !aligned(v_new, 16))) ||
+      (win_start && !aligned(win_start, 4)))
     return KVC_ERR_MISALIGNED;
   if (B == 0) return KVC_OK;
   const int ws_status = check_workspace(c.ws, workspace, ws_bytes);
@@ -304,6 +309,8 @@ static int dense_common(const void* q, const void* k_cache, const void* v_cache,
   p.d = d; p.K = topk ? K : 0; p.S = c.S; p.P_max = (int)c.P_max; p.even = c.even;
   p.scale_log2 = scale * 1.4426950408889634f;
   p.out_scale = 1.f;
+  p.window = window;
+  p.win_start = window > 0 ? win_start : nullptr;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (fp8) {
     p.scale_log2 *= k_scale;
@@ -349,6 +356,25 @@ int kvc_decode_attn_topk(const void* q, const void* k_cache,
   return dense_common(q, k_cache, v_cache, seq_lens, idx, K, out, lse, B, n_h,
                       n_kv, L_max, d, scale, dtype, flag, workspace, ws_bytes,
                       stream, true);
+}
+
+size_t kvc_decode_attn_window_workspace_size(int B, int n_h, int n_kv, int L_max,
+                                             int d, int dtype, int window) {
+  if (window < 1) return 0;
+  const DenseCheck c = check_dense_shape(B, n_h, n_kv, L_max, d, dtype, 0, false, false, window);
+  return c.status == KVC_OK ? c.ws.total : 0;
+}
+
+int kvc_decode_attn_window(const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* seq_lens, const int32_t* win_start,
+                           int window, void* out, float* lse, int B, int n_h,
+                           int n_kv, int L_max, int d, float scale, int dtype,
+                           void* workspace, size_t ws_bytes, void* stream) {
+  if (window < 1) return KVC_ERR_BAD_ARG;
+  return dense_common(q, k_cache, v_cache, seq_lens, nullptr, 0, out, lse, B,
+                      n_h, n_kv, L_max, d, scale, dtype, nullptr, workspace,
+                      ws_bytes, stream, false, nullptr, nullptr, false, false,
+                      1.f, 1.f, window, win_start);
 }
 
 size_t kvc_decode_attn_fp8_workspace_size(int B, int n_h, int n_kv, int L_max,

@@ -66,6 +66,8 @@ struct DenseParams {
   int even;               // 1: spread each sequence over the P_max splits
   float scale_log2;       // scale * log2(e) (times the key scale for FP8 caches)
   float out_scale;        // multiplies the output (the value scale for FP8 caches)
+  int window;             // > 0: attend only the newest `window` positions
+  const int32_t* win_start;  // window mode, may be null: first present position per sequence
 };
 
 struct MlaParams {
@@ -99,6 +101,14 @@ __host__ __device__ inline int dense_split_size(int n, int S, int P, int even) {
   int Sn = (n + P - 1) / P;
   Sn = (Sn + 31) / 32 * 32;
   return Sn > S ? Sn : S;
+}
+// Sliding window: the newest query (position n - 1) attends keys from
+// max(s, n - window) (bounded-replay rule, s = first present position).
+__device__ inline int window_low(const DenseParams& p, int b, int n) {
+  if (p.window <= 0) return 0;
+  int lo = n - p.window;
+  if (p.win_start) lo = max(lo, p.win_start[b]);
+  return min(max(lo, 0), n);
 }
 __host__ __device__ inline void dense_split_range(int n, int S, int split, int& start, int& end) {
   start = split * S;

@@ -31,6 +31,7 @@ DOMINANT = {
     "C4": "mla_kernel",
     "C5": "dense_mfma_kernel<true, false, false>",
     "C3F8": "dense_mfma_kernel<false, false, true>",
+    "C3W128": "dense_mfma_kernel<false, false, false>",
 }
 
 

@@ -222,3 +222,27 @@ def test_fp8_validation(L):
     assert L.kvc_decode_attn_fp8_workspace_size(32, 64, 8, 32768, 128) == \
         L.kvc_decode_attn_workspace_size(32, 64, 8, 32768, 128, kvc.KVC_BF16)
     assert L.kvc_decode_attn_fp8_workspace_size(32, 64, 8, 32768, 64) == 0
+
+
+def test_window_validation(L):
+    def wd(**kw):
+        a = dict(q=A16, k=A16, v=A16, sl=A4, st=NULL, W=128, out=A16, lse=NULL, B=2, n_h=8,
+                 n_kv=2, L_max=4096, d=128, scale=0.1, dt=kvc.KVC_BF16, ws=A16,
+                 wsb=1 << 30, stream=NULL)
+        a.update(kw)
+        return L.kvc_decode_attn_window(a["q"], a["k"], a["v"], a["sl"], a["st"], a["W"],
+                                        a["out"], a["lse"], a["B"], a["n_h"], a["n_kv"],
+                                        a["L_max"], a["d"], a["scale"], a["dt"], a["ws"],
+                                        a["wsb"], a["stream"])
+    assert wd(W=0) == -8
+    assert wd(W=-3) == -8
+    assert wd(st=ctypes.c_void_p(0x10002)) == -6
+    assert wd(k=NULL) == -1
+    assert wd(n_h=7) == -2
+    assert wd(B=0) == 0
+    full = L.kvc_decode_attn_workspace_size(32, 64, 8, 32768, 128, kvc.KVC_BF16)
+    win = L.kvc_decode_attn_window_workspace_size(32, 64, 8, 32768, 128, kvc.KVC_BF16, 128)
+    assert 0 <= win <= full
+    assert L.kvc_decode_attn_window_workspace_size(32, 64, 8, 32768, 128, kvc.KVC_BF16, 0) == 0
+    assert L.kvc_decode_attn_window_workspace_size(1, 8, 2, 64, 128, kvc.KVC_BF16, 10 ** 6) == \
+        L.kvc_decode_attn_workspace_size(1, 8, 2, 64, 128, kvc.KVC_BF16)

@@ -204,3 +204,36 @@ def test_fullsize_topk_layer():
         assert f_ref == 0
         compare(oracle.to_f64(bits(out[b, j * G:(j + 1) * G])), o_ref[0], 2e-2, f"topk b={b} j={j}")
         compare_lse(host(lse[b, j * G:(j + 1) * G]), l_ref[0], 4e-3)
+
+
+def test_fullsize_gqa_layer_window():
+    """The GQA layer attending its newest 128 positions (append, then the
+    window decode), as the benchmark's window workload runs it."""
+    c = syn.C3
+    W = 128
+    pre = syn.pre_append_lens(c)
+    L_max = int(max(c.L_max, pre.max() + 1))
+    K = normal((c.B, c.n_kv, L_max, c.d), c.cfg_id, 0, "k")
+    V = normal((c.B, c.n_kv, L_max, c.d), c.cfg_id, 0, "v")
+    q = normal((c.B, c.n_h, c.d), c.cfg_id, 0, "q")
+    kn = normal((c.B, c.n_kv, c.d), c.cfg_id, 0, "k_new")
+    vn = normal((c.B, c.n_kv, c.d), c.cfg_id, 0, "v_new")
+    sl = torch.tensor(pre, dtype=torch.int32, device="cuda")
+    out = torch.empty_like(q)
+    lse = torch.empty(c.B, c.n_h, dtype=torch.float32, device="cuda")
+    ws = kvc.workspace(kvc.kvc_decode_attn_window_workspace_size(c.B, c.n_h, c.n_kv, L_max, c.d,
+                                                                 kvc.KVC_BF16, W))
+    kvc.kvc_append(K, V, sl, kn, vn)
+    kvc.kvc_decode_attn_window(q, K, V, sl, out, W, lse=lse, scale=c.scale, workspace=ws)
+    torch.cuda.synchronize()
+    assert host(sl).tolist() == (pre + 1).tolist()
+    G = c.n_h // c.n_kv
+    for b, j in sample_units(pre, c.n_kv, 4, 35):
+        n = int(pre[b]) + 1
+        lo = n - W
+        o_ref, l_ref = oracle.decode_window(bits(q[b, j * G:(j + 1) * G])[None],
+                                            bits(K[b, j, lo:n])[None, None],
+                                            bits(V[b, j, lo:n])[None, None],
+                                            np.array([W], np.int32), c.scale, W)
+        compare(oracle.to_f64(bits(out[b, j * G:(j + 1) * G])), o_ref[0], 2e-2, f"window b={b} j={j}")
+        compare_lse(host(lse[b, j * G:(j + 1) * G]), l_ref[0], 4e-3)
