@@ -35,6 +35,14 @@ What it computes, and where the pages say so:
   per tensor (keys, values); a stored number is code value x scale, and a
   new row is quantised as x * (1 / scale) in float32, rounded to nearest
   even and saturated to +-448.
+* "KV cache" guide, "The allocator, not the algorithm": instead of one
+  contiguous reservation per sequence at its maximum length, the cache is
+  cut into fixed-size blocks of beta positions held in a shared pool, and a
+  per-sequence block table maps logical block k (positions [k*beta,
+  (k+1)*beta)) to a physical block; each sequence then wastes at most
+  beta - 1 slots.  Reading (the pages give no layout): a pool is
+  [num_blocks, n_kv, beta, d]; a block-table entry outside [0, num_blocks)
+  is invalid.
 * "890 bytes a token" (bemiagent), SWA bounded replay passage: with a
   window W and a replayed segment starting at position s, a query at
   position i attends to keys [max(s, i - W + 1), i].  For decode the query
@@ -171,6 +179,81 @@ def decode(q, k_cache, v_cache, seq_lens, scale: float):
             for i in range(j * G, (j + 1) * G):
                 o[b, i], lse[b, i] = _attend(to_f64(q[b, i]), K, V, scale)
     return o, lse
+
+
+# --------------------------------------------------------------------------
+# paged cache (guide "The allocator, not the algorithm")
+# --------------------------------------------------------------------------
+def paged_waste_fraction(lengths, beta: int) -> float:
+    """Slots held but unused over slots used, when each sequence holds
+    ceil(n / beta) blocks of beta slots."""
+    held = sum(-(-int(n) // beta) * beta for n in lengths)
+    used = sum(int(n) for n in lengths)
+    return (held - used) / used
+
+
+def paged_rows(pool, block_table, b: int, j: int, n: int, beta: int):
+    """Rows [0, n) of (sequence b, KV head j) gathered through the block
+    table, plus the list of positions whose block is invalid (skipped)."""
+    rows, bad = [], []
+    num_blocks = pool.shape[0]
+    for t in range(n):
+        blk = int(block_table[b, t // beta])
+        if 0 <= blk < num_blocks:
+            rows.append(pool[blk, j, t % beta])
+        else:
+            bad.append(t)
+    shape = (len(rows),) + pool.shape[3:]
+    return (np.stack(rows) if rows else np.zeros(shape, dtype=pool.dtype)), bad
+
+
+def append_paged(k_pool, v_pool, block_table, seq_lens, k_new, v_new) -> int:
+    """append() into a paged cache: slot n = seq_lens[b] lives in block
+    block_table[b, n // beta] at offset n % beta.  A full table (n at or past
+    max_blocks * beta) sets flag bit 0; an invalid block at the slot sets
+    flag bit 1; either way nothing is written and the length stays."""
+    beta = k_pool.shape[2]
+    max_blocks = block_table.shape[1]
+    flag = 0
+    for b in range(seq_lens.shape[0]):
+        n = int(seq_lens[b])
+        if n < 0 or n >= max_blocks * beta:
+            flag |= FLAG_CACHE_FULL
+            continue
+        blk = int(block_table[b, n // beta])
+        if not 0 <= blk < k_pool.shape[0]:
+            flag |= FLAG_BAD_INDEX
+            continue
+        k_pool[blk, :, n % beta] = k_new[b]
+        v_pool[blk, :, n % beta] = v_new[b]
+        seq_lens[b] = n + 1
+    return flag
+
+
+def decode_paged(q, k_pool, v_pool, block_table, seq_lens, scale: float):
+    """decode() over a paged cache: head i of sequence b attends over the
+    positions [0, seq_lens[b]) gathered through the block table; positions
+    in an invalid block are skipped and set flag bit 1.
+    Returns (o, lse, flag)."""
+    B, n_h, d = q.shape
+    n_kv = k_pool.shape[1]
+    beta = k_pool.shape[2]
+    G = n_h // n_kv
+    o = np.zeros((B, n_h, v_pool.shape[3]))
+    lse = np.full((B, n_h), -math.inf)
+    flag = 0
+    for b in range(B):
+        n = min(max(int(seq_lens[b]), 0), block_table.shape[1] * beta)
+        for j in range(n_kv):
+            Kr, bad = paged_rows(k_pool, block_table, b, j, n, beta)
+            Vr, _ = paged_rows(v_pool, block_table, b, j, n, beta)
+            if bad:
+                flag |= FLAG_BAD_INDEX
+            K = to_f64(Kr)
+            V = to_f64(Vr)
+            for i in range(j * G, (j + 1) * G):
+                o[b, i], lse[b, i] = _attend(to_f64(q[b, i]), K, V, scale)
+    return o, lse, flag
 
 
 # --------------------------------------------------------------------------

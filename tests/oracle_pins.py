@@ -579,6 +579,95 @@ def pin_window(orc):
     np.testing.assert_allclose(lse, math.log(g["n_win"]), rtol=0, atol=1e-12)
 
 
+# ------------------------------------------------------------------ paging
+def _to_pool(cache, beta, perm_rng=None, extra_blocks=0):
+    """Lay a contiguous [B, n_kv, L, d] cache out as a pool [num_blocks,
+    n_kv, beta, d] plus a block table, with explicit loops (physical block
+    order shuffled when perm_rng is given)."""
+    B, n_kv, L, d = cache.shape
+    mb = L // beta
+    nblk = B * mb + extra_blocks
+    order = list(range(nblk))
+    if perm_rng is not None:
+        perm_rng.shuffle(order)
+    pool = np.zeros((nblk, n_kv, beta, d), dtype=cache.dtype)
+    table = np.full((B, mb), -1, dtype=np.int32)
+    for b in range(B):
+        for k in range(mb):
+            phys = order[b * mb + k]
+            table[b, k] = phys
+            for j in range(n_kv):
+                for o in range(beta):
+                    pool[phys, j, o] = cache[b, j, k * beta + o]
+    return pool, table
+
+
+def pin_paged(orc):
+    """Guide, 'The allocator, not the algorithm': a sequence wastes at most
+    beta - 1 slots, under 3% at beta = 16 and mean length 512; decoding
+    through a block table (any physical order, shared prefix blocks) equals
+    decoding the contiguous cache; append writes exactly slot n of the
+    mapped block; invalid blocks are skipped and flagged."""
+    g = golden()["paged_waste_bound"]
+    beta, mean = g["beta"], g["mean_len"]
+    worst = [mean - beta + 1 + beta * k for k in (-2, -1, 0, 1, 2)]      # each wastes beta - 1
+    assert sum(worst) / len(worst) == mean - beta + 1
+    assert orc.paged_waste_fraction(worst, beta) == (beta - 1) / (mean - beta + 1)
+    assert orc.paged_waste_fraction([mean + 1] * 7, beta) < g["bound_below"]
+    assert orc.paged_waste_fraction([beta * 3] * 4, beta) == 0.0
+
+    rng = np.random.default_rng(31)
+    B, n_h, n_kv, d, beta, L = 3, 8, 2, 8, 4, 32
+    lens = [0, 13, 32]
+    q, kc, vc, sl = _f64_case(rng, B, n_h, n_kv, d, lens, L_max=L)
+    o_ref, l_ref = orc.decode(q, kc, vc, sl, 0.45)
+    for prng in (None, np.random.default_rng(5)):
+        kp, table = _to_pool(kc, beta, prng, extra_blocks=3)
+        vp, table2 = _to_pool(vc, beta, None if prng is None else np.random.default_rng(5), 3)
+        assert np.array_equal(table, table2)
+        o, lse, flag = orc.decode_paged(q, kp, vp, table, sl, 0.45)
+        assert flag == 0
+        np.testing.assert_allclose(o, o_ref, rtol=0, atol=1e-13)
+        np.testing.assert_allclose(lse, l_ref, rtol=0, atol=1e-13)
+    # shared prefix: sequence 1 points its first two blocks at sequence 2's
+    kp, table = _to_pool(kc, beta)
+    vp, _ = _to_pool(vc, beta)
+    kc2, vc2 = kc.copy(), vc.copy()
+    kc2[1, :, :2 * beta] = kc[2, :, :2 * beta]
+    vc2[1, :, :2 * beta] = vc[2, :, :2 * beta]
+    t2 = table.copy()
+    t2[1, :2] = table[2, :2]
+    o_sh, l_sh, _ = orc.decode_paged(q, kp, vp, t2, sl, 0.45)
+    o_cp, l_cp = orc.decode(q, kc2, vc2, sl, 0.45)
+    np.testing.assert_allclose(o_sh, o_cp, rtol=0, atol=1e-13)
+    # an invalid block: its positions are skipped (brute force) and flagged
+    t3 = table.copy()
+    t3[2, 1] = kp.shape[0] + 7
+    o3, l3, f3 = orc.decode_paged(q, kp, vp, t3, sl, 0.45)
+    assert f3 == orc.FLAG_BAD_INDEX
+    keep = [t for t in range(lens[2]) if t // beta != 1]
+    for i in range(n_h):
+        j = i // (n_h // n_kv)
+        bo, bl = brute_attend(q[2, i], kc[2, j, keep], vc[2, j, keep], 0.45)
+        assert np.allclose(o3[2, i], bo, rtol=1e-12, atol=1e-12)
+        assert abs(l3[2, i] - bl) < 1e-12
+    np.testing.assert_allclose(o3[:2], o_ref[:2], rtol=0, atol=1e-13)
+    # append: exactly slot n of its block; full table and invalid block flagged
+    kp = np.zeros((6, 2, 4, 3), np.float32)
+    vp = np.zeros((6, 2, 4, 3), np.float32)
+    table = np.array([[4, 1], [0, 5], [2, 77]], np.int32)
+    sl = np.array([5, 8, 4], np.int32)          # b0: block 1 slot 1; b1: full; b2: block 77
+    kn = np.arange(18, dtype=np.float32).reshape(3, 2, 3) + 1
+    vn = -kn
+    f = orc.append_paged(kp, vp, table, sl, kn, vn)
+    assert f == orc.FLAG_CACHE_FULL | orc.FLAG_BAD_INDEX
+    assert sl.tolist() == [6, 8, 4]
+    assert np.array_equal(kp[1, :, 1], kn[0]) and np.array_equal(vp[1, :, 1], vn[0])
+    kp[1, :, 1] = 0
+    vp[1, :, 1] = 0
+    assert not kp.any() and not vp.any()
+
+
 ALL_PINS = [
     pin_size_llama2, pin_size_matches_storage, pin_causal_equals_recompute,
     pin_full_causal_bruteforce, pin_decode_bruteforce, pin_single_position,
@@ -587,5 +676,5 @@ ALL_PINS = [
     pin_split_merge, pin_gqa_head_mapping, pin_mla_reduces_to_dense,
     pin_mla_rope_matters, pin_topk, pin_append, pin_bf16_decoding,
     pin_fp8_page_max, pin_fp8_codes, pin_fp8_roundtrip, pin_fp8_rounding,
-    pin_fp8_quantize_scale, pin_fp8_decode, pin_window,
+    pin_fp8_quantize_scale, pin_fp8_decode, pin_window, pin_paged,
 ]

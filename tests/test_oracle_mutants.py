@@ -260,6 +260,65 @@ def mutants():
         m = _copy()
         m.decode_window = window_variant(lo_of)
         out[name] = m
+
+    # paging
+    def rows_variant(kind):
+        def paged_rows(pool, table, b, j, n, beta):
+            rows, bad = [], []
+            for t in range(n):
+                k = t // beta if kind != "next_block" else (t + 1) // beta
+                k = min(k, table.shape[1] - 1)
+                blk = int(table[b, k]) if kind != "no_table" else b * table.shape[1] + t // beta
+                if not 0 <= blk < pool.shape[0]:
+                    bad.append(t)
+                    continue
+                off = t % beta if kind != "offset_swapped" else (t // beta) % beta
+                rows.append(pool[blk, j, off])
+            shape = (len(rows),) + pool.shape[3:]
+            return (np.stack(rows) if rows else np.zeros(shape, dtype=pool.dtype)), bad
+        return paged_rows
+    for kind in ("next_block", "no_table", "offset_swapped"):
+        m = _copy()
+        m.paged_rows = rows_variant(kind)
+
+        def decode_paged(q, kp, vp, table, sl, scale, _m=m):
+            B, n_h, d = q.shape
+            n_kv, beta = kp.shape[1], kp.shape[2]
+            G = n_h // n_kv
+            o = np.zeros((B, n_h, vp.shape[3]))
+            lse = np.full((B, n_h), -math.inf)
+            flag = 0
+            for b in range(B):
+                n = min(max(int(sl[b]), 0), table.shape[1] * beta)
+                for j in range(n_kv):
+                    Kr, bad = _m.paged_rows(kp, table, b, j, n, beta)
+                    Vr, _ = _m.paged_rows(vp, table, b, j, n, beta)
+                    flag |= K.FLAG_BAD_INDEX if bad else 0
+                    for i in range(j * G, (j + 1) * G):
+                        o[b, i], lse[b, i] = K._attend(K.to_f64(q[b, i]), K.to_f64(Kr), K.to_f64(Vr), scale)
+            return o, lse, flag
+        m.decode_paged = decode_paged
+        out["paged_" + kind] = m
+
+    def append_paged_slot_plus_one(kp, vp, table, sl, kn, vn):
+        beta = kp.shape[2]
+        flag = 0
+        for b in range(sl.shape[0]):
+            n = int(sl[b])
+            if n >= table.shape[1] * beta:
+                flag |= K.FLAG_CACHE_FULL
+                continue
+            blk = int(table[b, n // beta])
+            if not 0 <= blk < kp.shape[0]:
+                flag |= K.FLAG_BAD_INDEX
+                continue
+            kp[blk, :, (n + 1) % beta] = kn[b]
+            vp[blk, :, (n + 1) % beta] = vn[b]
+            sl[b] = n + 1
+        return flag
+    m = _copy()
+    m.append_paged = append_paged_slot_plus_one
+    out["append_paged_wrong_slot"] = m
     return out
 
 
