@@ -17,7 +17,8 @@ new k/v read and written + lengths).  `roofline` is the dense decode kernel
 alone, timed with HIP events over back-to-back launches of one step's
 layers.  `also` carries the same figures for the GQA, MLA and top-k
 workloads, for the GQA workload over FP8 E4M3 caches (C3F8) and for the GQA
-workload attending a sliding window of its newest 128 positions (C3W128).  `cpu_baseline` is the fp64 oracle on the same inputs (copied to
+workload attending a sliding window of its newest 128 positions (C3W128) and
+over a paged cache of 16-position blocks (C3P16).  `cpu_baseline` is the fp64 oracle on the same inputs (copied to
 the host), on a time-bounded sample of layer-steps.
 """
 from __future__ import annotations
@@ -46,8 +47,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="C2", choices=["C2", "C3", "C4", "C5", "C3F8", "C3W128"])
-    ap.add_argument("--others", default="C3,C4,C5,C3F8,C3W128",
+    ap.add_argument("--config", default="C2", choices=["C2", "C3", "C4", "C5", "C3F8", "C3W128", "C3P16"])
+    ap.add_argument("--others", default="C3,C4,C5,C3F8,C3W128,C3P16",
                     help="also-measured workloads (comma list; 'none' for none)")
     ap.add_argument("--kernel-reps", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true")
@@ -417,9 +418,95 @@ class WindowWorkload(DenseWorkload):
         return super().describe().replace(", seq_lens", f", window {self.WINDOW} of seq_lens")
 
 
+class PagedWorkload:
+    """The GQA layers of C3 over a paged cache: pools of 16-position blocks
+    sized to the sequences' lengths, blocks in shuffled physical order, one
+    block table per layer buffer.  A layer-step is kvc_append_paged then
+    kvc_decode_attn_paged."""
+
+    kernel = "dense_mfma_kernel<false, false, false, true> (paged, 16-position blocks)"
+    kernel_appends = False
+    BETA = 16
+
+    def __init__(self, cfg, slack, torch, kvc):
+        self.cfg, self.torch, self.kvc = cfg, torch, kvc
+        B, n_h, n_kv, d = cfg.B, cfg.n_h, cfg.n_kv, cfg.d
+        self.pre = syn.pre_append_lens(cfg).astype(np.int64)
+        self.L_max = int(self.pre.max() + 1 + slack)
+        self.max_blocks = -(-self.L_max // self.BETA)
+        self.layers = cfg.layers
+        self.nbuf = cfg.distinct_buffers
+        need = [-(-int(n + 1 + slack) // self.BETA) for n in self.pre]
+        self.num_blocks = int(sum(need))
+        order = np.random.default_rng(1000 + cfg.cfg_id).permutation(self.num_blocks)
+        table = np.full((B, self.max_blocks), 1 << 30, dtype=np.int32)
+        at = 0
+        for b in range(B):
+            table[b, :need[b]] = order[at:at + need[b]]
+            at += need[b]
+        self.table = torch.from_numpy(table).cuda()
+        dt = torch.bfloat16
+        pool = lambda i, t: syn.device_normal_(
+            torch.empty(self.num_blocks, n_kv, self.BETA, d, dtype=dt, device="cuda"),
+            syn.device_seed(cfg.cfg_id, i, t))
+        self.K = [pool(i, "k") for i in range(self.nbuf)]
+        self.V = [pool(i, "v") for i in range(self.nbuf)]
+        mk = lambda shape, l, t: syn.device_normal_(torch.empty(*shape, dtype=dt, device="cuda"),
+                                                    syn.device_seed(cfg.cfg_id, l, t))
+        self.q = [mk((B, n_h, d), l, "q") for l in range(self.layers)]
+        self.kn = [mk((B, n_kv, d), l, "k_new") for l in range(self.layers)]
+        self.vn = [mk((B, n_kv, d), l, "v_new") for l in range(self.layers)]
+        self.out = [torch.empty(B, n_h, d, dtype=dt, device="cuda") for _ in range(self.layers)]
+        pre_t = torch.tensor(self.pre, dtype=torch.int32)
+        self.sl = [pre_t.clone().cuda() for _ in range(self.layers)]
+        self.ws = kvc.workspace(kvc.kvc_decode_attn_paged_workspace_size(
+            B, n_h, n_kv, self.max_blocks, self.BETA, d, kvc.KVC_BF16))
+
+    def step(self):
+        for l in range(self.layers):
+            b = l % self.nbuf
+            self.kvc.kvc_append_paged(self.K[b], self.V[b], self.table, self.sl[l], self.kn[l],
+                                      self.vn[l])
+            self.kvc.kvc_decode_attn_paged(self.q[l], self.K[b], self.V[b], self.table, self.sl[l],
+                                           self.out[l], scale=self.cfg.scale, workspace=self.ws)
+
+    def decode_only(self):
+        for l in range(self.layers):
+            b = l % self.nbuf
+            self.kvc.kvc_decode_attn_paged(self.q[l], self.K[b], self.V[b], self.table, self.sl[l],
+                                           self.out[l], scale=self.cfg.scale, workspace=self.ws)
+
+    def kernel_only(self):
+        self.decode_only()
+
+    def lens_after(self, steps_done):
+        return np.minimum(self.pre + 1 + steps_done, self.L_max)
+
+    def kernel_bytes(self, n):
+        c = self.cfg
+        return int(2 * c.n_kv * c.d * 2 * n.sum() + 4 * (-(-n // self.BETA)).sum()
+                   + c.B * c.n_h * c.d * (2 + 2) + 4 * c.B)
+
+    def launch_bytes(self, steps_done):
+        return self.kernel_bytes(self.lens_after(steps_done - 1))
+
+    def step_bytes(self, steps_done):
+        c = self.cfg
+        per_layer = self.kernel_bytes(self.lens_after(steps_done)) + 4 * c.B * c.n_kv * c.d * 2 + 12 * c.B
+        return per_layer * self.layers
+
+    def describe(self):
+        c = self.cfg
+        return (f"{c.name} over a paged cache: B={c.B} n_h={c.n_h} n_kv={c.n_kv} d={c.d} bf16, "
+                f"{self.BETA}-position blocks ({self.num_blocks} in shuffled order), seq_lens ~ "
+                f"U[{c.len_range[0]}, {c.len_range[1]}] (post-append), {self.layers} layers "
+                f"({self.nbuf} distinct pools)")
+
+
 WORKLOADS = {"C2": (syn.C2, DenseWorkload), "C3": (syn.C3, DenseWorkload),
              "C4": (syn.C4, MlaWorkload), "C5": (syn.C5, TopKWorkload),
-             "C3F8": (syn.C3, Fp8DenseWorkload), "C3W128": (syn.C3, WindowWorkload)}
+             "C3F8": (syn.C3, Fp8DenseWorkload), "C3W128": (syn.C3, WindowWorkload),
+             "C3P16": (syn.C3, PagedWorkload)}
 
 
 # ---------------------------------------------------------------- timing

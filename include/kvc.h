@@ -149,6 +149,41 @@ int kvc_append_decode_attn(const void* q, void* k_cache, void* v_cache,
                            void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * Paged cache (guide, "The allocator, not the algorithm": fixed-size blocks
+ * in a shared pool, mapped per sequence by a block table, so a sequence
+ * wastes at most block_size - 1 slots).
+ *
+ * Layout: k_pool, v_pool [num_blocks, n_kv, block_size, d]; block_table
+ * [B, max_blocks] int32 device: position t of sequence b is row t % block_size
+ * of block block_table[b][t / block_size].  A table entry outside
+ * [0, num_blocks) is invalid.  block_size is a power of two in [8, 4096];
+ * each pool is at most 2^31 bytes; max_blocks * block_size < 2^31.
+ *
+ * kvc_append_paged - kvc_append into slot n = seq_lens[b]: n at or past
+ * max_blocks * block_size sets KVC_FLAG_CACHE_FULL, an invalid block at the
+ * slot sets KVC_FLAG_BAD_INDEX; in both cases nothing is written and the
+ * length stays.  dtype KVC_F32 or KVC_BF16, d * element size a multiple of 16.
+ *
+ * kvc_decode_attn_paged - kvc_decode_attn over positions [0, seq_lens[b])
+ * read through the block table (seq_lens clamped to max_blocks *
+ * block_size).  Positions in an invalid block are skipped and set
+ * KVC_FLAG_BAD_INDEX.  This build supports dtype KVC_BF16 with d = 128.
+ * The workspace query takes the table geometry.
+ */
+int kvc_append_paged(void* k_pool, void* v_pool, const int32_t* block_table,
+                     int max_blocks, int32_t* seq_lens, const void* k_new,
+                     const void* v_new, int B, int n_kv, int num_blocks,
+                     int block_size, int d, int dtype, int32_t* flag, void* stream);
+size_t kvc_decode_attn_paged_workspace_size(int B, int n_h, int n_kv, int max_blocks,
+                                            int block_size, int d, int dtype);
+int kvc_decode_attn_paged(const void* q, const void* k_pool, const void* v_pool,
+                          const int32_t* block_table, int max_blocks,
+                          const int32_t* seq_lens, void* out, float* lse, int B,
+                          int n_h, int n_kv, int num_blocks, int block_size, int d,
+                          float scale, int dtype, int32_t* flag, void* workspace,
+                          size_t ws_bytes, void* stream);
+
+/*
  * kvc_decode_attn_window - kvc_decode_attn over a sliding window of the
  * newest positions.  ("890 bytes a token", SWA bounded replay passage: for a
  * replay starting at position s, the query at position i attends to keys

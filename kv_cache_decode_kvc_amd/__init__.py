@@ -71,6 +71,10 @@ def lib() -> ctypes.CDLL:
         "kvc_decode_attn_window_workspace_size": (_Z, [_I, _I, _I, _I, _I, _I, _I]),
         "kvc_decode_attn_window": (_I, [_P, _P, _P, _P, _P, _I, _P, _P, _I, _I, _I, _I, _I,
                                         _F, _I, _P, _Z, _P]),
+        "kvc_append_paged": (_I, [_P, _P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P]),
+        "kvc_decode_attn_paged_workspace_size": (_Z, [_I, _I, _I, _I, _I, _I, _I]),
+        "kvc_decode_attn_paged": (_I, [_P, _P, _P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _I,
+                                       _F, _I, _P, _P, _Z, _P]),
         "kvc_append_fp8": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _F, _P, _P]),
         "kvc_decode_attn_fp8_workspace_size": (_Z, [_I, _I, _I, _I, _I]),
         "kvc_decode_attn_fp8": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
@@ -263,6 +267,38 @@ def kvc_decode_attn_window(q, k_cache, v_cache, seq_lens, out, window, win_start
                                       n_kv, L_max, d, scale, _dtype_code(q), wp, wn,
                                       _stream(stream))
     _check(st, "kvc_decode_attn_window")
+
+
+def kvc_append_paged(k_pool, v_pool, block_table, seq_lens, k_new, v_new, flag=None,
+                     stream=None):
+    """Append k_new/v_new [B, n_kv, d] into pools [num_blocks, n_kv, beta, d]
+    at slot seq_lens[b] through block_table [B, max_blocks]; bump seq_lens."""
+    num_blocks, n_kv, beta, d = k_pool.shape
+    B, max_blocks = block_table.shape
+    st = lib().kvc_append_paged(_ptr(k_pool), _ptr(v_pool), _ptr(block_table), max_blocks,
+                                _ptr(seq_lens), _ptr(k_new), _ptr(v_new), B, n_kv, num_blocks,
+                                beta, d, _dtype_code(k_pool), _ptr(flag), _stream(stream))
+    _check(st, "kvc_append_paged")
+
+
+def kvc_decode_attn_paged_workspace_size(B, n_h, n_kv, max_blocks, block_size, d, dtype) -> int:
+    return lib().kvc_decode_attn_paged_workspace_size(B, n_h, n_kv, max_blocks, block_size, d,
+                                                      dtype)
+
+
+def kvc_decode_attn_paged(q, k_pool, v_pool, block_table, seq_lens, out, lse=None, scale=None,
+                          flag=None, workspace=None, stream=None):
+    """Dense decode through a block table; q/out [B, n_h, d]."""
+    B, n_h, d = q.shape
+    num_blocks, n_kv, beta, _ = k_pool.shape
+    max_blocks = block_table.shape[1]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    wp, wn = _ws(workspace)
+    st = lib().kvc_decode_attn_paged(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table),
+                                     max_blocks, _ptr(seq_lens), _ptr(out), _ptr(lse), B, n_h,
+                                     n_kv, num_blocks, beta, d, scale, _dtype_code(q), _ptr(flag),
+                                     wp, wn, _stream(stream))
+    _check(st, "kvc_decode_attn_paged")
 
 
 def _need_u8(t, what):

@@ -103,6 +103,54 @@ hipError_t launch_append_fp8(const AppendParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Paged append: slot n of sequence b is offset n % beta of block
+// block_table[b][n / beta] in pools [num_blocks, n_kv, beta, d].  A full
+// table sets flag bit 0, an invalid block bit 1; then nothing is written and
+// the length stays.
+__global__ __launch_bounds__(256) void append_paged_kernel(AppendParams p) {
+  __shared__ int s_n, s_blk;
+  const int b = blockIdx.x;
+  if (threadIdx.x == 0) {
+    const int n = p.seq_lens[b];
+    int blk = -1;
+    if (n >= 0 && n < (p.max_blocks << p.page_shift))
+      blk = p.block_table[(size_t)b * p.max_blocks + (n >> p.page_shift)];
+    s_n = n;
+    s_blk = blk;
+  }
+  __syncthreads();
+  const int n = s_n, blk = s_blk;
+  if (n < 0 || n >= (p.max_blocks << p.page_shift)) {
+    if (threadIdx.x == 0 && p.flag) atomicOr(p.flag, 1);
+    return;
+  }
+  if (blk < 0 || blk >= p.num_blocks) {
+    if (threadIdx.x == 0 && p.flag) atomicOr(p.flag, 2);
+    return;
+  }
+  const int beta = 1 << p.page_shift;
+  const int units = p.d * p.elem_bytes / 16;
+  const int total = p.n_kv * units;
+  const u32x4* ks = reinterpret_cast<const u32x4*>(p.k_new);
+  const u32x4* vs = reinterpret_cast<const u32x4*>(p.v_new);
+  u32x4* kd = reinterpret_cast<u32x4*>(p.k_cache);
+  u32x4* vd = reinterpret_cast<u32x4*>(p.v_cache);
+  for (int e = threadIdx.x; e < total; e += blockDim.x) {
+    const int jj = e / units, c = e - jj * units;
+    const size_t dst = (((size_t)blk * p.n_kv + jj) * beta + (n & (beta - 1))) * units + c;
+    const size_t src = ((size_t)b * p.n_kv + jj) * units + c;
+    kd[dst] = ks[src];
+    vd[dst] = vs[src];
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) p.seq_lens[b] = n + 1;
+}
+
+hipError_t launch_append_paged(const AppendParams& p, hipStream_t s) {
+  hipLaunchKernelGGL(append_paged_kernel, dim3(p.B), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
 hipError_t launch_append(const AppendParams& p, hipStream_t s) {
   hipLaunchKernelGGL(append_kernel, dim3(p.B), dim3(256), 0, s, p);
   return hipGetLastError();

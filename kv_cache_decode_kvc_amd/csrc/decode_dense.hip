@@ -356,6 +356,58 @@ __device__ inline void load_listed(Chunk& c, const ChunkIdx& x, int cs, int end,
   }
 }
 
+// Paged cache: the block ids of a chunk's rows, loaded two chunks ahead of
+// the rows.  Lane (r, g) needs the blocks of its two K rows (cs + pi(a, r))
+// and of its eight V rows (cs + g*8 + 0..7, one block: beta is a multiple of
+// 8).  Entries past the table read as zero; rows past the split's end are
+// never loaded, so their (possibly unset) entries are not used.
+struct PageIdx {
+  uint32_t k[2];
+  uint32_t v;
+};
+
+__device__ inline void load_page_idx(PageIdx& x, int cs, __amdgpu_buffer_rsrc_t tr, int shift,
+                                     int r, int g) {
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+    x.k[a] = __builtin_amdgcn_raw_buffer_load_b32(
+        tr, (uint32_t)((cs + (r >> 2) * 8 + a * 4 + (r & 3)) >> shift) * 4, 0, 0);
+  x.v = __builtin_amdgcn_raw_buffer_load_b32(tr, (uint32_t)((cs + g * 8) >> shift) * 4, 0, 0);
+}
+
+// Rows through the block table (pool rows of 256 bytes: d = 128 bf16).  A
+// row in an invalid block is not loaded, its position is masked like an
+// unlisted top-k slot (vmask) and `bad` is set.
+__device__ inline void load_paged(Chunk& c, const PageIdx& x, int cs, int end,
+                                  const DenseParams& p, int j, __amdgpu_buffer_rsrc_t kr,
+                                  __amdgpu_buffer_rsrc_t vr, int r, int g, bool& bad) {
+  constexpr uint32_t kRow = 256;
+  const int shift = p.page_shift;
+  const int in_blk = (1 << shift) - 1;
+  const uint32_t nb = (uint32_t)p.num_blocks;
+  const int t0 = cs + g * 8;
+  const bool vok = x.v < nb;
+  if (t0 < end && !vok) bad = true;
+  const uint32_t vrow = ((x.v * (uint32_t)p.n_kv + j) << shift) + (t0 & in_blk);
+  uint32_t mask = 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const bool use = t0 + e < end && vok;
+    mask |= (use ? 1u : 0u) << e;
+    c.v[e] = buf_load16_stream(vr, use ? (vrow + e) * kRow + r * 16 : kOobOffset);
+  }
+  c.vmask = mask;
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    const int t = cs + (r >> 2) * 8 + a * 4 + (r & 3);
+    const bool use = t < end && x.k[a] < nb;
+    const uint32_t krow = ((x.k[a] * (uint32_t)p.n_kv + j) << shift) + (t & in_blk);
+    const uint32_t kb = use ? krow * kRow + g * 16 : kOobOffset;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) c.k[a][kk] = buf_load16_stream(kr, kb + kk * 64);
+  }
+}
+
 // Fused append: the chunk holding the new token's slot takes that row from
 // k_new/v_new (the cache copy is being written concurrently).  Lane (r, g)
 // holds K rows pi(a, r) at columns kk*32 + g*8 and V rows g*8 + e at columns
@@ -487,9 +539,10 @@ __device__ inline void expand_chunk(const ChunkF8& f, Chunk& c) {
 template <bool FP8> struct ChunkOf { using T = Chunk; };
 template <> struct ChunkOf<true> { using T = ChunkF8; };
 
-template <bool TOPK, bool APPEND, bool FP8 = false>
+template <bool TOPK, bool APPEND, bool FP8 = false, bool PAGED = false>
 __global__ __launch_bounds__(256, 2) void dense_mfma_kernel(DenseParams p) {
   static_assert(!FP8 || (!TOPK && !APPEND), "FP8 caches: plain decode only");
+  static_assert(!PAGED || (!TOPK && !APPEND && !FP8), "paged caches: plain decode only");
   __shared__ MergeLds<128> L;
   int b, j, split;
   decode_unit(p, b, j, split);
@@ -515,12 +568,19 @@ __global__ __launch_bounds__(256, 2) void dense_mfma_kernel(DenseParams p) {
   const size_t unit = (size_t)b * p.n_kv + j;
   constexpr uint32_t kRowBytes = FP8 ? 128u : 256u;
   const size_t unit_bytes = (size_t)p.L_max * kRowBytes;
+  // (paged: the whole pool, at most 2^31 bytes, checked on the host)
+  const uint32_t pool_bytes =
+      PAGED ? ((uint32_t)p.num_blocks * (uint32_t)p.n_kv << p.page_shift) * kRowBytes : 0u;
   const __amdgpu_buffer_rsrc_t kr =
-      make_rsrc((const char*)p.k + unit * unit_bytes, (uint32_t)n * kRowBytes);
+      PAGED ? make_rsrc(p.k, pool_bytes)
+            : make_rsrc((const char*)p.k + unit * unit_bytes, (uint32_t)n * kRowBytes);
   const __amdgpu_buffer_rsrc_t vr =
-      make_rsrc((const char*)p.v + unit * unit_bytes, (uint32_t)n * kRowBytes);
+      PAGED ? make_rsrc(p.v, pool_bytes)
+            : make_rsrc((const char*)p.v + unit * unit_bytes, (uint32_t)n * kRowBytes);
   const __amdgpu_buffer_rsrc_t ir =
-      TOPK ? make_rsrc(p.idx + unit * p.K, (uint32_t)p.K * 4u) : kr;
+      TOPK ? make_rsrc(p.idx + unit * p.K, (uint32_t)p.K * 4u)
+           : PAGED ? make_rsrc(p.block_table + (size_t)b * p.max_blocks, (uint32_t)p.max_blocks * 4u)
+                   : kr;
 
   bf16x8 qop[4];
   if (r < p.G) {
@@ -566,7 +626,7 @@ __global__ __launch_bounds__(256, 2) void dense_mfma_kernel(DenseParams p) {
       if constexpr (APPEND)
         if (new_slot >= at && new_slot < at + kDenseChunk)
           patch_new_row(c, new_slot - at, knr, vnr, r, g);
-      compute_chunk<TOPK>(c, at, end, qop, p.scale_log2, g, st);
+      compute_chunk<TOPK || PAGED>(c, at, end, qop, p.scale_log2, g, st);
     }
   };
   if constexpr (TOPK) {
@@ -592,6 +652,29 @@ __global__ __launch_bounds__(256, 2) void dense_mfma_kernel(DenseParams p) {
         if (cs >= end) break;
       }
     }
+  } else if constexpr (PAGED) {
+    if (cs < end) {
+      // block ids two chunks ahead, rows one chunk ahead
+      Chunk A, Bc;
+      PageIdx I0, I1;
+      load_page_idx(I0, cs, ir, p.page_shift, r, g);
+      load_page_idx(I1, cs + kStride, ir, p.page_shift, r, g);
+      load_paged(A, I0, cs, end, p, j, kr, vr, r, g, bad);
+      while (true) {
+        load_page_idx(I0, cs + 2 * kStride, ir, p.page_shift, r, g);
+        load_paged(Bc, I1, cs + kStride, end, p, j, kr, vr, r, g, bad);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(A, cs);
+        cs += kStride;
+        if (cs >= end) break;
+        load_page_idx(I1, cs + 2 * kStride, ir, p.page_shift, r, g);
+        load_paged(A, I0, cs + kStride, end, p, j, kr, vr, r, g, bad);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(Bc, cs);
+        cs += kStride;
+        if (cs >= end) break;
+      }
+    }
   } else if (cs < end) {
     Raw A, Bc;
     load(A, cs);
@@ -608,7 +691,7 @@ __global__ __launch_bounds__(256, 2) void dense_mfma_kernel(DenseParams p) {
       if (cs >= end) break;
     }
   }
-  if constexpr (TOPK) {
+  if constexpr (TOPK || PAGED) {
     if (p.flag && __any(bad) && lane == 0) atomicOr(p.flag, 2);
   }
 
@@ -796,6 +879,11 @@ hipError_t launch_dense_mfma(const DenseParams& p, bool topk, bool append, hipSt
     hipLaunchKernelGGL((dense_mfma_kernel<false, true>), dense_grid(p), dim3(256), 0, s, p);
   else
     hipLaunchKernelGGL((dense_mfma_kernel<false, false>), dense_grid(p), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_dense_paged(const DenseParams& p, hipStream_t s) {
+  hipLaunchKernelGGL((dense_mfma_kernel<false, false, false, true>), dense_grid(p), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

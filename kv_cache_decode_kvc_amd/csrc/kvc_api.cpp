@@ -274,7 +274,9 @@ static int dense_common(const void* q, const void* k_cache, const void* v_cache,
                         bool topk, const void* k_new = nullptr,
                         const void* v_new = nullptr, bool fused = false,
                         bool fp8 = false, float k_scale = 1.f, float v_scale = 1.f,
-                        int window = 0, const int32_t* win_start = nullptr) {
+                        int window = 0, const int32_t* win_start = nullptr,
+                        const int32_t* block_table = nullptr, int max_blocks = 0,
+                        int num_blocks = 0, int page_shift = 0) {
   // FP8 caches: q and out are bf16; the shape rules are those of bf16 with
   // d = 128 (checked by the caller).
   const DenseCheck c = check_dense_shape(B, n_h, n_kv, L_max, d, dtype, K, topk, fused, window);
@@ -311,6 +313,14 @@ static int dense_common(const void* q, const void* k_cache, const void* v_cache,
   p.out_scale = 1.f;
   p.window = window;
   p.win_start = window > 0 ? win_start : nullptr;
+  p.block_table = block_table;
+  p.max_blocks = max_blocks;
+  p.num_blocks = num_blocks;
+  p.page_shift = page_shift;
+  if (block_table) {
+    p.flag = flag;
+    return launch_status(launch_dense_paged(p, static_cast<hipStream_t>(stream)));
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (fp8) {
     p.scale_log2 *= k_scale;
@@ -375,6 +385,74 @@ int kvc_decode_attn_window(const void* q, const void* k_cache, const void* v_cac
                       n_h, n_kv, L_max, d, scale, dtype, nullptr, workspace,
                       ws_bytes, stream, false, nullptr, nullptr, false, false,
                       1.f, 1.f, window, win_start);
+}
+
+// Paged caches: block size a power of two in [8, 4096]; pools of at most
+// 2^31 bytes (32-bit offsets with an out-of-range marker above them).
+static int page_shift_of(int block_size) {
+  if (block_size < 8 || block_size > 4096 || (block_size & (block_size - 1))) return -1;
+  int sh = 0;
+  while ((1 << sh) < block_size) ++sh;
+  return sh;
+}
+
+static int check_paged(int B, int n_kv, int max_blocks, int num_blocks, int block_size,
+                       int d, int elem, int& shift) {
+  if (B < 0 || n_kv < 1 || max_blocks < 1 || num_blocks < 1 || d < 1) return KVC_ERR_BAD_SHAPE;
+  shift = page_shift_of(block_size);
+  if (shift < 0) return KVC_ERR_BAD_SHAPE;
+  if ((int64_t)max_blocks * block_size >= kMaxOffset) return KVC_ERR_BAD_SHAPE;
+  if ((int64_t)num_blocks * n_kv * block_size * d * elem > kMaxOffset) return KVC_ERR_BAD_SHAPE;
+  return KVC_OK;
+}
+
+size_t kvc_decode_attn_paged_workspace_size(int B, int n_h, int n_kv, int max_blocks,
+                                            int block_size, int d, int dtype) {
+  if (page_shift_of(block_size) < 0 || max_blocks < 1 ||
+      (int64_t)max_blocks * block_size >= kMaxOffset)
+    return 0;
+  const DenseCheck c = check_dense_shape(B, n_h, n_kv, max_blocks * block_size, d, dtype, 0, false);
+  return c.status == KVC_OK ? c.ws.total : 0;
+}
+
+int kvc_decode_attn_paged(const void* q, const void* k_pool, const void* v_pool,
+                          const int32_t* block_table, int max_blocks,
+                          const int32_t* seq_lens, void* out, float* lse, int B,
+                          int n_h, int n_kv, int num_blocks, int block_size, int d,
+                          float scale, int dtype, int32_t* flag, void* workspace,
+                          size_t ws_bytes, void* stream) {
+  if (!good_dtype(dtype)) return KVC_ERR_BAD_DTYPE;
+  int shift = 0;
+  const int st = check_paged(B, n_kv, max_blocks, num_blocks, block_size, d, elem_bytes(dtype), shift);
+  if (st != KVC_OK) return st;
+  if (dtype != KVC_BF16 || d != 128) return KVC_ERR_UNSUPPORTED;
+  if (!block_table) return KVC_ERR_NULL_PTR;
+  if (!aligned(block_table, 4)) return KVC_ERR_MISALIGNED;
+  return dense_common(q, k_pool, v_pool, seq_lens, nullptr, 0, out, lse, B, n_h, n_kv,
+                      max_blocks * block_size, d, scale, dtype, flag, workspace, ws_bytes,
+                      stream, false, nullptr, nullptr, false, false, 1.f, 1.f, 0, nullptr,
+                      block_table, max_blocks, num_blocks, shift);
+}
+
+int kvc_append_paged(void* k_pool, void* v_pool, const int32_t* block_table,
+                     int max_blocks, int32_t* seq_lens, const void* k_new,
+                     const void* v_new, int B, int n_kv, int num_blocks,
+                     int block_size, int d, int dtype, int32_t* flag, void* stream) {
+  if (!good_dtype(dtype)) return KVC_ERR_BAD_DTYPE;
+  int shift = 0;
+  const int st = check_paged(B, n_kv, max_blocks, num_blocks, block_size, d, elem_bytes(dtype), shift);
+  if (st != KVC_OK) return st;
+  if ((d * elem_bytes(dtype)) % 16 != 0) return KVC_ERR_BAD_SHAPE;
+  if (!k_pool || !v_pool || !block_table || !seq_lens || !k_new || !v_new) return KVC_ERR_NULL_PTR;
+  if (!aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(k_new, 16) ||
+      !aligned(v_new, 16) || !aligned(block_table, 4) || !aligned(seq_lens, 4) ||
+      (flag && !aligned(flag, 4)))
+    return KVC_ERR_MISALIGNED;
+  if (B == 0) return KVC_OK;
+  AppendParams p{k_pool, v_pool, seq_lens, k_new, v_new, flag,
+                 B, n_kv, max_blocks * block_size, d, elem_bytes(dtype), 1.f, 1.f,
+                 block_table, max_blocks, num_blocks, shift};
+  return launch_status(launch_append_paged(p, static_cast<hipStream_t>(stream)));
 }
 
 size_t kvc_decode_attn_fp8_workspace_size(int B, int n_h, int n_kv, int L_max,

@@ -39,6 +39,8 @@ struct AppendParams {
   int32_t* flag;          // may be null
   int B, n_kv, L_max, d, elem_bytes;
   float k_inv, v_inv;     // FP8 append: 1 / scale of the keys and values
+  const int32_t* block_table;   // paged append: [B, max_blocks]
+  int max_blocks, num_blocks, page_shift;
 };
 
 // Dense and top-k decode.  Workspace pointers are null when P_max == 1.
@@ -68,6 +70,10 @@ struct DenseParams {
   float out_scale;        // multiplies the output (the value scale for FP8 caches)
   int window;             // > 0: attend only the newest `window` positions
   const int32_t* win_start;  // window mode, may be null: first present position per sequence
+  // paged cache: k/v are pools [num_blocks, n_kv, 1 << page_shift, d];
+  // position t of sequence b is in block block_table[b * max_blocks + (t >> page_shift)]
+  const int32_t* block_table;
+  int max_blocks, num_blocks, page_shift;
 };
 
 struct MlaParams {
@@ -140,6 +146,8 @@ inline WsLayout ws_layout(size_t units, size_t B, size_t n_h, size_t P_max,
 hipError_t launch_append(const AppendParams& p, hipStream_t s);
 hipError_t launch_append_fp8(const AppendParams& p, hipStream_t s);
 hipError_t launch_dense_fp8(const DenseParams& p, hipStream_t s);
+hipError_t launch_dense_paged(const DenseParams& p, hipStream_t s);
+hipError_t launch_append_paged(const AppendParams& p, hipStream_t s);
 hipError_t launch_dense_mfma(const DenseParams& p, bool topk, bool append, hipStream_t s);
 hipError_t launch_dense_generic(const DenseParams& p, int dtype, bool topk,
                                 bool append, hipStream_t s);

@@ -32,6 +32,7 @@ DOMINANT = {
     "C5": "dense_mfma_kernel<true, false, false>",
     "C3F8": "dense_mfma_kernel<false, false, true>",
     "C3W128": "dense_mfma_kernel<false, false, false>",
+    "C3P16": "dense_mfma_kernel<false, false, false, true>",
 }
 
 

@@ -246,3 +246,41 @@ def test_window_validation(L):
     assert L.kvc_decode_attn_window_workspace_size(32, 64, 8, 32768, 128, kvc.KVC_BF16, 0) == 0
     assert L.kvc_decode_attn_window_workspace_size(1, 8, 2, 64, 128, kvc.KVC_BF16, 10 ** 6) == \
         L.kvc_decode_attn_workspace_size(1, 8, 2, 64, 128, kvc.KVC_BF16)
+
+
+def test_paged_validation(L):
+    def dp(**kw):
+        a = dict(q=A16, k=A16, v=A16, t=A4, mb=64, sl=A4, out=A16, lse=NULL, B=2, n_h=8, n_kv=2,
+                 nb=100, bs=16, d=128, scale=0.1, dt=kvc.KVC_BF16, flag=NULL, ws=A16,
+                 wsb=1 << 30, stream=NULL)
+        a.update(kw)
+        return L.kvc_decode_attn_paged(a["q"], a["k"], a["v"], a["t"], a["mb"], a["sl"], a["out"],
+                                       a["lse"], a["B"], a["n_h"], a["n_kv"], a["nb"], a["bs"],
+                                       a["d"], a["scale"], a["dt"], a["flag"], a["ws"], a["wsb"],
+                                       a["stream"])
+    assert dp(t=NULL) == -1
+    assert dp(bs=12) == -2          # not a power of two
+    assert dp(bs=4) == -2           # below 8
+    assert dp(nb=0) == -2
+    assert dp(nb=1 << 20, bs=64) == -2      # pool beyond 2^31 bytes
+    assert dp(d=64) == -4
+    assert dp(dt=kvc.KVC_F32) == -4
+    assert dp(t=ctypes.c_void_p(0x10002)) == -6
+    assert dp(B=0) == 0
+
+    def ap(**kw):
+        a = dict(k=A16, v=A16, t=A4, mb=64, sl=A4, kn=A16, vn=A16, B=2, n_kv=2, nb=100, bs=16,
+                 d=128, dt=kvc.KVC_BF16, flag=NULL, stream=NULL)
+        a.update(kw)
+        return L.kvc_append_paged(a["k"], a["v"], a["t"], a["mb"], a["sl"], a["kn"], a["vn"],
+                                  a["B"], a["n_kv"], a["nb"], a["bs"], a["d"], a["dt"], a["flag"],
+                                  a["stream"])
+    assert ap(v=NULL) == -1
+    assert ap(d=4) == -2            # 8 bytes per row: not whole 16-byte pieces
+    assert ap(bs=24) == -2
+    assert ap(dt=3) == -3
+    assert ap(k=A8) == -6
+    assert ap(B=0) == 0
+    assert L.kvc_decode_attn_paged_workspace_size(32, 64, 8, 2048, 16, 128, kvc.KVC_BF16) == \
+        L.kvc_decode_attn_workspace_size(32, 64, 8, 32768, 128, kvc.KVC_BF16)
+    assert L.kvc_decode_attn_paged_workspace_size(32, 64, 8, 2048, 12, 128, kvc.KVC_BF16) == 0

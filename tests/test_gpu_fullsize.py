@@ -237,3 +237,47 @@ def test_fullsize_gqa_layer_window():
                                             np.array([W], np.int32), c.scale, W)
         compare(oracle.to_f64(bits(out[b, j * G:(j + 1) * G])), o_ref[0], 2e-2, f"window b={b} j={j}")
         compare_lse(host(lse[b, j * G:(j + 1) * G]), l_ref[0], 4e-3)
+
+
+def test_fullsize_gqa_layer_paged():
+    """The GQA layer over a paged cache of 16-position blocks in shuffled
+    order (pools sized to the lengths), as the benchmark's paged workload."""
+    c = syn.C3
+    beta = 16
+    pre = syn.pre_append_lens(c)
+    need = [-(-int(n + 1) // beta) for n in pre]
+    nblk = int(sum(need))
+    mb = -(-int(pre.max() + 1) // beta)
+    order = np.random.default_rng(7).permutation(nblk)
+    table = np.full((c.B, mb), 1 << 30, dtype=np.int32)
+    at = 0
+    for b in range(c.B):
+        table[b, :need[b]] = order[at:at + need[b]]
+        at += need[b]
+    K = normal((nblk, c.n_kv, beta, c.d), c.cfg_id, 0, "k")
+    V = normal((nblk, c.n_kv, beta, c.d), c.cfg_id, 0, "v")
+    q = normal((c.B, c.n_h, c.d), c.cfg_id, 0, "q")
+    kn = normal((c.B, c.n_kv, c.d), c.cfg_id, 0, "k_new")
+    vn = normal((c.B, c.n_kv, c.d), c.cfg_id, 0, "v_new")
+    tab = torch.from_numpy(table).cuda()
+    sl = torch.tensor(pre, dtype=torch.int32, device="cuda")
+    out = torch.empty_like(q)
+    lse = torch.empty(c.B, c.n_h, dtype=torch.float32, device="cuda")
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ws = kvc.workspace(kvc.kvc_decode_attn_paged_workspace_size(c.B, c.n_h, c.n_kv, mb, beta, c.d,
+                                                                kvc.KVC_BF16))
+    kvc.kvc_append_paged(K, V, tab, sl, kn, vn, flag=flag)
+    kvc.kvc_decode_attn_paged(q, K, V, tab, sl, out, lse, scale=c.scale, flag=flag, workspace=ws)
+    torch.cuda.synchronize()
+    assert host(sl).tolist() == (pre + 1).tolist()
+    assert int(host(flag)[0]) == 0
+    G = c.n_h // c.n_kv
+    for b, j in sample_units(pre, c.n_kv, 3, 37):
+        n = int(pre[b]) + 1
+        blocks = torch.from_numpy(table[b, :need[b]].astype(np.int64)).cuda()
+        kb = bits(K.index_select(0, blocks)[:, j].reshape(-1, c.d)[:n])
+        vb = bits(V.index_select(0, blocks)[:, j].reshape(-1, c.d)[:n])
+        o_ref, l_ref = oracle.decode(bits(q[b, j * G:(j + 1) * G])[None], kb[None, None],
+                                     vb[None, None], np.array([n], np.int32), c.scale)
+        compare(oracle.to_f64(bits(out[b, j * G:(j + 1) * G])), o_ref[0], 2e-2, f"paged b={b} j={j}")
+        compare_lse(host(lse[b, j * G:(j + 1) * G]), l_ref[0], 4e-3)
