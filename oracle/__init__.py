@@ -3,6 +3,6 @@ from .kvc_oracle import (  # noqa: F401
     FLAG_BAD_INDEX, FLAG_CACHE_FULL, FP8_E4M3_MAX, append, append_fp8,
     append_paged, bf16_to_f64, cache_bytes, decode, decode_fp8, decode_mla,
     decode_paged, decode_topk, paged_rows, paged_waste_fraction,
-    decode_window, f64_to_fp8_e4m3, fp8_e4m3_to_f64, full_causal,
+    decode_window, topk_select, f64_to_fp8_e4m3, fp8_e4m3_to_f64, full_causal,
     merge_partials, mla_cache_bytes, quantize_fp8, to_f64, window_range,
 )

@@ -35,6 +35,14 @@ What it computes, and where the pages say so:
   per tensor (keys, values); a stored number is code value x scale, and a
   new row is quantised as x * (1 / scale) in float32, rounded to nearest
   even and saturated to +-448.
+* Podcast transcript, DeepSeek Sparse Attention passage, and the "A
+  Hundred Messages" blog's hierarchical-indexer passage: an indexer scores
+  the visible prefix and a top-k subset of positions is kept (k = 2048); a
+  deeper indexer picks its own top-k only among the positions of a candidate
+  pool of 8-position blocks.  Reading (the pages give no tie rule): the k
+  highest scores, equal scores ordered by lower position first; the kept
+  positions are returned in ascending order (the order the sparse decode
+  reads them), padded with -1 when fewer than k positions exist.
 * "KV cache" guide, "The allocator, not the algorithm": instead of one
   contiguous reservation per sequence at its maximum length, the cache is
   cut into fixed-size blocks of beta positions held in a shared pool, and a
@@ -179,6 +187,34 @@ def decode(q, k_cache, v_cache, seq_lens, scale: float):
             for i in range(j * G, (j + 1) * G):
                 o[b, i], lse[b, i] = _attend(to_f64(q[b, i]), K, V, scale)
     return o, lse
+
+
+# --------------------------------------------------------------------------
+# top-k selection from indexer scores (DSA; hierarchical indexer pool)
+# --------------------------------------------------------------------------
+def topk_select(scores, seq_lens, K: int, pool=None, pool_block: int = 8):
+    """Indices of the K highest scores among positions [0, seq_lens[b]) of
+    each row scores[b, j, :], equal scores by lower position, returned in
+    ascending position order and padded with -1.
+
+    scores: [B, n_idx, L_max] float32.  pool (optional): [B, n_idx, P] int32
+    block ids (-1 = unused); then only positions t < seq_lens[b] with
+    t // pool_block in the row's pool are candidates.
+    Returns int32 [B, n_idx, K]."""
+    B, R, L = scores.shape
+    out = np.full((B, R, K), -1, dtype=np.int32)
+    for b in range(B):
+        n = min(max(int(seq_lens[b]), 0), L)
+        for j in range(R):
+            if pool is None:
+                cand = range(n)
+            else:
+                blocks = {int(x) for x in pool[b, j] if x >= 0}
+                cand = [t for t in range(n) if t // pool_block in blocks]
+            ranked = sorted(cand, key=lambda t: (-float(scores[b, j, t]), t))[:K]
+            ranked.sort()
+            out[b, j, :len(ranked)] = ranked
+    return out
 
 
 # --------------------------------------------------------------------------

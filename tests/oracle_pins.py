@@ -668,6 +668,61 @@ def pin_paged(orc):
     assert not kp.any() and not vp.any()
 
 
+# ------------------------------------------------------------ top-k select
+def _heap_topk(scores_row, cand, K):
+    """Independent selection: heapq.nlargest on (score, -position), then
+    ascending positions."""
+    import heapq
+    best = heapq.nlargest(K, ((float(scores_row[t]), -t) for t in cand))
+    return sorted(-t for _, t in best)
+
+
+def pin_topk_select(orc):
+    """DSA keeps the k = 2048 highest-scoring positions; the hierarchical
+    indexer's pool is 2048 blocks of 8 positions (16,384 candidates) and its
+    top-512 comes only from the pool.  Checked against an independent heap
+    selection, ties (lower position first), a known permutation, short
+    sequences (-1 padding) and the pool restriction."""
+    g = golden()
+    assert g["dsa_topk"]["k"] == 2048
+    hp = g["hierarchical_indexer_pool"]
+    assert hp["pool_blocks"] * hp["block_positions"] == hp["candidates"]
+    rng = np.random.default_rng(41)
+    B, R, L = 2, 3, 700
+    sc = rng.standard_normal((B, R, L)).astype(np.float32)
+    sc[0, 1, 100:400] = 0.5                      # a run of ties
+    sl = np.array([700, 333], np.int32)
+    K = 64
+    got = orc.topk_select(sc, sl, K)
+    for b in range(B):
+        for j in range(R):
+            want = _heap_topk(sc[b, j], range(int(sl[b])), K)
+            assert got[b, j].tolist() == want, (b, j)
+    # all equal: the first K positions
+    eq = np.zeros((1, 1, 50), np.float32)
+    assert orc.topk_select(eq, np.array([50]), 7)[0, 0].tolist() == list(range(7))
+    # a permutation of 0..n-1 as scores: the top K are where n-K..n-1 sit
+    perm = rng.permutation(300)
+    ps = perm.astype(np.float32)[None, None]
+    want = sorted(np.nonzero(perm >= 300 - 20)[0].tolist())
+    assert orc.topk_select(ps, np.array([300]), 20)[0, 0].tolist() == want
+    # fewer positions than K: all of them, then -1
+    short = orc.topk_select(sc[:1, :1], np.array([5], np.int32), 8)[0, 0].tolist()
+    assert short == [0, 1, 2, 3, 4, -1, -1, -1]
+    # pool of 8-position blocks: candidates only from the listed blocks
+    pool = np.full((B, R, 16), -1, np.int32)
+    for b in range(B):
+        for j in range(R):
+            pool[b, j, :10] = rng.choice(L // 8, 10, replace=False)
+    gp = orc.topk_select(sc, sl, 32, pool=pool, pool_block=hp["block_positions"])
+    for b in range(B):
+        for j in range(R):
+            blocks = set(pool[b, j, :10].tolist())
+            cand = [t for t in range(int(sl[b])) if t // 8 in blocks]
+            want = _heap_topk(sc[b, j], cand, 32)
+            assert gp[b, j, :len(want)].tolist() == want and (gp[b, j, len(want):] == -1).all()
+
+
 ALL_PINS = [
     pin_size_llama2, pin_size_matches_storage, pin_causal_equals_recompute,
     pin_full_causal_bruteforce, pin_decode_bruteforce, pin_single_position,
@@ -676,5 +731,5 @@ ALL_PINS = [
     pin_split_merge, pin_gqa_head_mapping, pin_mla_reduces_to_dense,
     pin_mla_rope_matters, pin_topk, pin_append, pin_bf16_decoding,
     pin_fp8_page_max, pin_fp8_codes, pin_fp8_roundtrip, pin_fp8_rounding,
-    pin_fp8_quantize_scale, pin_fp8_decode, pin_window, pin_paged,
+    pin_fp8_quantize_scale, pin_fp8_decode, pin_window, pin_paged, pin_topk_select,
 ]

@@ -319,6 +319,33 @@ def mutants():
     m = _copy()
     m.append_paged = append_paged_slot_plus_one
     out["append_paged_wrong_slot"] = m
+
+    # top-k selection
+    def select_variant(kind):
+        def topk_select(scores, seq_lens, K, pool=None, pool_block=8):
+            B, R, L = scores.shape
+            out = np.full((B, R, K), -1, dtype=np.int32)
+            for b in range(B):
+                n = min(max(int(seq_lens[b]), 0), L)
+                for j in range(R):
+                    if pool is None or kind == "ignores_pool":
+                        cand = range(n)
+                    else:
+                        blocks = {int(x) for x in pool[b, j] if x >= 0}
+                        shift = 1 if kind == "pool_block_off_by_one" else 0
+                        cand = [t for t in range(n) if t // pool_block + shift in blocks]
+                    tie = (lambda t: -t) if kind == "ties_high" else (lambda t: t)
+                    ranked = sorted(cand, key=lambda t: (-float(scores[b, j, t]), tie(t)))
+                    ranked = ranked[:K - 1] if kind == "one_short" else ranked[:K]
+                    if kind != "score_order":
+                        ranked.sort()
+                    out[b, j, :len(ranked)] = ranked
+            return out
+        return topk_select
+    for kind in ("ties_high", "one_short", "score_order", "ignores_pool", "pool_block_off_by_one"):
+        m = _copy()
+        m.topk_select = select_variant(kind)
+        out["topk_select_" + kind] = m
     return out
 
 
