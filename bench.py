@@ -18,7 +18,8 @@ alone, timed with HIP events over back-to-back launches of one step's
 layers.  `also` carries the same figures for the GQA, MLA and top-k
 workloads, for the GQA workload over FP8 E4M3 caches (C3F8) and for the GQA
 workload attending a sliding window of its newest 128 positions (C3W128) and
-over a paged cache of 16-position blocks (C3P16).  `cpu_baseline` is the fp64 oracle on the same inputs (copied to
+over a paged cache of 16-position blocks (C3P16), and for the top-k
+selection that feeds the sparse workload (C5S).  `cpu_baseline` is the fp64 oracle on the same inputs (copied to
 the host), on a time-bounded sample of layer-steps.
 """
 from __future__ import annotations
@@ -47,8 +48,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="C2", choices=["C2", "C3", "C4", "C5", "C3F8", "C3W128", "C3P16"])
-    ap.add_argument("--others", default="C3,C4,C5,C3F8,C3W128,C3P16",
+    ap.add_argument("--config", default="C2", choices=["C2", "C3", "C4", "C5", "C3F8", "C3W128", "C3P16", "C5S"])
+    ap.add_argument("--others", default="C3,C4,C5,C3F8,C3W128,C3P16,C5S",
                     help="also-measured workloads (comma list; 'none' for none)")
     ap.add_argument("--kernel-reps", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true")
@@ -503,10 +504,58 @@ class PagedWorkload:
                 f"({self.nbuf} distinct pools)")
 
 
+class SelectWorkload:
+    """Top-k selection for the sparse workload's shape: per sequence and KV
+    head, the 2048 highest of 131072 indexer scores (float32, seeded N(0,1)),
+    32 index sets over 16 distinct score buffers (512 MB)."""
+
+    kernel = "topk_select_kernel"
+    kernel_appends = False
+    NBUF = 16
+
+    def __init__(self, cfg, slack, torch, kvc):
+        self.cfg, self.torch, self.kvc = cfg, torch, kvc
+        B, R, L = cfg.B, cfg.n_kv, cfg.pre_len
+        self.layers = cfg.index_sets
+        self.S = []
+        for i in range(self.NBUF):
+            g = torch.Generator(device="cuda")
+            g.manual_seed(syn.device_seed(cfg.cfg_id, 100 + i, "idx"))
+            self.S.append(torch.randn(B, R, L, generator=g, device="cuda", dtype=torch.float32))
+        self.lens = torch.full((B,), L, dtype=torch.int32, device="cuda")
+        self.out = [torch.empty(B, R, cfg.K, dtype=torch.int32, device="cuda")
+                    for _ in range(self.layers)]
+
+    def step(self):
+        for l in range(self.layers):
+            self.kvc.kvc_topk_select(self.S[l % self.NBUF], self.lens, self.out[l])
+
+    decode_only = step
+    kernel_only = step
+
+    def lens_after(self, steps_done):
+        return np.full(self.cfg.B, self.cfg.pre_len)
+
+    def kernel_bytes(self, n=None):
+        c = self.cfg
+        return int(c.B * c.n_kv * (c.pre_len * 4 + c.K * 4) + 4 * c.B)
+
+    def launch_bytes(self, steps_done):
+        return self.kernel_bytes()
+
+    def step_bytes(self, steps_done):
+        return self.kernel_bytes() * self.layers
+
+    def describe(self):
+        c = self.cfg
+        return (f"top-k selection: B={c.B} x {c.n_kv} rows, K={c.K} of {c.pre_len} float32 scores, "
+                f"{self.layers} index sets over {self.NBUF} score buffers")
+
+
 WORKLOADS = {"C2": (syn.C2, DenseWorkload), "C3": (syn.C3, DenseWorkload),
              "C4": (syn.C4, MlaWorkload), "C5": (syn.C5, TopKWorkload),
              "C3F8": (syn.C3, Fp8DenseWorkload), "C3W128": (syn.C3, WindowWorkload),
-             "C3P16": (syn.C3, PagedWorkload)}
+             "C3P16": (syn.C3, PagedWorkload), "C5S": (syn.C5, SelectWorkload)}
 
 
 # ---------------------------------------------------------------- timing

@@ -288,6 +288,29 @@ int kvc_decode_attn_topk(const void* q, const void* k_cache,
                          float scale, int dtype, int32_t* flag,
                          void* workspace, size_t ws_bytes, void* stream);
 
+/*
+ * kvc_topk_select - which positions the sparse decode reads.  (Podcast
+ * transcript, DeepSeek Sparse Attention passage: an indexer scores the
+ * prefix and keeps a top-k subset, k = 2048 in the released code; "A Hundred
+ * Messages" blog, section 4: a deeper indexer picks its top-512 only from a
+ * candidate pool of 8-position blocks, at most 2,048 of them.)
+ *
+ * For each row r = (b, j) of scores [B, R, L_max] float32: the K positions
+ * t < clamp(seq_lens[b], 0, L_max) with the highest scores, equal scores
+ * taken by lower position first, written to idx_out[b, j, :] in ascending
+ * position order (the layout kvc_decode_attn_topk reads); if fewer than K
+ * positions qualify, the rest of the row is -1.  With pool != NULL
+ * ([B, R, P] int32 block ids), only positions t with t / pool_block among
+ * the row's pool entries qualify (entries outside [0, ceil(L_max /
+ * pool_block)) are ignored).  Scores are compared exactly (-0 equals +0);
+ * NaN scores are outside the contract.  The result is deterministic.
+ *   K >= 1; pool mode: P >= 1, pool_block >= 1, ceil(L_max / pool_block)
+ *   <= 393216 (else KVC_ERR_UNSUPPORTED).
+ */
+int kvc_topk_select(const float* scores, const int32_t* seq_lens, const int32_t* pool,
+                    int P, int pool_block, int32_t* idx_out, int B, int R, int L_max,
+                    int K, void* stream);
+
 /* Text for a status code (static storage). */
 const char* kvc_status_string(int status);
 

@@ -509,6 +509,27 @@ int kvc_decode_attn_mla(const void* q, const void* ckv,
   return launch_status(launch_mla(p, static_cast<hipStream_t>(stream)));
 }
 
+int kvc_topk_select(const float* scores, const int32_t* seq_lens, const int32_t* pool,
+                    int P, int pool_block, int32_t* idx_out, int B, int R, int L_max,
+                    int K, void* stream) {
+  if (B < 0 || R < 1 || L_max < 1 || K < 1) return KVC_ERR_BAD_SHAPE;
+  int words = 0;
+  if (pool) {
+    if (P < 1 || pool_block < 1) return KVC_ERR_BAD_SHAPE;
+    const int64_t nblk = ((int64_t)L_max + pool_block - 1) / pool_block;
+    words = (int)((nblk + 31) / 32);
+    if (words > kSelectPoolWords) return KVC_ERR_UNSUPPORTED;
+  }
+  if (!scores || !seq_lens || !idx_out) return KVC_ERR_NULL_PTR;
+  if (!aligned(scores, 4) || !aligned(seq_lens, 4) || !aligned(idx_out, 4) ||
+      (pool && !aligned(pool, 4)))
+    return KVC_ERR_MISALIGNED;
+  if (B == 0) return KVC_OK;
+  SelectParams p{scores, seq_lens, pool, idx_out, B, R, L_max, K, pool ? P : 0,
+                 pool ? pool_block : 1, words};
+  return launch_status(launch_topk_select(p, static_cast<hipStream_t>(stream)));
+}
+
 size_t kvc_stream_read_sink_floats(size_t bytes) { return stream_read_blocks(bytes); }
 
 int kvc_stream_read(const void* src, size_t bytes, float* sink, void* stream) {

@@ -76,6 +76,17 @@ struct DenseParams {
   int max_blocks, num_blocks, page_shift;
 };
 
+// Pool bitmap words the selection kernel holds in LDS (one bit per block).
+constexpr int kSelectPoolWords = 12288;
+
+struct SelectParams {
+  const float* scores;      // [B, R, L_max]
+  const int32_t* seq_lens;  // [B]
+  const int32_t* pool;      // [B, R, P] block ids, or null
+  int32_t* out;             // [B, R, K]
+  int B, R, L_max, K, P, pool_block, pool_words;
+};
+
 struct MlaParams {
   const void* q;
   const void* ckv;
@@ -152,6 +163,7 @@ hipError_t launch_dense_mfma(const DenseParams& p, bool topk, bool append, hipSt
 hipError_t launch_dense_generic(const DenseParams& p, int dtype, bool topk,
                                 bool append, hipStream_t s);
 hipError_t launch_mla(const MlaParams& p, hipStream_t s);
+hipError_t launch_topk_select(const SelectParams& p, hipStream_t s);
 hipError_t launch_stream_read(const void* src, size_t bytes, float* sink,
                               hipStream_t s);
 hipError_t launch_copy(void* dst, const void* src, size_t bytes,

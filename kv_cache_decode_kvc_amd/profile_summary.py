@@ -33,6 +33,7 @@ DOMINANT = {
     "C3F8": "dense_mfma_kernel<false, false, true>",
     "C3W128": "dense_mfma_kernel<false, false, false>",
     "C3P16": "dense_mfma_kernel<false, false, false, true>",
+    "C5S": "topk_select_kernel",
 }
 
 

@@ -284,3 +284,21 @@ def test_paged_validation(L):
     assert L.kvc_decode_attn_paged_workspace_size(32, 64, 8, 2048, 16, 128, kvc.KVC_BF16) == \
         L.kvc_decode_attn_workspace_size(32, 64, 8, 32768, 128, kvc.KVC_BF16)
     assert L.kvc_decode_attn_paged_workspace_size(32, 64, 8, 2048, 12, 128, kvc.KVC_BF16) == 0
+
+
+def test_select_validation(L):
+    def sel(**kw):
+        a = dict(s=A4, sl=A4, pool=NULL, P=0, pb=8, out=A4, B=2, R=8, L=131072, K=2048,
+                 stream=NULL)
+        a.update(kw)
+        return L.kvc_topk_select(a["s"], a["sl"], a["pool"], a["P"], a["pb"], a["out"], a["B"],
+                                 a["R"], a["L"], a["K"], a["stream"])
+    assert sel(s=NULL) == -1
+    assert sel(out=NULL) == -1
+    assert sel(K=0) == -2
+    assert sel(R=0) == -2
+    assert sel(pool=A4, P=0) == -2
+    assert sel(pool=A4, P=16, pb=0) == -2
+    assert sel(pool=A4, P=16, pb=1, L=1 << 20) == -4     # pool bitmap beyond LDS
+    assert sel(s=ctypes.c_void_p(0x10002)) == -6
+    assert sel(B=0) == 0

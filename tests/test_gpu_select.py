@@ -1,0 +1,117 @@
+"""Top-k selection from indexer scores: HIP path vs the oracle, bit for bit.
+
+The selected positions (ascending, -1 padded) must equal the oracle's for
+random scores, heavy ties (lower position first), signed zeros, short rows,
+the pool-restricted variant, and at the sparse workload's full size on
+sampled rows.  Selection followed by the sparse decode matches the oracle's
+decode over the same positions.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+
+import kvc_synth as syn
+import oracle
+from gpu_helpers import compare, dev, host, host_f64
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+import kv_cache_decode_kvc_amd as kvc  # noqa: E402
+
+
+@pytest.fixture(autouse=True)
+def _gpu_only():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU (run with -m 'not gpu' elsewhere)")
+    yield
+    torch.cuda.synchronize()
+
+
+def run_select(scores, lens, K, pool=None, pool_block=8):
+    B, R, L = scores.shape
+    out = torch.full((B, R, K), 12345, dtype=torch.int32, device="cuda")
+    kvc.kvc_topk_select(dev(scores), dev(np.asarray(lens, np.int32)), out,
+                        pool=None if pool is None else dev(pool), pool_block=pool_block)
+    torch.cuda.synchronize()
+    return host(out)
+
+
+@pytest.mark.parametrize("kind", ["normal", "ties", "zeros", "short"])
+def test_select_matches_oracle(kind):
+    rng = np.random.default_rng({"normal": 1, "ties": 2, "zeros": 3, "short": 4}[kind])
+    B, R, L, K = 3, 4, 5000, 256
+    sc = rng.standard_normal((B, R, L)).astype(np.float32)
+    lens = [5000, 4097, 1]
+    if kind == "ties":
+        sc = rng.integers(0, 4, size=(B, R, L)).astype(np.float32)
+    elif kind == "zeros":
+        sc = np.where(rng.random((B, R, L)) < 0.5, np.float32(0.0), np.float32(-0.0)).astype(np.float32)
+        sc[:, :, ::7] = 1.0
+    elif kind == "short":
+        lens = [0, 100, 255]
+    got = run_select(sc, lens, K)
+    want = oracle.topk_select(sc, np.asarray(lens), K)
+    assert np.array_equal(got, want), np.argwhere(got != want)[:5]
+
+
+def test_select_pool_variant():
+    rng = np.random.default_rng(5)
+    B, R, L, K, blk = 2, 3, 20000, 512, 8
+    sc = rng.standard_normal((B, R, L)).astype(np.float32)
+    pool = np.full((B, R, 300), -1, np.int32)
+    for b in range(B):
+        for j in range(R):
+            pool[b, j, :250] = rng.choice(L // blk, 250, replace=False)
+    pool[0, 0, 250:260] = [10 ** 7, -3, 5, 5, 5, 7, 99999, 0, 0, 1]   # out of range and repeats
+    lens = [20000, 15000]
+    got = run_select(sc, lens, K, pool=pool, pool_block=blk)
+    want = oracle.topk_select(sc, np.asarray(lens), K, pool=pool, pool_block=blk)
+    assert np.array_equal(got, want)
+
+
+def test_select_fullsize_sampled_rows():
+    """The sparse workload's shape: 8 sequences x 8 KV heads, 2048 of 131072."""
+    c = syn.C5
+    B, R, L, K = c.B, c.n_kv, c.pre_len, c.K
+    g = torch.Generator(device="cuda")
+    g.manual_seed(syn.device_seed(c.cfg_id, 0, "idx"))
+    scores = torch.randn(B, R, L, generator=g, device="cuda", dtype=torch.float32)
+    out = torch.empty(B, R, K, dtype=torch.int32, device="cuda")
+    lens = torch.full((B,), L, dtype=torch.int32, device="cuda")
+    kvc.kvc_topk_select(scores, lens, out)
+    torch.cuda.synchronize()
+    got = host(out)
+    for b, j in [(0, 0), (3, 5), (7, 7)]:
+        row = host(scores[b:b + 1, j:j + 1])
+        want = oracle.topk_select(row, np.array([L]), K)
+        assert np.array_equal(got[b, j], want[0, 0]), (b, j)
+
+
+def test_select_then_sparse_decode():
+    """Selection feeding the sparse decode equals the oracle's decode over
+    the oracle's selection."""
+    rng = np.random.default_rng(6)
+    B, n_h, n_kv, d, L, K = 2, 32, 4, 128, 3000, 300
+    lens = [3000, 1200]
+    case = syn.dense_case(B, n_h, n_kv, d, L, lens, "bf16", cfg_id=140)
+    sc = rng.standard_normal((B, n_kv, L)).astype(np.float32)
+    idx = torch.empty(B, n_kv, K, dtype=torch.int32, device="cuda")
+    sl = dev(np.asarray(lens, np.int32))
+    kvc.kvc_topk_select(dev(sc), sl, idx)
+    q = dev(case["q"])
+    out = torch.empty_like(q)
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ws = kvc.workspace(kvc.kvc_decode_attn_topk_workspace_size(B, n_h, n_kv, K, d, 1))
+    kvc.kvc_decode_attn_topk(q, dev(case["k_cache"]), dev(case["v_cache"]), sl, idx, out,
+                             flag=flag, workspace=ws)
+    torch.cuda.synchronize()
+    sel = oracle.topk_select(sc, np.asarray(lens), K)
+    assert np.array_equal(host(idx), sel)
+    o_ref, _, f_ref = oracle.decode_topk(case["q"], case["k_cache"], case["v_cache"],
+                                        np.asarray(lens, np.int32), sel, 1 / math.sqrt(d))
+    assert f_ref == 0 == int(host(flag)[0])
+    compare(host_f64(out), o_ref, 2e-2, "select + sparse decode")
