@@ -61,7 +61,7 @@ class DenseWorkload:
     """MHA/GQA layers over [B, n_kv, L_max, d] caches (C2, C3).  Each layer
     runs the fused append-and-attend call (one kernel per layer-step)."""
 
-    kernel = "dense_mfma_kernel<false, true, false> (append + attend)"
+    kernel = "dense_mfma_kernel<false, true, false, false> (append + attend)"
     kernel_appends = True
 
     def __init__(self, cfg, slack, torch, kvc):
@@ -157,7 +157,7 @@ class DenseWorkload:
 class MlaWorkload:
     """Latent-cache layers, [B, L_max, 576] per layer buffer (C4)."""
 
-    kernel = "mla_kernel"
+    kernel = "mla_kernel + mla_merge_kernel"
     kernel_appends = False
 
     def __init__(self, cfg, slack, torch, kvc):
@@ -220,7 +220,7 @@ class MlaWorkload:
 class TopKWorkload:
     """Top-k sparse GQA over [B, n_kv, L_max, d] caches (C5)."""
 
-    kernel = "dense_mfma_kernel<true, false, false> (top-k)"
+    kernel = "dense_mfma_kernel<true, false, false, false> (top-k)"
     kernel_appends = False
 
     def __init__(self, cfg, slack, torch, kvc):
@@ -287,7 +287,7 @@ class Fp8DenseWorkload:
     one float32 scale per tensor).  A layer-step is kvc_append_fp8 then
     kvc_decode_attn_fp8."""
 
-    kernel = "dense_mfma_kernel<false, false, true> (fp8 E4M3 cache)"
+    kernel = "dense_mfma_kernel<false, false, true, false> (fp8 E4M3 cache)"
     kernel_appends = False
     K_SCALE = 1.0 / 64      # N(0,1) / (1/64) stays within +-448
     V_SCALE = 1.0 / 64
@@ -375,7 +375,7 @@ class WindowWorkload(DenseWorkload):
     DeepSeek article's n_win = 128).  A layer-step is kvc_append then
     kvc_decode_attn_window."""
 
-    kernel = "dense_mfma_kernel<false, false, false> (window 128)"
+    kernel = "dense_mfma_kernel<false, false, false, false> (window 128)"
     kernel_appends = False
     WINDOW = 128
 
