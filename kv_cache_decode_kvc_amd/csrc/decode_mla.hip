@@ -13,7 +13,8 @@
 // n_h is not a multiple of 128) of one (sequence, split): every compute unit
 // streams rows no other compute unit reads.  Each wave owns 32 heads with the
 // full row (no exchange between waves) and runs alone on its SIMD with the
-// whole register file: 256 accumulators, 144 query registers.
+// whole register file: 256 accumulators, 144 query registers (the whole
+// 576-wide query of its 32 heads stays in registers).
 //
 // Per wave (lane l: r = l % 32, g = l / 32) and 32-position chunk, with
 // v_mfma_f32_32x32x16_bf16:
@@ -24,20 +25,28 @@
 //          16(i / 8) + 8g + i % 8, i.e. the B operand of the value product.
 //  weights softmax numerators 2^(s - m_ref) in log2 units against a fixed
 //          per-head reference (see the pass loop below).
-//  values  O^T[c][h] += C^T[c][t] P^T[t][h]: 16 column tiles x 2 k-steps;
-//          lane (r, g) reads rows 16 s + 8g + 0..7 x 16 B at columns
-//          256cb + 8r and transposes 8 x 8 bf16 in registers (v_perm), so
-//          tile (cb, m) row r is column 256cb + 8r + m.  (The transposing LDS
-//          read has no alias information for the compiler, which then waits
-//          for every tile copy in flight before it; plain reads do not.)
+//  values  O^T[c][h] += C^T[c][t] P^T[t][h]: 16 column tiles x 2 k-steps.
+//          The A operand (8 positions of one column per lane) is read from
+//          LDS already transposed by ds_read_b64_tr_b16 (in each 16-lane
+//          group, lane i receives element i % 4 of the 8-byte pieces
+//          addressed by lanes i / 4, 4 + i / 4, 8 + i / 4, 12 + i / 4), two
+//          reads per MFMA.  The addressing makes row m of tile ct column
+//          32ct + 16((m / 4) % 2) + 4(m / 8) + m % 4, so accumulator k of lane
+//          (r, g) holds head r at column 32ct + 16g + k: 16 consecutive
+//          columns per lane and tile.  These reads are issued from inline
+//          assembly with explicit LDS counter waits: through the builtin the
+//          compiler, lacking alias information, would wait for every tile
+//          copy in flight before each of them.
 //
-// Latent tiles go HBM -> LDS directly (buffer_load ... lds), three stages (two
-// tiles in flight while one is read), with 16-byte piece k of row rho stored
+// Latent tiles go HBM -> LDS directly (buffer_load ... lds), four stages
+// (three tiles in flight while one is read), with 16-byte piece k of row rho stored
 // at k ^ key(rho), key = bit-reverse of (rho >> 1) & 7: conflict-free for
 // the 16-byte score and value reads on the 64-bank LDS.  Rows at or past the sequence length read as zeros (buffer range
 // check) and are masked.  Splits of one sequence publish normalised partials
 // and a second kernel, spread over every compute unit, merges them by
 // log-sum-exp.
+
+#include <utility>
 
 #include "kvc_device.h"
 #include "kvc_internal.h"
@@ -49,12 +58,13 @@ namespace {
 constexpr int kD = kMlaDc + kMlaDr;          // 576
 constexpr int kRowB = kD * 2;                // 1152 bytes per row
 constexpr int kTileB = kMlaChunk * kRowB;    // 36864 bytes per chunk
-constexpr int kStages = 3;
+constexpr int kStages = 4;
 constexpr int kKSteps = kD / 16;             // 36
 constexpr int kColTiles = kMlaDc / 32;       // 16
-// The last kQPark query k-steps wait in LDS (per wave and lane, 1 KB per
-// k-step), which keeps the wave within the register file.
-constexpr int kQPark = 12;
+// The last kQPark query k-steps may wait in LDS (per wave and lane, 1 KB per
+// k-step) if the wave would not fit the register file; the four stages leave
+// room for at most 3.
+constexpr int kQPark = 0;
 constexpr int kQRegs = kKSteps - kQPark;
 constexpr size_t kParkOff = (size_t)kStages * kTileB;
 constexpr size_t kMlaLds = kParkOff + 4 * kQPark * 1024;
@@ -64,6 +74,13 @@ constexpr float kMlaRefMargin = 64.0f;
 // LDS reads in flight ahead of the MFMA that consumes them (hides the LDS
 // latency behind earlier MFMAs of the same wave).
 constexpr int kQkAhead = 4;
+// Value product: 32 MFMAs per chunk (k-step J / 16, column tile J % 16); the
+// two transposed reads of each are issued kPvAhead MFMAs ahead into one of
+// kPvBuf register pairs (one more than in flight, so a read never targets
+// the registers of the MFMA issued just before it).
+constexpr int kPvSteps = 2 * kColTiles;
+constexpr int kPvAhead = 4;
+constexpr int kPvBuf = kPvAhead + 1;
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -147,6 +164,51 @@ __device__ inline bool any_vote4(u32x4 v) {
   return x != 0;
 }
 
+// Transposed reads of value MFMA J: tile ct = J % 16, k-step J / 16 (16 rows
+// further), bases tb[half][ct % 2] plus 128 (ct / 2) bytes.
+template <int J>
+__device__ __forceinline__ void pv_issue(u32x2 (&lo)[kPvBuf], u32x2 (&hi)[kPvBuf],
+                                         const uint32_t (&tb)[2][2]) {
+  constexpr int ct = J % kColTiles;
+  constexpr int off = (J / kColTiles) * 16 * kRowB + 128 * (ct >> 1);
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
+               : "=v"(lo[J % kPvBuf]) : "v"(tb[0][ct & 1]), "n"(off));
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
+               : "=v"(hi[J % kPvBuf]) : "v"(tb[1][ct & 1]), "n"(off));
+}
+
+// Value MFMA J: wait until its two reads have landed (LDS operations complete
+// in order, so at most the reads issued after them may still be pending;
+// the wait is tied to the registers so the MFMA cannot move above it), then
+// accumulate and issue the reads kPvAhead MFMAs ahead.
+template <int J>
+__device__ __forceinline__ void pv_step(f32x16 (&acc)[kColTiles], const bf16x8 (&pop)[2],
+                                        u32x2 (&lo)[kPvBuf], u32x2 (&hi)[kPvBuf],
+                                        const uint32_t (&tb)[2][2]) {
+  constexpr int later = (kPvSteps - 1 - J) < (kPvAhead - 1) ? (kPvSteps - 1 - J) : (kPvAhead - 1);
+  asm volatile("s_waitcnt lgkmcnt(%2)"
+               : "+v"(lo[J % kPvBuf]), "+v"(hi[J % kPvBuf]) : "n"(2 * later));
+  const u32x4 a = {lo[J % kPvBuf][0], lo[J % kPvBuf][1], hi[J % kPvBuf][0], hi[J % kPvBuf][1]};
+  acc[J % kColTiles] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+      as_bf16x8(a), pop[J / kColTiles], acc[J % kColTiles], 0, 0, 0);
+  if constexpr (J + kPvAhead < kPvSteps) pv_issue<J + kPvAhead>(lo, hi, tb);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int... Js>
+__device__ __forceinline__ void pv_head(std::integer_sequence<int, Js...>, u32x2 (&lo)[kPvBuf],
+                                        u32x2 (&hi)[kPvBuf], const uint32_t (&tb)[2][2]) {
+  (pv_issue<Js>(lo, hi, tb), ...);
+}
+
+template <int... Js>
+__device__ __forceinline__ void pv_all(std::integer_sequence<int, Js...>,
+                                       f32x16 (&acc)[kColTiles], const bf16x8 (&pop)[2],
+                                       u32x2 (&lo)[kPvBuf], u32x2 (&hi)[kPvBuf],
+                                       const uint32_t (&tb)[2][2]) {
+  (pv_step<Js>(acc, pop, lo, hi, tb), ...);
+}
+
 }  // namespace
 
 template <int NW>
@@ -205,26 +267,38 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_kernel(MlaParams p) {
     for (int m = 0; m < 4; ++m)
       wqk[m] = (uint32_t)(row * kRowB + (((2 * m + g) ^ swz_key(row)) << 4));
   }
-  // Values, k-step s2, column block cb: lane (r, g) reads rows
-  // 16 s2 + 8g + jj (jj = 0..7), logical piece 32cb + r (columns
-  // 256cb + 8r .. +8), stored at 32cb + 8(r / 8) + ((r % 8) ^ key(row)).  The
-  // key depends on (g, jj / 2) only: base by jj / 2, plus (jj % 2) rows,
-  // 16 s2 rows and 512 cb.
-  uint32_t wpv[4];
+  // Values, k-step s2, half t, column tile ct: lane L = lane % 16 of 16-lane
+  // group q16 (g = q16 / 2) addresses row 16 s2 + 8g + 4t + L / 4, columns
+  // 32ct + 16(L % 2) + 8(q16 % 2) + 4((L / 2) % 2) .. +4, i.e. logical piece
+  // 4ct + 2(L % 2) + q16 % 2, half (L / 2) % 2.  The key does not depend on
+  // s2 and only flips piece bits 0..2: base by (t, ct % 2), plus 16 s2 rows
+  // and 128 (ct / 2) bytes.
+  // (the reads are issued from inline assembly, which takes the LDS byte
+  // address itself: the low 32 bits of the generic address of smem)
+  uint32_t wtr[2][2];
+  {
+    const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>(smem);
+    const int q16 = lane >> 4, L = lane & 15;
 #pragma unroll
-  for (int q4 = 0; q4 < 4; ++q4) {
-    const int row = 8 * g + 2 * q4;
-    wpv[q4] = (uint32_t)(row * kRowB + ((8 * (r >> 3) + ((r & 7) ^ swz_key(row))) << 4));
+    for (int t = 0; t < 2; ++t) {
+      const int row = 8 * g + 4 * t + (L >> 2);
+#pragma unroll
+      for (int cp = 0; cp < 2; ++cp)
+        wtr[t][cp] = lds0 + (uint32_t)(row * kRowB +
+                                (((4 * cp + 2 * (L & 1) + (q16 & 1)) ^ swz_key(row)) << 4) +
+                                8 * ((L >> 1) & 1));
+    }
   }
 
-  // The first tile copies go out before the query loads, so the two
-  // latencies overlap.
+  // The first tiles (one per stage) go out right after the query loads, so
+  // the two latencies overlap; the query loads come first so that waiting
+  // for a tile also covers them.
   auto issue_first = [&]() {
     issue_tile<kLpt>(smem, cr, start, blk0, lane);
-    if (nchunks > 1) issue_tile<kLpt>(smem + kTileB, cr, start + kMlaChunk, blk0, lane);
-    if (nchunks > 2) issue_tile<kLpt>(smem + 2 * kTileB, cr, start + 2 * kMlaChunk, blk0, lane);
+#pragma unroll
+    for (int k = 1; k < kStages; ++k)
+      if (nchunks > k) issue_tile<kLpt>(smem + k * kTileB, cr, start + k * kMlaChunk, blk0, lane);
   };
-  issue_first();
 
   bf16x8 qop[kQRegs];
   const uint32_t qpark = (uint32_t)(kParkOff + (wave * kQPark * 64 + lane) * 16);
@@ -238,6 +312,7 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_kernel(MlaParams p) {
       *reinterpret_cast<u32x4*>(smem + qpark + (k - kQRegs) * 1024) =
           *reinterpret_cast<const u32x4*>(qrow + k * 16 + g * 8);
   }
+  issue_first();
 
   // Scores of one chunk (stage offset toff).  The LDS reads run kQkAhead
   // k-steps ahead of the MFMAs; the scheduling barriers keep that order.
@@ -296,42 +371,42 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_kernel(MlaParams p) {
     l_run = 0.f;
     if (!first_pass) issue_first();
     first_pass = false;
-    // (tile k >= 3 is issued at the top of chunk k - 2, into the stage of
-    // chunk k - 3)
+    // (tile k >= 4 is issued during the scores of chunk k - 3, into the
+    // stage of chunk k - 4)
 
     float m_seen = m_ref;     // largest score of this head in this pass
     bool restart = false;
     for (int c = 0; c < nchunks; ++c) {
       const int cs = start + c * kMlaChunk;
-      // Tile c landed (tiles issued after it: c + 1, and c + 2 on the first
-      // chunk, may still be in flight); every wave is done with the stage of
-      // chunk c - 1 and has cast its vote on it.
-      if (c == 0 && nchunks > 2) wait_vmcnt<2 * kLpt>();
-      else if (c + 1 < nchunks) wait_vmcnt<kLpt>();
+      // Tile c landed (tiles issued after it: c + 1 and c + 2, and c + 3 on
+      // the first chunk, may still be in flight); every wave is done with the
+      // stage of chunk c - 1 and has cast its vote on it.
+      const int after = c == 0 ? min(kStages - 1, nchunks - 1) : min(kStages - 2, nchunks - 1 - c);
+      if (after >= 3) wait_vmcnt<3 * kLpt>();
+      else if (after == 2) wait_vmcnt<2 * kLpt>();
+      else if (after == 1) wait_vmcnt<kLpt>();
       else wait_vmcnt<0>();
       lds_barrier();
       // (the votes on chunk c - 1 are read here and tested after this
       // chunk's scores, so the read's latency hides behind the MFMAs)
       const u32x4 vw = *reinterpret_cast<const u32x4*>(s_vote[(c - 1) & 1]);
       const uint32_t toff = (uint32_t)((c % kStages) * kTileB);
-      const f32x16 S = scores(toff, c >= 1 && c + 2 < nchunks,
-                              smem + ((c + 2) % kStages) * kTileB, cs + 2 * kMlaChunk);
+      const f32x16 S = scores(toff, c >= 1 && c + kStages - 1 < nchunks,
+                              smem + ((c + kStages - 1) % kStages) * kTileB,
+                              cs + (kStages - 1) * kMlaChunk);
       if (c > 0 && !scan && !scanned && any_vote4<NW>(vw)) { restart = true; break; }
 
-      // value rows of the first column block, read ahead of the softmax
-      uint32_t pb[4];
+      // the first value MFMAs' reads go out ahead of the softmax
+      uint32_t tb[2][2];
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        pb[q4] = toff + wpv[q4];
-        asm volatile("" : "+v"(pb[q4]));
-      }
-      auto pv_read = [&](u32x4 (&vr)[8], int s2, int cb) {
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj)
-          vr[jj] = lds_load16(smem, pb[jj >> 1] + (jj & 1) * kRowB + s2 * 16 * kRowB + cb * 512);
-      };
-      u32x4 va[8], vb[8];
-      pv_read(va, 0, 0);
+        for (int cp = 0; cp < 2; ++cp) {
+          tb[t][cp] = toff + wtr[t][cp];
+          asm volatile("" : "+v"(tb[t][cp]));
+        }
+      u32x2 trlo[kPvBuf], trhi[kPvBuf];
+      pv_head(std::make_integer_sequence<int, kPvAhead>{}, trlo, trhi, tb);
 
       // weights of this lane's 16 positions of head r
       float sv[16];
@@ -381,34 +456,9 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_kernel(MlaParams p) {
       }
       l_run += psum;      // the rounded weights' sum (bf16 dot with ones)
 
-      // weighted sum of the latents of chunk c: per column block cb and
-      // k-step s2, 8 row reads (16 B each) and an 8 x 8 register transpose
-      // give the A operands of 8 MFMAs (tiles cb * 8 + m).  The reads of the
-      // next (s2, cb) group go out before the current group's MFMAs.
-      auto pv_mma = [&](const u32x4 (&vr)[8], int s2, int cb) {
-#pragma unroll
-        for (int m = 0; m < 8; ++m) {
-          const uint32_t sel = (m & 1) ? 0x07060302u : 0x05040100u;
-          const int dw = m >> 1;
-          u32x4 a;
-          a[0] = __builtin_amdgcn_perm(vr[1][dw], vr[0][dw], sel);
-          a[1] = __builtin_amdgcn_perm(vr[3][dw], vr[2][dw], sel);
-          a[2] = __builtin_amdgcn_perm(vr[5][dw], vr[4][dw], sel);
-          a[3] = __builtin_amdgcn_perm(vr[7][dw], vr[6][dw], sel);
-          acc[cb * 8 + m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), pop[s2],
-                                                                     acc[cb * 8 + m], 0, 0, 0);
-        }
-      };
-      pv_read(vb, 0, 1);
+      // weighted sum of the latents of chunk c
       __builtin_amdgcn_sched_barrier(0);
-      pv_mma(va, 0, 0);
-      pv_read(va, 1, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      pv_mma(vb, 0, 1);
-      pv_read(vb, 1, 1);
-      __builtin_amdgcn_sched_barrier(0);
-      pv_mma(va, 1, 0);
-      pv_mma(vb, 1, 1);
+      pv_all(std::make_integer_sequence<int, kPvSteps>{}, acc, pop, trlo, trhi, tb);
     }
     if (scan) {
       scan = false;
@@ -429,8 +479,8 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_kernel(MlaParams p) {
     lds_barrier();
   }
 
-  // This split's result for head h: lane (r, g) holds column
-  // 256cb + 8(8a + 4g + e) + m in acc[cb * 8 + m][4a + e].
+  // This split's result for head h: lane (r, g) holds column 32ct + 16g + k
+  // in acc[ct][k].
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const float lse2 = l_tot > 0.f ? m_ref + __log2f(l_tot) : kNegInf;
@@ -438,15 +488,14 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_kernel(MlaParams p) {
   if (nsplit == 1) {
     uint16_t* o = (uint16_t*)p.out + bh * kMlaDc;
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
+    for (int ct = 0; ct < kColTiles; ++ct)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int col = 256 * cb + 8 * (8 * (i >> 2) + 4 * g + (i & 3));
+      for (int hf = 0; hf < 2; ++hf) {
         u32x4 v;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          v[e] = pack_bf16x2(acc[cb * 8 + 2 * e][i] * inv, acc[cb * 8 + 2 * e + 1][i] * inv);
-        *reinterpret_cast<u32x4*>(o + col) = v;
+          v[e] = pack_bf16x2(acc[ct][8 * hf + 2 * e] * inv, acc[ct][8 * hf + 2 * e + 1] * inv);
+        *reinterpret_cast<u32x4*>(o + 32 * ct + 16 * g + 8 * hf) = v;
       }
     if (p.lse && g == 0) p.lse[bh] = lse2 * kLn2;
     return;
@@ -474,8 +523,8 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_kernel(MlaParams p) {
 }
 
 // Split merge: one workgroup (NW waves, the main kernel's lane layout) per
-// (sequence, head group, column block cb, quad q4).  Every lane combines the
-// same 8 slots (tiles cb*8 + m, quad q4) of all the splits' blocks by
+// (sequence, head group, tile pair tp).  Every lane combines the same 8 slots
+// (tiles 2tp and 2tp + 1, quads 0..3) of all the splits' blocks by
 // log-sum-exp weights, with the loads of up to 4 splits in flight together.
 // Sequences that needed one split (or none) were finished by the main kernel.
 // (Register budget for two waves per SIMD, so that all 32 slot loads of a
@@ -487,10 +536,9 @@ void mla_merge_kernel(MlaParams p) {
   constexpr size_t kBlock = (size_t)NW * 64 * 256;
   const int groups = p.n_h / kHpw;
   int id = blockIdx.x;
-  const int part = id & 7;
+  const int part = id & 7;    // tile pair: tiles 2 part, 2 part + 1
   id >>= 3;
   const int hg = id % groups, b = id / groups;
-  const int cb = part >> 2, q4 = part & 3;
   const int n = min(max(p.seq_lens[b], 0), p.L_max);
   const int nsplit = (n + p.S - 1) / p.S;
   if (nsplit <= 1) return;
@@ -529,7 +577,7 @@ void mla_merge_kernel(MlaParams p) {
       ls[u] = lse_p[(size_t)su * kHpw];
       const f32x4* blk = base + (size_t)su * (kBlock / 4);
 #pragma unroll
-      for (int m = 0; m < 8; ++m) v[u][m] = blk[(4 * (cb * 8 + m) + q4) * 64];
+      for (int m = 0; m < 8; ++m) v[u][m] = blk[(8 * part + m) * 64];
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -540,15 +588,19 @@ void mla_merge_kernel(MlaParams p) {
     }
   }
   const float zi = Z > 0.f ? 1.f / Z : 0.f;
-  // slot (cb*8 + m, q4) element e is column 256cb + 8(8 q4 + 4g + e) + m
+  // slot m = 4tt + q4 (tile 2 part + tt, quad q4) element e is column
+  // 32(2 part + tt) + 16g + 4q4 + e: eight consecutive columns per pair of
+  // slots
   uint16_t* orow = (uint16_t*)p.out + bh * kMlaDc;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
+  for (int j = 0; j < 4; ++j) {
     u32x4 o;
 #pragma unroll
-    for (int mm = 0; mm < 4; ++mm)
-      o[mm] = pack_bf16x2(sum[2 * mm][e] * zi, sum[2 * mm + 1][e] * zi);
-    *reinterpret_cast<u32x4*>(orow + 256 * cb + 8 * (8 * q4 + 4 * g + e)) = o;
+    for (int e = 0; e < 2; ++e) {
+      o[e] = pack_bf16x2(sum[2 * j][2 * e] * zi, sum[2 * j][2 * e + 1] * zi);
+      o[2 + e] = pack_bf16x2(sum[2 * j + 1][2 * e] * zi, sum[2 * j + 1][2 * e + 1] * zi);
+    }
+    *reinterpret_cast<u32x4*>(orow + 64 * part + 32 * (j >> 1) + 16 * g + 8 * (j & 1)) = o;
   }
   if (part == 0 && p.lse && g == 0) p.lse[bh] = Z > 0.f ? (M + __log2f(Z)) * kLn2 : kNegInf;
 }
