@@ -326,9 +326,11 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_kernel(MlaParams p) {
       qb[m] = toff + wqk[m];
       asm volatile("" : "+v"(qb[m]));
     }
+    // The scores accumulate in vector registers (the accumulation registers
+    // all hold the value product), so the chain is written as inline
+    // assembly with a VGPR accumulator: back-to-back accumulation into the
+    // same registers needs no wait states.
     f32x16 s;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) s[i] = 0.f;
     // A: latent rows; Bq: parked query k-steps (k >= kQRegs)
     u32x4 A[kQkAhead], Bq[kQkAhead];
 #pragma unroll
@@ -336,10 +338,15 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_kernel(MlaParams p) {
       A[k] = lds_load16(smem, qb[k & 3] + (k >> 2) * 128);
       if (k >= kQRegs) Bq[k] = lds_load16(smem, qpark + (k - kQRegs) * 1024);
     }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int k = 0; k < kKSteps; ++k) {
       const bf16x8 bop = k < kQRegs ? qop[k < kQRegs ? k : 0] : as_bf16x8(Bq[k % kQkAhead]);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(A[k % kQkAhead]), bop, s, 0, 0, 0);
+      const bf16x8 aop = as_bf16x8(A[k % kQkAhead]);
+      if (k == 0)
+        asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(s) : "v"(aop), "v"(bop));
+      else
+        asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(aop), "v"(bop));
       if (k % NW == 1 && dma) issue_block(dstage, cr, dcs, blk0 + k / NW, lane);
       const int kn = k + kQkAhead;
       if (kn < kKSteps) {
@@ -348,6 +355,9 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_kernel(MlaParams p) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    // vector ALU reads of the chain's result need 11 wait states after an
+    // 8-pass matrix instruction; give 21
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4" : "+v"(s));
     return s;
   };
 
