@@ -218,17 +218,19 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_kernel(MlaParams p) {
   constexpr int kHpw = 32 * NW;        // heads per workgroup
   constexpr int kLpt = 36 / NW;        // 1-KB blocks each wave copies per tile
 
-  // Block id -> (head group, unit = b * P_max + split).  Units are dealt to
-  // the 8 XCDs round-robin and every head group of a unit gets the same XCD.
+  // Block id -> (sequence b, split, head group).  Consecutive block ids go
+  // to the 8 XCDs in turn; every block of sequence b runs on XCD b % 8, so
+  // the splits of a sequence share one L2 (its query comes from HBM once,
+  // and the merge kernel finds the partials there).
   const int groups = p.n_h / kHpw;
-  const int units = p.B * p.P_max;
   int id = blockIdx.x;
   const int xcd = id & 7;
   id >>= 3;
   const int hg = id % groups;
-  const int u = (id / groups) * 8 + xcd;
-  if (u >= units) return;
-  const int b = u / p.P_max, split = u % p.P_max;
+  id /= groups;
+  const int split = id % p.P_max;
+  const int b = (id / p.P_max) * 8 + xcd;
+  if (b >= p.B) return;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -546,9 +548,13 @@ void mla_merge_kernel(MlaParams p) {
   constexpr size_t kBlock = (size_t)NW * 64 * 256;
   const int groups = p.n_h / kHpw;
   int id = blockIdx.x;
+  const int xcd = id & 7;     // sequence b runs on XCD b % 8, as in the main kernel
+  id >>= 3;
   const int part = id & 7;    // tile pair: tiles 2 part, 2 part + 1
   id >>= 3;
-  const int hg = id % groups, b = id / groups;
+  const int hg = id % groups;
+  const int b = (id / groups) * 8 + xcd;
+  if (b >= p.B) return;
   const int n = min(max(p.seq_lens[b], 0), p.L_max);
   const int nsplit = (n + p.S - 1) / p.S;
   if (nsplit <= 1) return;
@@ -618,8 +624,8 @@ void mla_merge_kernel(MlaParams p) {
 template <int NW>
 static hipError_t launch_mla_t(const MlaParams& p, hipStream_t s) {
   const int groups = p.n_h / (32 * NW);
-  const size_t units = (size_t)p.B * p.P_max;
-  const size_t blocks = (units + 7) / 8 * 8 * groups;
+  const size_t bq = ((size_t)p.B + 7) / 8;     // sequences per XCD
+  const size_t blocks = 8 * bq * p.P_max * groups;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)mla_kernel<NW>,
@@ -629,7 +635,7 @@ static hipError_t launch_mla_t(const MlaParams& p, hipStream_t s) {
   }
   hipLaunchKernelGGL(mla_kernel<NW>, dim3((unsigned)blocks), dim3(NW * 64), kMlaLds, s, p);
   if (p.P_max > 1)
-    hipLaunchKernelGGL(mla_merge_kernel<NW>, dim3((unsigned)((size_t)p.B * groups * 8)),
+    hipLaunchKernelGGL(mla_merge_kernel<NW>, dim3((unsigned)(8 * bq * groups * 8)),
                        dim3(NW * 64), 0, s, p);
   return hipGetLastError();
 }
