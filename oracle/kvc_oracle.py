@@ -35,6 +35,16 @@ What it computes, and where the pages say so:
   per tensor (keys, values); a stored number is code value x scale, and a
   new row is quantised as x * (1 / scale) in float32, rounded to nearest
   even and saturated to +-448.
+* Podcast transcript, the 890-byte passage, and the DeepSeek article's FP4
+  section: the main key/value cache may be FP4, E2M1 numbers with one E4M3
+  scale per 16 channels and no second-level global scale (the pages call
+  it MXFP4 but give these NVFP4-style parameters; the largest stored
+  magnitude, 448 x 6 = 2688, is the article's bound), dequantised before
+  attention.  Reading (no rounding rule is given): a block's scale is the
+  E4M3 value nearest float32(amax / 6), each number the E2M1 value nearest
+  float32(x / scale) with ties to the even code and saturation at 6, an
+  all-zero scale stores zero codes; two codes per byte, even channel in the
+  low nibble.
 * Podcast transcript, DeepSeek Sparse Attention passage, and the "A
   Hundred Messages" blog's hierarchical-indexer passage: an indexer scores
   the visible prefix and a top-k subset of positions is kept (k = 2048); a
@@ -514,6 +524,108 @@ def decode_fp8(q, k_cache8, v_cache8, seq_lens, scale: float, k_scale: float,
         for j in range(n_kv):
             K = fp8_e4m3_to_f64(k_cache8[b, j, :n]) * float(k_scale)
             V = fp8_e4m3_to_f64(v_cache8[b, j, :n]) * float(v_scale)
+            for i in range(j * G, (j + 1) * G):
+                o[b, i], lse[b, i] = _attend(to_f64(q[b, i]), K, V, scale)
+    return o, lse
+
+
+# --------------------------------------------------------------------------
+# FP4 block-scaled cache (DeepSeek article, FP4 section; podcast, the
+# 890-byte passage): E2M1 numbers, one E4M3 scale per 16 channels, no
+# second-level scale, dequantised before attention.  Reading of how a block
+# is encoded (the pages give the format, not the rounding): scale = E4M3 of
+# float32(amax / 6), every number float32(x / scale) rounded to the nearest
+# E2M1 value, ties to the even code, magnitudes past 6 saturating.
+# --------------------------------------------------------------------------
+FP4_E2M1_MAX = 6.0
+FP4_BLOCK = 16
+# E2M1 magnitudes of codes 0..7 (sign in bit 3): exponent bias 1, one
+# mantissa bit, code 1 subnormal.
+_E2M1_MAG = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
+
+
+def fp4_e2m1_to_f64(codes: np.ndarray) -> np.ndarray:
+    """4-bit E2M1 codes (0..15) -> float64, from the field definition:
+    sign bit 3, exponent bits 2..1 (bias 1), mantissa bit 0."""
+    c = np.asarray(codes).astype(np.int64) & 0xF
+    e = (c >> 1) & 3
+    m = c & 1
+    mag = np.where(e == 0, m * 0.5, (1.0 + 0.5 * m) * np.ldexp(1.0, e - 1))
+    return np.where(c & 8, -mag, mag)
+
+
+def f64_to_fp4_e2m1(q: np.ndarray) -> np.ndarray:
+    """Nearest E2M1 code, ties to the even code, |q| > 6 -> 6; the sign bit
+    copies the sign of q (also for zero).  Written as a search over the
+    eight magnitudes, like the E4M3 encoder."""
+    q = np.asarray(q, dtype=np.float64)
+    a = np.abs(q)
+    vals = np.asarray(_E2M1_MAG)
+    best = np.zeros(a.shape, dtype=np.int64)
+    for code in range(1, 8):
+        d_new = np.abs(a - vals[code])
+        d_best = np.abs(a - vals[best])
+        take = (d_new < d_best) | ((d_new == d_best) & (code % 2 == 0))
+        best = np.where(take, code, best)
+    best = np.where(a > FP4_E2M1_MAX, 7, best)
+    return (best | np.where(np.signbit(q), 8, 0)).astype(np.uint8)
+
+
+def quantize_fp4(x_raw) -> tuple:
+    """Storage-form rows [..., d] (d a multiple of 16) -> (codes [..., d/2]
+    uint8, two per byte with the even channel in the low nibble; scales
+    [..., d/16] uint8 E4M3 codes)."""
+    x = to_f64(x_raw).astype(np.float32)
+    shp = x.shape
+    d = shp[-1]
+    blk = x.reshape(shp[:-1] + (d // FP4_BLOCK, FP4_BLOCK))
+    amax = np.max(np.abs(blk), axis=-1)
+    s_raw = amax / np.float32(FP4_E2M1_MAX)                       # float32 quotient
+    sc = f64_to_fp8_e4m3(s_raw.astype(np.float64))
+    s = fp8_e4m3_to_f64(sc).astype(np.float32)                    # exact
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = blk / s[..., None]                                    # float32 quotient
+    codes = f64_to_fp4_e2m1(q.astype(np.float64))
+    codes = np.where((s == 0)[..., None], np.uint8(0), codes).astype(np.uint8)
+    codes = codes.reshape(shp)
+    packed = (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8)
+    return packed, sc.astype(np.uint8)
+
+
+def dequantize_fp4(packed, scales) -> np.ndarray:
+    """(codes, scales) as written by quantize_fp4 -> float64 rows."""
+    packed = np.asarray(packed, dtype=np.uint8)
+    lo = fp4_e2m1_to_f64(packed & 0xF)
+    hi = fp4_e2m1_to_f64(packed >> 4)
+    vals = np.stack([lo, hi], axis=-1).reshape(packed.shape[:-1] + (2 * packed.shape[-1],))
+    s = fp8_e4m3_to_f64(np.asarray(scales, dtype=np.uint8))
+    return vals * np.repeat(s, FP4_BLOCK, axis=-1)
+
+
+def append_fp4(k_codes, k_scales, v_codes, v_scales, seq_lens, k_new, v_new) -> int:
+    """append() for an FP4 cache: the new rows are quantised, then codes and
+    scales go to slot seq_lens[b] of their arrays (one length bump)."""
+    kc, ks = quantize_fp4(k_new)
+    vc, vs = quantize_fp4(v_new)
+    lens2 = np.array(seq_lens, copy=True)
+    flag = append(k_codes, v_codes, seq_lens, kc, vc)
+    append(k_scales, v_scales, lens2, ks, vs)
+    return flag
+
+
+def decode_fp4(q, k_codes, k_scales, v_codes, v_scales, seq_lens, scale: float):
+    """decode() over an FP4 cache: every stored number is its E2M1 value
+    times the E4M3 scale of its 16-channel block (dequantise, then attend)."""
+    B, n_h, d = q.shape
+    n_kv = k_codes.shape[1]
+    G = n_h // n_kv
+    o = np.zeros((B, n_h, 2 * v_codes.shape[3]))
+    lse = np.full((B, n_h), -math.inf)
+    for b in range(B):
+        n = int(seq_lens[b])
+        for j in range(n_kv):
+            K = dequantize_fp4(k_codes[b, j, :n], k_scales[b, j, :n])
+            V = dequantize_fp4(v_codes[b, j, :n], v_scales[b, j, :n])
             for i in range(j * G, (j + 1) * G):
                 o[b, i], lse[b, i] = _attend(to_f64(q[b, i]), K, V, scale)
     return o, lse

@@ -346,6 +346,69 @@ def mutants():
         m = _copy()
         m.topk_select = select_variant(kind)
         out["topk_select_" + kind] = m
+
+    # FP4 block format: each variant rebuilds the encoder / decoder chain
+    def e2m1_encode(ties_away=False):
+        def enc(q):
+            q = np.asarray(q, dtype=np.float64)
+            a = np.abs(q)
+            vals = np.asarray(K._E2M1_MAG)
+            best = np.zeros(a.shape, dtype=np.int64)
+            for code in range(1, 8):
+                d_new = np.abs(a - vals[code])
+                d_best = np.abs(a - vals[best])
+                tie = (code > best) if ties_away else (code % 2 == 0)
+                best = np.where((d_new < d_best) | ((d_new == d_best) & tie), code, best)
+            best = np.where(a > 6.0, 7, best)
+            return (best | np.where(np.signbit(q), 8, 0)).astype(np.uint8)
+        return enc
+
+    def fp4_variant(kind):
+        enc = e2m1_encode(ties_away=(kind == "ties_away"))
+        block = 32 if kind == "block_32" else 16
+
+        def decode_e2m1(codes):
+            v = K.fp4_e2m1_to_f64(codes)
+            return v * 2.0 if kind == "exponent_bias_0" else v
+
+        def quantize(x_raw):
+            x = K.to_f64(x_raw).astype(np.float32)
+            shp = x.shape
+            blk = x.reshape(shp[:-1] + (shp[-1] // block, block))
+            amax = np.max(np.abs(blk), axis=-1)
+            s_raw = amax if kind == "scale_amax" else amax / np.float32(6.0)
+            sc = K.f64_to_fp8_e4m3(s_raw.astype(np.float64))
+            s = K.fp8_e4m3_to_f64(sc).astype(np.float32)
+            if kind == "scale_unrounded":
+                s = s_raw.astype(np.float32)
+            with np.errstate(divide="ignore", invalid="ignore"):
+                q = blk / s[..., None]
+            codes = np.where((s == 0)[..., None], np.uint8(0), enc(q.astype(np.float64)))
+            codes = codes.astype(np.uint8).reshape(shp)
+            lo, hi = (codes[..., 1::2], codes[..., 0::2]) if kind == "nibbles_swapped" else \
+                     (codes[..., 0::2], codes[..., 1::2])
+            packed = (lo | (hi << 4)).astype(np.uint8)
+            if block == 32:
+                sc = np.repeat(sc, 2, axis=-1)
+            return packed, sc.astype(np.uint8)
+
+        def dequantize(packed, scales):
+            packed = np.asarray(packed, dtype=np.uint8)
+            lo = decode_e2m1(packed & 0xF)
+            hi = decode_e2m1(packed >> 4)
+            vals = np.stack([lo, hi], axis=-1).reshape(packed.shape[:-1] + (2 * packed.shape[-1],))
+            s = K.fp8_e4m3_to_f64(np.asarray(scales, dtype=np.uint8))
+            return vals * np.repeat(s, 16, axis=-1)
+
+        m = _copy()
+        m.f64_to_fp4_e2m1 = enc
+        m.fp4_e2m1_to_f64 = decode_e2m1
+        m.quantize_fp4 = quantize
+        m.dequantize_fp4 = dequantize
+        return m
+    for kind in ("scale_amax", "ties_away", "nibbles_swapped", "block_32", "exponent_bias_0",
+                 "scale_unrounded"):
+        out["fp4_" + kind] = fp4_variant(kind)
     return out
 
 
