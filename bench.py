@@ -16,7 +16,8 @@ GB/s over the algorithmic bytes of a step (cache read + q read + out write +
 new k/v read and written + lengths).  `roofline` is the dense decode kernel
 alone, timed with HIP events over back-to-back launches of one step's
 layers.  `also` carries the same figures for the GQA, MLA and top-k
-workloads, for the GQA workload over FP8 E4M3 caches (C3F8) and for the GQA
+workloads, for the GQA workload over FP8 E4M3 caches (C3F8) and over FP4
+caches (C3F4: E2M1 codes, one E4M3 scale per 16 channels), for the GQA
 workload attending a sliding window of its newest 128 positions (C3W128) and
 over a paged cache of 16-position blocks (C3P16), and for the top-k
 selection that feeds the sparse workload (C5S).  `cpu_baseline` is the fp64 oracle on the same inputs (copied to
@@ -48,8 +49,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="C2", choices=["C2", "C3", "C4", "C5", "C3F8", "C3W128", "C3P16", "C5S"])
-    ap.add_argument("--others", default="C3,C4,C5,C3F8,C3W128,C3P16,C5S",
+    ap.add_argument("--config", default="C2", choices=["C2", "C3", "C4", "C5", "C3F8", "C3F4", "C3W128", "C3P16", "C5S"])
+    ap.add_argument("--others", default="C3,C4,C5,C3F8,C3F4,C3W128,C3P16,C5S",
                     help="also-measured workloads (comma list; 'none' for none)")
     ap.add_argument("--kernel-reps", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true")
@@ -61,7 +62,7 @@ class DenseWorkload:
     """MHA/GQA layers over [B, n_kv, L_max, d] caches (C2, C3).  Each layer
     runs the fused append-and-attend call (one kernel per layer-step)."""
 
-    kernel = "dense_mfma_kernel<false, true, false, false> (append + attend)"
+    kernel = "dense_mfma_kernel<false, true, false, false, false> (append + attend)"
     kernel_appends = True
 
     def __init__(self, cfg, slack, torch, kvc):
@@ -220,7 +221,7 @@ class MlaWorkload:
 class TopKWorkload:
     """Top-k sparse GQA over [B, n_kv, L_max, d] caches (C5)."""
 
-    kernel = "dense_mfma_kernel<true, false, false, false> (top-k)"
+    kernel = "dense_mfma_kernel<true, false, false, false, false> (top-k)"
     kernel_appends = False
 
     def __init__(self, cfg, slack, torch, kvc):
@@ -287,7 +288,7 @@ class Fp8DenseWorkload:
     one float32 scale per tensor).  A layer-step is kvc_append_fp8 then
     kvc_decode_attn_fp8."""
 
-    kernel = "dense_mfma_kernel<false, false, true, false> (fp8 E4M3 cache)"
+    kernel = "dense_mfma_kernel<false, false, true, false, false> (fp8 E4M3 cache)"
     kernel_appends = False
     K_SCALE = 1.0 / 64      # N(0,1) / (1/64) stays within +-448
     V_SCALE = 1.0 / 64
@@ -370,12 +371,101 @@ class Fp8DenseWorkload:
                 f"{self.layers} layers ({self.nbuf} distinct cache buffers), bf16 q/out")
 
 
+class Fp4DenseWorkload:
+    """The GQA layers of C3 over FP4 block-scaled caches: E2M1 codes
+    (uint8 [B, n_kv, L_max, d/2]) and one E4M3 scale per 16 channels (uint8
+    [B, n_kv, L_max, d/16]).  A layer-step is kvc_append_fp4 then
+    kvc_decode_attn_fp4."""
+
+    kernel = "dense_mfma_kernel<false, false, false, false, true> (fp4 E2M1 cache)"
+    kernel_appends = False
+
+    def __init__(self, cfg, slack, torch, kvc):
+        self.cfg, self.torch, self.kvc = cfg, torch, kvc
+        B, n_h, n_kv, d = cfg.B, cfg.n_h, cfg.n_kv, cfg.d
+        self.pre = syn.pre_append_lens(cfg).astype(np.int64)
+        self.L_max = int(max(cfg.L_max, self.pre.max() + 1) + slack)
+        self.layers = cfg.layers
+        self.nbuf = cfg.distinct_buffers
+        dt = torch.bfloat16
+        fill = lambda shape, i, t, lo, hi: self._bytes(
+            torch.empty(*shape, dtype=torch.uint8, device="cuda"), syn.device_seed(cfg.cfg_id, i, t),
+            lo, hi)
+        cshape, sshape = (B, n_kv, self.L_max, d // 2), (B, n_kv, self.L_max, d // 16)
+        # any byte is a pair of E2M1 codes; scales 0x30..0x40 are E4M3 0.5 .. 2
+        self.KC = [fill(cshape, i, "k", 0, 256) for i in range(self.nbuf)]
+        self.VC = [fill(cshape, i, "v", 0, 256) for i in range(self.nbuf)]
+        self.KS = [fill(sshape, i, "k_scales", 0x30, 0x41) for i in range(self.nbuf)]
+        self.VS = [fill(sshape, i, "v_scales", 0x30, 0x41) for i in range(self.nbuf)]
+        mk = lambda shape, l, t: syn.device_normal_(torch.empty(*shape, dtype=dt, device="cuda"),
+                                                    syn.device_seed(cfg.cfg_id, l, t))
+        self.q = [mk((B, n_h, d), l, "q") for l in range(self.layers)]
+        self.kn = [mk((B, n_kv, d), l, "k_new") for l in range(self.layers)]
+        self.vn = [mk((B, n_kv, d), l, "v_new") for l in range(self.layers)]
+        self.out = [torch.empty(B, n_h, d, dtype=dt, device="cuda") for _ in range(self.layers)]
+        pre_t = torch.tensor(self.pre, dtype=torch.int32)
+        self.sl = [pre_t.clone().cuda() for _ in range(self.layers)]
+        self.ws = kvc.workspace(kvc.kvc_decode_attn_fp4_workspace_size(B, n_h, n_kv, self.L_max, d))
+
+    def _bytes(self, t, seed, lo, hi):
+        """Seeded uniform bytes in [lo, hi) (input set-up only)."""
+        g = self.torch.Generator(device=t.device)
+        g.manual_seed(seed)
+        t.copy_(self.torch.randint(lo, hi, t.shape, generator=g, device=t.device,
+                                   dtype=self.torch.int32).to(self.torch.uint8))
+        return t
+
+    def step(self):
+        for l in range(self.layers):
+            b = l % self.nbuf
+            self.kvc.kvc_append_fp4(self.KC[b], self.KS[b], self.VC[b], self.VS[b], self.sl[l],
+                                    self.kn[l], self.vn[l])
+            self.kvc.kvc_decode_attn_fp4(self.q[l], self.KC[b], self.KS[b], self.VC[b],
+                                         self.VS[b], self.sl[l], self.out[l], None,
+                                         scale=self.cfg.scale, workspace=self.ws)
+
+    def decode_only(self):
+        for l in range(self.layers):
+            b = l % self.nbuf
+            self.kvc.kvc_decode_attn_fp4(self.q[l], self.KC[b], self.KS[b], self.VC[b],
+                                         self.VS[b], self.sl[l], self.out[l], None,
+                                         scale=self.cfg.scale, workspace=self.ws)
+
+    def kernel_only(self):
+        self.decode_only()
+
+    def lens_after(self, steps_done):
+        return np.minimum(self.pre + 1 + steps_done, self.L_max)
+
+    def row_bytes(self):
+        return self.cfg.d // 2 + self.cfg.d // 16          # codes + scales per position
+
+    def kernel_bytes(self, n):
+        c = self.cfg
+        return int(2 * c.n_kv * self.row_bytes() * n.sum() + c.B * c.n_h * c.d * (2 + 2) + 4 * c.B)
+
+    def launch_bytes(self, steps_done):
+        return self.kernel_bytes(self.lens_after(steps_done - 1))
+
+    def step_bytes(self, steps_done):
+        c = self.cfg
+        append = 2 * c.B * c.n_kv * (c.d * 2 + self.row_bytes()) + 8 * c.B
+        return (self.kernel_bytes(self.lens_after(steps_done)) + append) * self.layers
+
+    def describe(self):
+        c = self.cfg
+        return (f"{c.name} over FP4 caches (E2M1 + E4M3 scale per 16 channels): B={c.B} "
+                f"n_h={c.n_h} n_kv={c.n_kv} d={c.d}, seq_lens ~ U[{c.len_range[0]}, "
+                f"{c.len_range[1]}] (post-append), {self.layers} layers ({self.nbuf} distinct "
+                f"cache buffers), bf16 q/out")
+
+
 class WindowWorkload(DenseWorkload):
     """The GQA layers of C3 attending only the newest WINDOW positions (the
     DeepSeek article's n_win = 128).  A layer-step is kvc_append then
     kvc_decode_attn_window."""
 
-    kernel = "dense_mfma_kernel<false, false, false, false> (window 128)"
+    kernel = "dense_mfma_kernel<false, false, false, false, false> (window 128)"
     kernel_appends = False
     WINDOW = 128
 
@@ -425,7 +515,7 @@ class PagedWorkload:
     block table per layer buffer.  A layer-step is kvc_append_paged then
     kvc_decode_attn_paged."""
 
-    kernel = "dense_mfma_kernel<false, false, false, true> (paged, 16-position blocks)"
+    kernel = "dense_mfma_kernel<false, false, false, true, false> (paged, 16-position blocks)"
     kernel_appends = False
     BETA = 16
 
@@ -555,7 +645,7 @@ class SelectWorkload:
 WORKLOADS = {"C2": (syn.C2, DenseWorkload), "C3": (syn.C3, DenseWorkload),
              "C4": (syn.C4, MlaWorkload), "C5": (syn.C5, TopKWorkload),
              "C3F8": (syn.C3, Fp8DenseWorkload), "C3W128": (syn.C3, WindowWorkload),
-             "C3P16": (syn.C3, PagedWorkload), "C5S": (syn.C5, SelectWorkload)}
+             "C3P16": (syn.C3, PagedWorkload), "C3F4": (syn.C3, Fp4DenseWorkload), "C5S": (syn.C5, SelectWorkload)}
 
 
 # ---------------------------------------------------------------- timing

@@ -247,6 +247,43 @@ int kvc_decode_attn_fp8(const void* q, const void* k_cache, const void* v_cache,
                         size_t ws_bytes, void* stream);
 
 /*
+ * FP4 cache (podcast transcript, the 890-byte passage; DeepSeek KV cache
+ * article, section 6): each number is a 4-bit E2M1 code (sign, 2 exponent
+ * bits with bias 1, 1 mantissa bit: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6)
+ * and every 16 consecutive channels of a row share one E4M3 scale byte; no
+ * second-level scale.  Stored value = E2M1(code) * E4M3(scale), at most
+ * 448 * 6 = 2688 in magnitude.  Two codes per byte, channel 2i in the low
+ * nibble of byte i.  Layout per tensor (keys, values):
+ *   codes  [B, n_kv, L_max, d/2] uint8     scales [B, n_kv, L_max, d/16] uint8
+ *
+ * kvc_append_fp4 - quantise the new bf16 rows k_new, v_new [B, n_kv, d] into
+ * slot n = seq_lens[b], then bump it (full cache: flag bit 0, nothing
+ * written).  Per 16-channel block: scale = the E4M3 value nearest
+ * float32(amax / 6) (ties to even, saturating at 448); each number x becomes
+ * the E2M1 code nearest float32(x / scale) (ties to the even code, magnitudes
+ * past 6 saturating, sign bit from the quotient's sign); a block whose scale
+ * is zero stores zero codes.  NaN or infinite inputs are outside the
+ * contract.  d a multiple of 16; codes 8-byte aligned, new rows 16-byte
+ * aligned.
+ */
+int kvc_append_fp4(void* k_codes, void* k_scales, void* v_codes, void* v_scales,
+                   int32_t* seq_lens, const void* k_new, const void* v_new, int B, int n_kv,
+                   int L_max, int d, int32_t* flag, void* stream);
+
+/*
+ * kvc_decode_attn_fp4 - kvc_decode_attn over an FP4 cache written by
+ * kvc_append_fp4: keys and values are dequantised (exactly, to bf16) before
+ * the attention.  q and out are bf16, lse float32 or NULL.  d = 128,
+ * n_h / n_kv <= 16; scale arrays 8-byte aligned.  Workspace rules as for
+ * kvc_decode_attn.
+ */
+size_t kvc_decode_attn_fp4_workspace_size(int B, int n_h, int n_kv, int L_max, int d);
+int kvc_decode_attn_fp4(const void* q, const void* k_codes, const void* k_scales,
+                        const void* v_codes, const void* v_scales, const int32_t* seq_lens,
+                        void* out, float* lse, int B, int n_h, int n_kv, int L_max, int d,
+                        float scale, void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * kvc_decode_attn_mla - decode attention over a latent (MLA) cache.
  * (Guide, "Caching a compressed latent" and the memory footnote.)
  *

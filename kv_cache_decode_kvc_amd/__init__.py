@@ -80,6 +80,10 @@ def lib() -> ctypes.CDLL:
         "kvc_decode_attn_fp8_workspace_size": (_Z, [_I, _I, _I, _I, _I]),
         "kvc_decode_attn_fp8": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
                                      _F, _F, _F, _P, _Z, _P]),
+        "kvc_append_fp4": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P]),
+        "kvc_decode_attn_fp4_workspace_size": (_Z, [_I, _I, _I, _I, _I]),
+        "kvc_decode_attn_fp4": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
+                                     _F, _P, _Z, _P]),
         "kvc_status_string": (ctypes.c_char_p, [_I]),
         "kvc_set_split_override": (_I, [_I]),
         "kvc_split_positions": (_I, [_I, _I, _I, _I]),
@@ -360,6 +364,48 @@ def kvc_decode_attn_fp8(q, k_cache, v_cache, seq_lens, out, k_scale, v_scale,
                                    n_kv, L_max, d, scale, k_scale, v_scale, wp, wn,
                                    _stream(stream))
     _check(st, "kvc_decode_attn_fp8")
+
+
+def kvc_append_fp4(k_codes, k_scales, v_codes, v_scales, seq_lens, k_new, v_new,
+                   flag=None, stream=None):
+    """Quantise bf16 k_new/v_new [B, n_kv, d] into FP4 slot seq_lens[b]: codes
+    uint8 [B, n_kv, L_max, d/2], scales uint8 [B, n_kv, L_max, d/16]; bump
+    seq_lens."""
+    import torch
+    for t, nm in ((k_codes, "k_codes"), (k_scales, "k_scales"), (v_codes, "v_codes"),
+                  (v_scales, "v_scales")):
+        _need_u8(t, nm)
+    if k_new.dtype != torch.bfloat16 or v_new.dtype != torch.bfloat16:
+        raise TypeError("k_new/v_new must be bfloat16")
+    B, n_kv, L_max, half = k_codes.shape
+    st = lib().kvc_append_fp4(_ptr(k_codes), _ptr(k_scales), _ptr(v_codes), _ptr(v_scales),
+                              _ptr(seq_lens), _ptr(k_new), _ptr(v_new), B, n_kv, L_max,
+                              2 * half, _ptr(flag), _stream(stream))
+    _check(st, "kvc_append_fp4")
+
+
+def kvc_decode_attn_fp4_workspace_size(B, n_h, n_kv, L_max, d) -> int:
+    return lib().kvc_decode_attn_fp4_workspace_size(B, n_h, n_kv, L_max, d)
+
+
+def kvc_decode_attn_fp4(q, k_codes, k_scales, v_codes, v_scales, seq_lens, out, lse=None,
+                        scale=None, workspace=None, stream=None):
+    """Dense decode over an FP4 cache (codes [B, n_kv, L_max, d/2], scales
+    [B, n_kv, L_max, d/16], uint8); q/out bf16."""
+    import torch
+    for t, nm in ((k_codes, "k_codes"), (k_scales, "k_scales"), (v_codes, "v_codes"),
+                  (v_scales, "v_scales")):
+        _need_u8(t, nm)
+    if q.dtype != torch.bfloat16 or out.dtype != torch.bfloat16:
+        raise TypeError("q/out must be bfloat16")
+    B, n_h, d = q.shape
+    _, n_kv, L_max, _ = k_codes.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    wp, wn = _ws(workspace)
+    st = lib().kvc_decode_attn_fp4(_ptr(q), _ptr(k_codes), _ptr(k_scales), _ptr(v_codes),
+                                   _ptr(v_scales), _ptr(seq_lens), _ptr(out), _ptr(lse), B,
+                                   n_h, n_kv, L_max, d, scale, wp, wn, _stream(stream))
+    _check(st, "kvc_decode_attn_fp4")
 
 
 def kvc_stream_read_sink_floats(nbytes: int) -> int:

@@ -103,6 +103,80 @@ hipError_t launch_append_fp8(const AppendParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+// FP4 append (E2M1 numbers, one E4M3 scale per 16 channels): one thread per
+// 16-channel block of a new row.  scale = E4M3(float32(amax / 6)) (nearest
+// even, saturating at 448); each number becomes the E2M1 code nearest
+// float32(x / scale), ties to the even code, saturating at 6, sign bit from
+// the quotient's sign; a zero scale stores zero codes.  Codes are packed two
+// per byte, the even channel in the low nibble.
+__device__ inline uint32_t e2m1_code(float q) {
+  const float a = fabsf(q);
+  const uint32_t c = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) +
+                     (a > 2.5f) + (a >= 3.5f) + (a > 5.0f);
+  return c | (signbit(q) ? 8u : 0u);
+}
+
+__device__ inline void quant_block_fp4(const uint16_t* src, uint8_t* codes, uint8_t* scale) {
+  const u32x4* s4 = reinterpret_cast<const u32x4*>(src);
+  const u32x4 w0 = s4[0], w1 = s4[1];
+  float x[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = bf16_lo(w0[i]);
+    x[2 * i + 1] = bf16_hi(w0[i]);
+    x[8 + 2 * i] = bf16_lo(w1[i]);
+    x[8 + 2 * i + 1] = bf16_hi(w1[i]);
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(x[i]));
+  const float s_raw = fminf(__fdiv_rn(amax, 6.0f), kFp8Max);
+  const uint32_t sc = __builtin_amdgcn_cvt_pk_fp8_f32(s_raw, 0.f, 0u, false) & 0xFFu;
+  const float s = __builtin_amdgcn_cvt_f32_fp8(sc, 0);
+  uint32_t lo = 0, hi = 0;
+  if (s > 0.f) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      lo |= e2m1_code(__fdiv_rn(x[i], s)) << (4 * i);
+      hi |= e2m1_code(__fdiv_rn(x[8 + i], s)) << (4 * i);
+    }
+  }
+  *reinterpret_cast<u32x2*>(codes) = u32x2{lo, hi};
+  *scale = (uint8_t)sc;
+}
+
+__global__ __launch_bounds__(256) void append_fp4_kernel(AppendParams p) {
+  __shared__ int s_n;
+  const int b = blockIdx.x;
+  if (threadIdx.x == 0) s_n = p.seq_lens[b];
+  __syncthreads();
+  const int n = s_n;
+  if (n < 0 || n >= p.L_max) {
+    if (threadIdx.x == 0 && p.flag) atomicOr(p.flag, 1);
+    return;
+  }
+  const int nb = p.d / 16;                 // blocks per row
+  const int per = p.n_kv * nb;
+  for (int e = threadIdx.x; e < 2 * per; e += blockDim.x) {
+    const int t = e / per, rem = e - t * per;
+    const int jj = rem / nb, blk = rem - jj * nb;
+    const size_t unit = (size_t)b * p.n_kv + jj;
+    const size_t slot = unit * p.L_max + n;
+    const uint16_t* src = reinterpret_cast<const uint16_t*>(t ? p.v_new : p.k_new) +
+                          unit * p.d + blk * 16;
+    uint8_t* codes = reinterpret_cast<uint8_t*>(t ? p.v_cache : p.k_cache) + slot * (p.d / 2) + blk * 8;
+    uint8_t* scale = reinterpret_cast<uint8_t*>(t ? p.v_scales : p.k_scales) + slot * nb + blk;
+    quant_block_fp4(src, codes, scale);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) p.seq_lens[b] = n + 1;
+}
+
+hipError_t launch_append_fp4(const AppendParams& p, hipStream_t s) {
+  hipLaunchKernelGGL(append_fp4_kernel, dim3(p.B), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
 // Paged append: slot n of sequence b is offset n % beta of block
 // block_table[b][n / beta] in pools [num_blocks, n_kv, beta, d].  A full
 // table sets flag bit 0, an invalid block bit 1; then nothing is written and

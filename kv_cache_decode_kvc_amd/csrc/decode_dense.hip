@@ -536,13 +536,67 @@ __device__ inline void expand_chunk(const ChunkF8& f, Chunk& c) {
   c.vmask = 0xFF;
 }
 
-template <bool FP8> struct ChunkOf { using T = Chunk; };
-template <> struct ChunkOf<true> { using T = ChunkF8; };
+// FP4 cache (d = 128): rows of 64 code bytes (E2M1, channel 2i in the low
+// nibble of byte i) and 8 scale bytes (E4M3, one per 16 channels).  K: lane
+// group g loads the 16 code bytes of channels 32g .. 32g + 31, so k-step kk
+// covers channels 32g + 8kk .. +7 (q is loaded in that order), and the scale
+// word holding blocks 2g and 2g + 1.  V keeps the bf16 layout: 4 code bytes
+// (channels 8r .. 8r + 7) per row and the word holding block r / 2.
+struct ChunkF4 {
+  u32x4 k[2];
+  uint32_t ks[2];
+  uint32_t v[8];
+  uint32_t vs[8];
+};
 
-template <bool TOPK, bool APPEND, bool FP8 = false, bool PAGED = false>
+__device__ inline int fp4_q_col(int kk, int g) { return g * 32 + kk * 8; }
+
+__device__ inline void load_chunk(ChunkF4& c, int cs, int end, __amdgpu_buffer_rsrc_t kr,
+                                  __amdgpu_buffer_rsrc_t vr, __amdgpu_buffer_rsrc_t ksr,
+                                  __amdgpu_buffer_rsrc_t vsr, int r, int g) {
+  constexpr uint32_t kRow = 64, kSRow = 8;
+  const bool live = cs < end;
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    const uint32_t row = cs + (r >> 2) * 8 + a * 4 + (r & 3);
+    c.k[a] = buf_load16_stream(kr, live ? row * kRow + g * 16 : kOobOffset);
+    c.ks[a] = __builtin_amdgcn_raw_buffer_load_b32(
+        ksr, live ? row * kSRow + (g >> 1) * 4 : kOobOffset, 0, kStream);
+  }
+  const uint32_t row0 = cs + g * 8;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    c.v[e] = __builtin_amdgcn_raw_buffer_load_b32(
+        vr, live ? (row0 + e) * kRow + r * 4 : kOobOffset, 0, kStream);
+    c.vs[e] = __builtin_amdgcn_raw_buffer_load_b32(
+        vsr, live ? (row0 + e) * kSRow + (r >> 3) * 4 : kOobOffset, 0, kStream);
+  }
+}
+
+__device__ inline void expand_chunk(const ChunkF4& f, Chunk& c, int r, int g) {
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    const uint32_t w = f.ks[a] >> (16 * (g & 1));          // blocks 2g, 2g + 1
+    const float s0 = __builtin_amdgcn_cvt_f32_fp8(w, 0);
+    const float s1 = __builtin_amdgcn_cvt_f32_fp8(w, 1);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) c.k[a][kk] = fp4x8_to_bf16x8(f.k[a][kk], kk < 2 ? s0 : s1);
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    c.v[e] = fp4x8_to_bf16x8(f.v[e], __builtin_amdgcn_cvt_f32_fp8(f.vs[e] >> (8 * ((r >> 1) & 3)), 0));
+  c.vmask = 0xFF;
+}
+
+template <bool FP8, bool FP4> struct ChunkOf { using T = Chunk; };
+template <> struct ChunkOf<true, false> { using T = ChunkF8; };
+template <> struct ChunkOf<false, true> { using T = ChunkF4; };
+
+template <bool TOPK, bool APPEND, bool FP8 = false, bool PAGED = false, bool FP4 = false>
 __global__ __launch_bounds__(256, 2) void dense_mfma_kernel(DenseParams p) {
   static_assert(!FP8 || (!TOPK && !APPEND), "FP8 caches: plain decode only");
   static_assert(!PAGED || (!TOPK && !APPEND && !FP8), "paged caches: plain decode only");
+  static_assert(!FP4 || (!TOPK && !APPEND && !FP8 && !PAGED), "FP4 caches: plain decode only");
   __shared__ MergeLds<128> L;
   int b, j, split;
   decode_unit(p, b, j, split);
@@ -566,7 +620,7 @@ __global__ __launch_bounds__(256, 2) void dense_mfma_kernel(DenseParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, g = lane >> 4;
   const size_t unit = (size_t)b * p.n_kv + j;
-  constexpr uint32_t kRowBytes = FP8 ? 128u : 256u;
+  constexpr uint32_t kRowBytes = FP4 ? 64u : FP8 ? 128u : 256u;
   const size_t unit_bytes = (size_t)p.L_max * kRowBytes;
   // (paged: the whole pool, at most 2^31 bytes, checked on the host)
   const uint32_t pool_bytes =
@@ -577,6 +631,11 @@ __global__ __launch_bounds__(256, 2) void dense_mfma_kernel(DenseParams p) {
   const __amdgpu_buffer_rsrc_t vr =
       PAGED ? make_rsrc(p.v, pool_bytes)
             : make_rsrc((const char*)p.v + unit * unit_bytes, (uint32_t)n * kRowBytes);
+  // (FP4: the scale rows, 8 bytes per position)
+  const __amdgpu_buffer_rsrc_t ksr =
+      FP4 ? make_rsrc((const char*)p.k_scales + unit * (size_t)p.L_max * 8, (uint32_t)n * 8u) : kr;
+  const __amdgpu_buffer_rsrc_t vsr =
+      FP4 ? make_rsrc((const char*)p.v_scales + unit * (size_t)p.L_max * 8, (uint32_t)n * 8u) : kr;
   const __amdgpu_buffer_rsrc_t ir =
       TOPK ? make_rsrc(p.idx + unit * p.K, (uint32_t)p.K * 4u)
            : PAGED ? make_rsrc(p.block_table + (size_t)b * p.max_blocks, (uint32_t)p.max_blocks * 4u)
@@ -588,7 +647,8 @@ __global__ __launch_bounds__(256, 2) void dense_mfma_kernel(DenseParams p) {
         (const uint16_t*)p.q + ((size_t)b * p.n_h + j * p.G + r) * 128;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
-      qop[kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow + (FP8 ? fp8_q_col(kk, g) : kk * 32 + g * 8)));
+      qop[kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(
+          qrow + (FP4 ? fp4_q_col(kk, g) : FP8 ? fp8_q_col(kk, g) : kk * 32 + g * 8)));
   } else {
     const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
@@ -614,10 +674,17 @@ __global__ __launch_bounds__(256, 2) void dense_mfma_kernel(DenseParams p) {
     for (int kk = 0; kk < 4; ++kk) knr[kk] = kn[kk * 4 + g];
     vnr = vn[r];
   }
-  using Raw = typename ChunkOf<FP8>::T;
-  auto load = [&](Raw& c, int at) { load_chunk(c, at, end, kr, vr, r, g); };
+  using Raw = typename ChunkOf<FP8, FP4>::T;
+  auto load = [&](Raw& c, int at) {
+    if constexpr (FP4) load_chunk(c, at, end, kr, vr, ksr, vsr, r, g);
+    else load_chunk(c, at, end, kr, vr, r, g);
+  };
   auto compute = [&](Raw& c, int at) {
-    if constexpr (FP8) {
+    if constexpr (FP4) {
+      Chunk x;
+      expand_chunk(c, x, r, g);
+      compute_chunk<false>(x, at, end, qop, p.scale_log2, g, st);
+    } else if constexpr (FP8) {
       Chunk x;
       expand_chunk(c, x);
       compute_chunk<false>(x, at, end, qop, p.scale_log2, g, st);
@@ -889,6 +956,12 @@ hipError_t launch_dense_paged(const DenseParams& p, hipStream_t s) {
 
 hipError_t launch_dense_fp8(const DenseParams& p, hipStream_t s) {
   hipLaunchKernelGGL((dense_mfma_kernel<false, false, true>), dense_grid(p), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_dense_fp4(const DenseParams& p, hipStream_t s) {
+  hipLaunchKernelGGL((dense_mfma_kernel<false, false, false, false, true>), dense_grid(p),
+                     dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

@@ -253,6 +253,23 @@ int kvc_append_fp8(void* k_cache, void* v_cache, int32_t* seq_lens,
   return launch_status(launch_append_fp8(p, static_cast<hipStream_t>(stream)));
 }
 
+int kvc_append_fp4(void* k_codes, void* k_scales, void* v_codes, void* v_scales,
+                   int32_t* seq_lens, const void* k_new, const void* v_new, int B, int n_kv,
+                   int L_max, int d, int32_t* flag, void* stream) {
+  if (B < 0 || n_kv < 1 || L_max < 1 || d < 1) return KVC_ERR_BAD_SHAPE;
+  if (d % 16 != 0 || (int64_t)n_kv * d >= kMaxOffset) return KVC_ERR_BAD_SHAPE;
+  if (!k_codes || !k_scales || !v_codes || !v_scales || !seq_lens || !k_new || !v_new)
+    return KVC_ERR_NULL_PTR;
+  if (!aligned(k_codes, 8) || !aligned(v_codes, 8) || !aligned(k_new, 16) ||
+      !aligned(v_new, 16) || !aligned(seq_lens, 4) || (flag && !aligned(flag, 4)))
+    return KVC_ERR_MISALIGNED;
+  if (B == 0) return KVC_OK;
+  AppendParams p{k_codes, v_codes, seq_lens, k_new, v_new, flag, B, n_kv, L_max, d, 1};
+  p.k_scales = k_scales;
+  p.v_scales = v_scales;
+  return launch_status(launch_append_fp4(p, static_cast<hipStream_t>(stream)));
+}
+
 size_t kvc_decode_attn_workspace_size(int B, int n_h, int n_kv, int L_max,
                                       int d, int dtype) {
   const DenseCheck c = check_dense_shape(B, n_h, n_kv, L_max, d, dtype, 0, false);
@@ -276,7 +293,9 @@ static int dense_common(const void* q, const void* k_cache, const void* v_cache,
                         bool fp8 = false, float k_scale = 1.f, float v_scale = 1.f,
                         int window = 0, const int32_t* win_start = nullptr,
                         const int32_t* block_table = nullptr, int max_blocks = 0,
-                        int num_blocks = 0, int page_shift = 0) {
+                        int num_blocks = 0, int page_shift = 0,
+                        const void* k_scales = nullptr, const void* v_scales = nullptr,
+                        bool fp4 = false) {
   // FP8 caches: q and out are bf16; the shape rules are those of bf16 with
   // d = 128 (checked by the caller).
   const DenseCheck c = check_dense_shape(B, n_h, n_kv, L_max, d, dtype, K, topk, fused, window);
@@ -285,8 +304,9 @@ static int dense_common(const void* q, const void* k_cache, const void* v_cache,
   if (fp8 && !(isfinite(k_scale) && isfinite(v_scale) && k_scale > 0.f && v_scale > 0.f))
     return KVC_ERR_BAD_ARG;
   if (!q || !k_cache || !v_cache || !seq_lens || !out || (topk && !idx) ||
-      (fused && (!k_new || !v_new)))
+      (fused && (!k_new || !v_new)) || (fp4 && (!k_scales || !v_scales)))
     return KVC_ERR_NULL_PTR;
+  if (fp4 && (!aligned(k_scales, 8) || !aligned(v_scales, 8))) return KVC_ERR_MISALIGNED;
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
       !aligned(out, 16) || !aligned(seq_lens, 4) || (lse && !aligned(lse, 4)) ||
       (idx && !aligned(idx, 16)) || (flag && !aligned(flag, 4)) ||
@@ -322,6 +342,11 @@ static int dense_common(const void* q, const void* k_cache, const void* v_cache,
     return launch_status(launch_dense_paged(p, static_cast<hipStream_t>(stream)));
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (fp4) {
+    p.k_scales = k_scales;
+    p.v_scales = v_scales;
+    return launch_status(launch_dense_fp4(p, s));
+  }
   if (fp8) {
     p.scale_log2 *= k_scale;
     p.out_scale = v_scale;
@@ -473,6 +498,25 @@ int kvc_decode_attn_fp8(const void* q, const void* k_cache, const void* v_cache,
                       n_h, n_kv, L_max, d, scale, KVC_BF16, nullptr, workspace,
                       ws_bytes, stream, false, nullptr, nullptr, false, true,
                       k_scale, v_scale);
+}
+
+size_t kvc_decode_attn_fp4_workspace_size(int B, int n_h, int n_kv, int L_max,
+                                          int d) {
+  if (d != 128) return 0;
+  const DenseCheck c = check_dense_shape(B, n_h, n_kv, L_max, d, KVC_BF16, 0, false);
+  return c.status == KVC_OK ? c.ws.total : 0;
+}
+
+int kvc_decode_attn_fp4(const void* q, const void* k_codes, const void* k_scales,
+                        const void* v_codes, const void* v_scales, const int32_t* seq_lens,
+                        void* out, float* lse, int B, int n_h, int n_kv, int L_max, int d,
+                        float scale, void* workspace, size_t ws_bytes, void* stream) {
+  if (B < 0 || n_h < 1 || n_kv < 1 || L_max < 1 || d < 1) return KVC_ERR_BAD_SHAPE;
+  if (d != 128) return KVC_ERR_UNSUPPORTED;
+  return dense_common(q, k_codes, v_codes, seq_lens, nullptr, 0, out, lse, B, n_h, n_kv,
+                      L_max, d, scale, KVC_BF16, nullptr, workspace, ws_bytes, stream, false,
+                      nullptr, nullptr, false, false, 1.f, 1.f, 0, nullptr, nullptr, 0, 0, 0,
+                      k_scales, v_scales, true);
 }
 
 size_t kvc_decode_attn_mla_workspace_size(int B, int n_h, int L_max, int d_c,

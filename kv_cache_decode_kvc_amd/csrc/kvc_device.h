@@ -55,6 +55,23 @@ __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Eight E2M1 codes (byte i holds channels 2i (low nibble) and 2i + 1) times
+// the block scale s, as eight bf16.  The conversion with scale 1.0 is exact,
+// and an E2M1 value times an E4M3 scale has at most 6 significant bits, so
+// the float32 product and its bf16 rounding are exact too.  (The
+// conversion's own scale operand only honours a power of two, hence the
+// separate multiply.)
+__device__ inline u32x4 fp4x8_to_bf16x8(uint32_t w, float s) {
+  const f32x2 f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+  const f32x2 f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+  const f32x2 f2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+  const f32x2 f3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+  return u32x4{pack_bf16x2(f0.x * s, f0.y * s), pack_bf16x2(f1.x * s, f1.y * s),
+               pack_bf16x2(f2.x * s, f2.y * s), pack_bf16x2(f3.x * s, f3.y * s)};
+}
+
 __device__ inline uint16_t to_bf16_bits(float x) {
   return __builtin_bit_cast(uint16_t, (__bf16)x);
 }

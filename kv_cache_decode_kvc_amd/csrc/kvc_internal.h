@@ -41,6 +41,8 @@ struct AppendParams {
   float k_inv, v_inv;     // FP8 append: 1 / scale of the keys and values
   const int32_t* block_table;   // paged append: [B, max_blocks]
   int max_blocks, num_blocks, page_shift;
+  void* k_scales;         // FP4 append: per-16-channel E4M3 scales [B, n_kv, L_max, d/16]
+  void* v_scales;
 };
 
 // Dense and top-k decode.  Workspace pointers are null when P_max == 1.
@@ -74,6 +76,10 @@ struct DenseParams {
   // position t of sequence b is in block block_table[b * max_blocks + (t >> page_shift)]
   const int32_t* block_table;
   int max_blocks, num_blocks, page_shift;
+  // FP4 cache: k/v hold E2M1 codes [B, n_kv, L_max, d/2]; these the E4M3
+  // scale of every 16 channels [B, n_kv, L_max, d/16]
+  const void* k_scales;
+  const void* v_scales;
 };
 
 // Pool bitmap words the selection kernel holds in LDS (one bit per block).
@@ -157,6 +163,8 @@ inline WsLayout ws_layout(size_t units, size_t B, size_t n_h, size_t P_max,
 hipError_t launch_append(const AppendParams& p, hipStream_t s);
 hipError_t launch_append_fp8(const AppendParams& p, hipStream_t s);
 hipError_t launch_dense_fp8(const DenseParams& p, hipStream_t s);
+hipError_t launch_append_fp4(const AppendParams& p, hipStream_t s);
+hipError_t launch_dense_fp4(const DenseParams& p, hipStream_t s);
 hipError_t launch_dense_paged(const DenseParams& p, hipStream_t s);
 hipError_t launch_append_paged(const AppendParams& p, hipStream_t s);
 hipError_t launch_dense_mfma(const DenseParams& p, bool topk, bool append, hipStream_t s);

@@ -26,13 +26,14 @@ COPY_BYTES = 1 << 30
 
 # dominant kernel of each bench workload (substring of the demangled name)
 DOMINANT = {
-    "C2": "dense_mfma_kernel<false, true, false, false>",
-    "C3": "dense_mfma_kernel<false, true, false, false>",
+    "C2": "dense_mfma_kernel<false, true, false, false, false>",
+    "C3": "dense_mfma_kernel<false, true, false, false, false>",
     "C4": "mla_kernel",
-    "C5": "dense_mfma_kernel<true, false, false, false>",
-    "C3F8": "dense_mfma_kernel<false, false, true, false>",
-    "C3W128": "dense_mfma_kernel<false, false, false, false>",
-    "C3P16": "dense_mfma_kernel<false, false, false, true>",
+    "C5": "dense_mfma_kernel<true, false, false, false, false>",
+    "C3F8": "dense_mfma_kernel<false, false, true, false, false>",
+    "C3F4": "dense_mfma_kernel<false, false, false, false, true>",
+    "C3W128": "dense_mfma_kernel<false, false, false, false, false>",
+    "C3P16": "dense_mfma_kernel<false, false, false, true, false>",
     "C5S": "topk_select_kernel",
 }
 

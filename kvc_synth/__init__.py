@@ -29,7 +29,8 @@ import math
 import numpy as np
 
 TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "k_new": 3, "v_new": 4,
-              "seq_lens": 5, "idx": 6, "ckv": 7, "ckv_new": 8}
+              "seq_lens": 5, "idx": 6, "ckv": 7, "ckv_new": 8,
+              "k_scales": 9, "v_scales": 10}
 
 F32 = "f32"
 BF16 = "bf16"

@@ -224,6 +224,43 @@ def test_fp8_validation(L):
     assert L.kvc_decode_attn_fp8_workspace_size(32, 64, 8, 32768, 64) == 0
 
 
+def test_fp4_validation(L):
+    def ap(**kw):
+        a = dict(kc=A16, ks=A16, vc=A16, vs=A16, sl=A4, kn=A16, vn=A16, B=2, n_kv=2, L_max=8,
+                 d=128, flag=NULL, stream=NULL)
+        a.update(kw)
+        return L.kvc_append_fp4(a["kc"], a["ks"], a["vc"], a["vs"], a["sl"], a["kn"], a["vn"],
+                                a["B"], a["n_kv"], a["L_max"], a["d"], a["flag"], a["stream"])
+    assert ap(ks=NULL) == -1          # scales are required
+    assert ap(vc=NULL) == -1
+    assert ap(vn=NULL) == -1
+    assert ap(d=120) == -2            # whole 16-channel blocks
+    assert ap(kc=A4) == -6            # codes: 8-byte stores
+    assert ap(kn=A8) == -6
+    assert ap(B=0) == 0
+
+    def dc(**kw):
+        a = dict(q=A16, kc=A16, ks=A16, vc=A16, vs=A16, sl=A4, out=A16, lse=NULL, B=2, n_h=8,
+                 n_kv=2, L_max=64, d=128, scale=0.1, ws=A16, wsb=1 << 30, stream=NULL)
+        a.update(kw)
+        return L.kvc_decode_attn_fp4(a["q"], a["kc"], a["ks"], a["vc"], a["vs"], a["sl"],
+                                     a["out"], a["lse"], a["B"], a["n_h"], a["n_kv"],
+                                     a["L_max"], a["d"], a["scale"], a["ws"], a["wsb"],
+                                     a["stream"])
+    assert dc(kc=NULL) == -1
+    assert dc(vs=NULL) == -1
+    assert dc(d=64) == -4
+    assert dc(n_h=7) == -2
+    assert dc(n_h=64, n_kv=2) == -4   # group of 32 heads
+    assert dc(scale=float("nan")) == -8
+    assert dc(ks=A4) == -6            # scale rows are read 4 bytes at a time, 8-byte aligned
+    assert dc(out=A8) == -6
+    assert dc(B=0) == 0
+    assert L.kvc_decode_attn_fp4_workspace_size(32, 64, 8, 32768, 128) == \
+        L.kvc_decode_attn_workspace_size(32, 64, 8, 32768, 128, kvc.KVC_BF16)
+    assert L.kvc_decode_attn_fp4_workspace_size(32, 64, 8, 32768, 64) == 0
+
+
 def test_window_validation(L):
     def wd(**kw):
         a = dict(q=A16, k=A16, v=A16, sl=A4, st=NULL, W=128, out=A16, lse=NULL, B=2, n_h=8,
