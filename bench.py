@@ -392,11 +392,12 @@ class Fp4DenseWorkload:
             torch.empty(*shape, dtype=torch.uint8, device="cuda"), syn.device_seed(cfg.cfg_id, i, t),
             lo, hi)
         cshape, sshape = (B, n_kv, self.L_max, d // 2), (B, n_kv, self.L_max, d // 16)
-        # any byte is a pair of E2M1 codes; scales 0x30..0x40 are E4M3 0.5 .. 2
+        # any byte is a pair of E2M1 codes; scale codes 0x20..0x2F are E4M3
+        # 0.125 .. 0.47, so stored values have about unit rms, like N(0,1) data
         self.KC = [fill(cshape, i, "k", 0, 256) for i in range(self.nbuf)]
         self.VC = [fill(cshape, i, "v", 0, 256) for i in range(self.nbuf)]
-        self.KS = [fill(sshape, i, "k_scales", 0x30, 0x41) for i in range(self.nbuf)]
-        self.VS = [fill(sshape, i, "v_scales", 0x30, 0x41) for i in range(self.nbuf)]
+        self.KS = [fill(sshape, i, "k_scales", 0x20, 0x30) for i in range(self.nbuf)]
+        self.VS = [fill(sshape, i, "v_scales", 0x20, 0x30) for i in range(self.nbuf)]
         mk = lambda shape, l, t: syn.device_normal_(torch.empty(*shape, dtype=dt, device="cuda"),
                                                     syn.device_seed(cfg.cfg_id, l, t))
         self.q = [mk((B, n_h, d), l, "q") for l in range(self.layers)]

@@ -4,7 +4,10 @@ Each test builds one layer of a benchmark workload at its real shape on the
 device (seeded N(0,1), the same generators and split policy the benchmark
 uses), runs the calls the benchmark times, and checks a sample of the
 outputs against the fp64 oracle on host copies of just the rows those
-outputs depend on.  Appended rows and lengths are checked bit for bit.
+outputs depend on.  Those host copies are taken before any library call (so
+no oracle input passes through the HIP path); the appended row is the
+generated new row itself, or the oracle's own quantisation of it, and the
+row the library wrote is checked against it bit for bit, as are the lengths.
 """
 from __future__ import annotations
 
@@ -37,7 +40,7 @@ def normal(shape, cfg_id, layer, tensor):
 
 
 def bits(t):
-    """bf16 device tensor -> host uint16 bit patterns."""
+    """bf16 (or uint8) device tensor -> host copy of its storage."""
     return host(t.contiguous())
 
 
@@ -49,13 +52,25 @@ def sample_units(pre, n_kv, count, seed):
     return [(b, int(rng.integers(n_kv))) for b in sorted(bs)]
 
 
-def check_dense_units(cfg, pre, q, K, V, out, lse, units, what):
+def snapshot(units, pre, **tensors):
+    """Host copies, taken before the library runs, of what the sampled
+    units' outputs depend on: cached rows [0, pre[b]) of each [B, n_kv, L, .]
+    tensor given, and the unit's slice of each [B, n_kv, .] new-row tensor."""
+    snap = {}
+    for b, j in units:
+        for name, t in tensors.items():
+            snap[(name, b, j)] = bits(t[b, j, :int(pre[b])] if t.dim() == 4 else t[b, j])
+    return snap
+
+
+def check_dense_units(cfg, pre, q_h, snap, out, lse, units, what):
+    """Oracle decode over the snapshot rows plus the generated new row."""
     G = cfg.n_h // cfg.n_kv
     for b, j in units:
         n = int(pre[b]) + 1
-        kb = bits(K[b, j, :n])[None, None]
-        vb = bits(V[b, j, :n])[None, None]
-        qb = bits(q[b, j * G:(j + 1) * G])[None]
+        kb = np.concatenate([snap[("K", b, j)], snap[("kn", b, j)][None]])[None, None]
+        vb = np.concatenate([snap[("V", b, j)], snap[("vn", b, j)][None]])[None, None]
+        qb = q_h[b, j * G:(j + 1) * G][None]
         o_ref, l_ref = oracle.decode(qb, kb, vb, np.array([n], np.int32), cfg.scale)
         got = oracle.to_f64(bits(out[b, j * G:(j + 1) * G]))
         compare(got, o_ref[0], 2e-2, f"{what} b={b} j={j} n={n}")
@@ -83,6 +98,8 @@ def _fused_dense(c, units):
     q = normal((c.B, c.n_h, c.d), c.cfg_id, 0, "q")
     kn = normal((c.B, c.n_kv, c.d), c.cfg_id, 0, "k_new")
     vn = normal((c.B, c.n_kv, c.d), c.cfg_id, 0, "v_new")
+    snap = snapshot(units, pre, K=K, V=V, kn=kn, vn=vn)
+    q_h = bits(q)
     sl = torch.tensor(pre, dtype=torch.int32, device="cuda")
     out = torch.empty_like(q)
     lse = torch.empty(c.B, c.n_h, dtype=torch.float32, device="cuda")
@@ -95,9 +112,19 @@ def _fused_dense(c, units):
     assert host(sl).tolist() == (pre + 1).tolist()
     assert int(host(flag)[0]) == 0
     for b, j in units:
-        assert np.array_equal(bits(K[b, j, pre[b]]), bits(kn[b, j]))
-        assert np.array_equal(bits(V[b, j, pre[b]]), bits(vn[b, j]))
-    check_dense_units(c, pre, q, K, V, out, lse, units, c.name)
+        assert np.array_equal(bits(K[b, j, pre[b]]), snap[("kn", b, j)])
+        assert np.array_equal(bits(V[b, j, pre[b]]), snap[("vn", b, j)])
+    check_dense_units(c, pre, q_h, snap, out, lse, units, c.name)
+
+
+def _random_codes(shape, tensor, c, lo=0, hi=256):
+    """Seeded uniform bytes on the device (the benchmark's cache fill)."""
+    t = torch.empty(*shape, dtype=torch.uint8, device="cuda")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(syn.device_seed(c.cfg_id, 0, tensor))
+    t.copy_(torch.randint(lo, hi, t.shape, generator=g, device="cuda",
+                          dtype=torch.int32).to(torch.uint8))
+    return t
 
 
 def test_fullsize_gqa_layer_fp8():
@@ -124,6 +151,9 @@ def test_fullsize_gqa_layer_fp8():
     q = normal((c.B, c.n_h, c.d), c.cfg_id, 0, "q")
     kn = normal((c.B, c.n_kv, c.d), c.cfg_id, 0, "k_new")
     vn = normal((c.B, c.n_kv, c.d), c.cfg_id, 0, "v_new")
+    units = sample_units(pre, c.n_kv, 4, 33)
+    snap = snapshot(units, pre, K=K8, V=V8, kn=kn, vn=vn)
+    q_h = bits(q)
     sl = torch.tensor(pre, dtype=torch.int32, device="cuda")
     out = torch.empty_like(q)
     lse = torch.empty(c.B, c.n_h, dtype=torch.float32, device="cuda")
@@ -132,16 +162,60 @@ def test_fullsize_gqa_layer_fp8():
     kvc.kvc_decode_attn_fp8(q, K8, V8, sl, out, ks, vs, lse, scale=c.scale, workspace=ws)
     torch.cuda.synchronize()
     assert host(sl).tolist() == (pre + 1).tolist()
-    for b, j in sample_units(pre, c.n_kv, 4, 33):
+    for b, j in units:
         n = int(pre[b]) + 1
-        assert np.array_equal(host(K8[b, j, pre[b]]), oracle.quantize_fp8(bits(kn[b, j]), ks))
-        assert np.array_equal(host(V8[b, j, pre[b]]), oracle.quantize_fp8(bits(vn[b, j]), vs))
-        o_ref, l_ref = oracle.decode_fp8(bits(q[b, j * G:(j + 1) * G])[None],
-                                         host(K8[b, j, :n])[None, None],
-                                         host(V8[b, j, :n])[None, None],
+        k_new = oracle.quantize_fp8(snap[("kn", b, j)], ks)
+        v_new = oracle.quantize_fp8(snap[("vn", b, j)], vs)
+        assert np.array_equal(host(K8[b, j, pre[b]]), k_new)
+        assert np.array_equal(host(V8[b, j, pre[b]]), v_new)
+        kb = np.concatenate([snap[("K", b, j)], k_new[None]])[None, None]
+        vb = np.concatenate([snap[("V", b, j)], v_new[None]])[None, None]
+        o_ref, l_ref = oracle.decode_fp8(q_h[b, j * G:(j + 1) * G][None], kb, vb,
                                          np.array([n], np.int32), c.scale, ks, vs)
         got = oracle.to_f64(bits(out[b, j * G:(j + 1) * G]))
         compare(got, o_ref[0], 2e-2, f"fp8 b={b} j={j} n={n}")
+        compare_lse(host(lse[b, j * G:(j + 1) * G]), l_ref[0], 4e-3)
+
+
+def test_fullsize_gqa_layer_fp4():
+    """The GQA layer over FP4 caches (E2M1 codes, E4M3 scales per 16
+    channels): append_fp4 then decode_fp4, as the benchmark's FP4 workload."""
+    c = syn.C3
+    pre = syn.pre_append_lens(c)
+    L_max = int(max(c.L_max, pre.max() + 1))
+    G = c.n_h // c.n_kv
+    cshape, sshape = (c.B, c.n_kv, L_max, c.d // 2), (c.B, c.n_kv, L_max, c.d // 16)
+    KC, VC = _random_codes(cshape, "k", c), _random_codes(cshape, "v", c)
+    KS = _random_codes(sshape, "k_scales", c, 0x20, 0x30)
+    VS = _random_codes(sshape, "v_scales", c, 0x20, 0x30)
+    q = normal((c.B, c.n_h, c.d), c.cfg_id, 0, "q")
+    kn = normal((c.B, c.n_kv, c.d), c.cfg_id, 0, "k_new")
+    vn = normal((c.B, c.n_kv, c.d), c.cfg_id, 0, "v_new")
+    units = sample_units(pre, c.n_kv, 4, 34)
+    snap = snapshot(units, pre, KC=KC, VC=VC, KS=KS, VS=VS, kn=kn, vn=vn)
+    q_h = bits(q)
+    sl = torch.tensor(pre, dtype=torch.int32, device="cuda")
+    out = torch.empty_like(q)
+    lse = torch.empty(c.B, c.n_h, dtype=torch.float32, device="cuda")
+    ws = kvc.workspace(kvc.kvc_decode_attn_fp4_workspace_size(c.B, c.n_h, c.n_kv, L_max, c.d))
+    kvc.kvc_append_fp4(KC, KS, VC, VS, sl, kn, vn)
+    kvc.kvc_decode_attn_fp4(q, KC, KS, VC, VS, sl, out, lse, scale=c.scale, workspace=ws)
+    torch.cuda.synchronize()
+    assert host(sl).tolist() == (pre + 1).tolist()
+    for b, j in units:
+        n = int(pre[b]) + 1
+        kc_new, ks_new = oracle.quantize_fp4(snap[("kn", b, j)])
+        vc_new, vs_new = oracle.quantize_fp4(snap[("vn", b, j)])
+        assert np.array_equal(host(KC[b, j, pre[b]]), kc_new)
+        assert np.array_equal(host(KS[b, j, pre[b]]), ks_new)
+        assert np.array_equal(host(VC[b, j, pre[b]]), vc_new)
+        assert np.array_equal(host(VS[b, j, pre[b]]), vs_new)
+        cat = lambda old, new: np.concatenate([snap[(old, b, j)], new[None]])[None, None]
+        o_ref, l_ref = oracle.decode_fp4(q_h[b, j * G:(j + 1) * G][None], cat("KC", kc_new),
+                                         cat("KS", ks_new), cat("VC", vc_new), cat("VS", vs_new),
+                                         np.array([n], np.int32), c.scale)
+        got = oracle.to_f64(bits(out[b, j * G:(j + 1) * G]))
+        compare(got, o_ref[0], 2e-2, f"fp4 b={b} j={j} n={n}")
         compare_lse(host(lse[b, j * G:(j + 1) * G]), l_ref[0], 4e-3)
 
 
@@ -153,6 +227,8 @@ def test_fullsize_mla_layer():
     C = normal((c.B, L_max, D), c.cfg_id, 0, "ckv")
     q = normal((c.B, c.n_h, D), c.cfg_id, 0, "q")
     cn = normal((c.B, D), c.cfg_id, 0, "ckv_new")
+    check = (0, 37, 63)
+    snap = {b: (bits(C[b, :c.pre_len]), bits(cn[b]), bits(q[b])) for b in check}
     pre = np.full(c.B, c.pre_len, dtype=np.int32)
     sl = torch.tensor(pre, dtype=torch.int32, device="cuda")
     out = torch.empty(c.B, c.n_h, c.d_c, dtype=torch.bfloat16, device="cuda")
@@ -163,9 +239,10 @@ def test_fullsize_mla_layer():
     kvc.kvc_decode_attn_mla(q, C, sl, out, lse, scale=c.scale, workspace=ws)
     torch.cuda.synchronize()
     assert host(sl).tolist() == (pre + 1).tolist()
-    for b in (0, 37, 63):
-        assert np.array_equal(bits(C[b, c.pre_len]), bits(cn[b]))
-        o_ref, l_ref = oracle.decode_mla(bits(q[b])[None], bits(C[b])[None],
+    for b in check:
+        rows, new, qb = snap[b]
+        assert np.array_equal(bits(C[b, c.pre_len]), new)
+        o_ref, l_ref = oracle.decode_mla(qb[None], np.concatenate([rows, new[None]])[None],
                                          np.array([c.pre_len + 1], np.int32), c.d_c, c.d_r, c.scale)
         compare(oracle.to_f64(bits(out[b])), o_ref[0], 2e-2, f"mla b={b}")
         compare_lse(host(lse[b]), l_ref[0], 4e-3)
@@ -183,6 +260,9 @@ def test_fullsize_topk_layer():
     idx_h = syn.topk_indices(c.cfg_id, 0, c.B, c.n_kv, c.K, c.pre_len, index_set=0)
     idx = torch.from_numpy(idx_h).cuda()
     pre = np.full(c.B, c.pre_len, dtype=np.int32)
+    units = [(0, 0), (3, 5), (7, 7)]
+    snap = snapshot(units, pre, K=K, V=V, kn=kn, vn=vn)
+    q_h = bits(q)
     sl = torch.tensor(pre, dtype=torch.int32, device="cuda")
     out = torch.empty_like(q)
     lse = torch.empty(c.B, c.n_h, dtype=torch.float32, device="cuda")
@@ -194,11 +274,11 @@ def test_fullsize_topk_layer():
     torch.cuda.synchronize()
     assert int(host(flag)[0]) == 0
     G = c.n_h // c.n_kv
-    for b, j in [(0, 0), (3, 5), (7, 7)]:
+    for b, j in units:
         n = c.pre_len + 1
-        kb = bits(K[b, j, :n])[None, None]
-        vb = bits(V[b, j, :n])[None, None]
-        qb = bits(q[b, j * G:(j + 1) * G])[None]
+        kb = np.concatenate([snap[("K", b, j)], snap[("kn", b, j)][None]])[None, None]
+        vb = np.concatenate([snap[("V", b, j)], snap[("vn", b, j)][None]])[None, None]
+        qb = q_h[b, j * G:(j + 1) * G][None]
         o_ref, l_ref, f_ref = oracle.decode_topk(qb, kb, vb, np.array([n], np.int32),
                                                  idx_h[b:b + 1, j:j + 1], c.scale)
         assert f_ref == 0
@@ -218,6 +298,9 @@ def test_fullsize_gqa_layer_window():
     q = normal((c.B, c.n_h, c.d), c.cfg_id, 0, "q")
     kn = normal((c.B, c.n_kv, c.d), c.cfg_id, 0, "k_new")
     vn = normal((c.B, c.n_kv, c.d), c.cfg_id, 0, "v_new")
+    units = sample_units(pre, c.n_kv, 4, 35)
+    snap = snapshot(units, pre, K=K, V=V, kn=kn, vn=vn)
+    q_h = bits(q)
     sl = torch.tensor(pre, dtype=torch.int32, device="cuda")
     out = torch.empty_like(q)
     lse = torch.empty(c.B, c.n_h, dtype=torch.float32, device="cuda")
@@ -228,13 +311,13 @@ def test_fullsize_gqa_layer_window():
     torch.cuda.synchronize()
     assert host(sl).tolist() == (pre + 1).tolist()
     G = c.n_h // c.n_kv
-    for b, j in sample_units(pre, c.n_kv, 4, 35):
+    for b, j in units:
         n = int(pre[b]) + 1
         lo = n - W
-        o_ref, l_ref = oracle.decode_window(bits(q[b, j * G:(j + 1) * G])[None],
-                                            bits(K[b, j, lo:n])[None, None],
-                                            bits(V[b, j, lo:n])[None, None],
-                                            np.array([W], np.int32), c.scale, W)
+        kb = np.concatenate([snap[("K", b, j)], snap[("kn", b, j)][None]])[lo:n]
+        vb = np.concatenate([snap[("V", b, j)], snap[("vn", b, j)][None]])[lo:n]
+        o_ref, l_ref = oracle.decode_window(q_h[b, j * G:(j + 1) * G][None], kb[None, None],
+                                            vb[None, None], np.array([W], np.int32), c.scale, W)
         compare(oracle.to_f64(bits(out[b, j * G:(j + 1) * G])), o_ref[0], 2e-2, f"window b={b} j={j}")
         compare_lse(host(lse[b, j * G:(j + 1) * G]), l_ref[0], 4e-3)
 
@@ -259,6 +342,16 @@ def test_fullsize_gqa_layer_paged():
     q = normal((c.B, c.n_h, c.d), c.cfg_id, 0, "q")
     kn = normal((c.B, c.n_kv, c.d), c.cfg_id, 0, "k_new")
     vn = normal((c.B, c.n_kv, c.d), c.cfg_id, 0, "v_new")
+    units = sample_units(pre, c.n_kv, 3, 37)
+    # rows [0, pre) of each sampled unit, gathered through its block table
+    # before the library runs
+    snap = {}
+    for b, j in units:
+        blocks = torch.from_numpy(table[b, :need[b]].astype(np.int64)).cuda()
+        snap[("K", b, j)] = bits(K.index_select(0, blocks)[:, j].reshape(-1, c.d)[:int(pre[b])])
+        snap[("V", b, j)] = bits(V.index_select(0, blocks)[:, j].reshape(-1, c.d)[:int(pre[b])])
+        snap[("kn", b, j)], snap[("vn", b, j)] = bits(kn[b, j]), bits(vn[b, j])
+    q_h = bits(q)
     tab = torch.from_numpy(table).cuda()
     sl = torch.tensor(pre, dtype=torch.int32, device="cuda")
     out = torch.empty_like(q)
@@ -272,12 +365,14 @@ def test_fullsize_gqa_layer_paged():
     assert host(sl).tolist() == (pre + 1).tolist()
     assert int(host(flag)[0]) == 0
     G = c.n_h // c.n_kv
-    for b, j in sample_units(pre, c.n_kv, 3, 37):
+    for b, j in units:
         n = int(pre[b]) + 1
-        blocks = torch.from_numpy(table[b, :need[b]].astype(np.int64)).cuda()
-        kb = bits(K.index_select(0, blocks)[:, j].reshape(-1, c.d)[:n])
-        vb = bits(V.index_select(0, blocks)[:, j].reshape(-1, c.d)[:n])
-        o_ref, l_ref = oracle.decode(bits(q[b, j * G:(j + 1) * G])[None], kb[None, None],
+        slot_blk, slot_off = int(table[b, pre[b] // beta]), int(pre[b]) % beta
+        assert np.array_equal(bits(K[slot_blk, j, slot_off]), snap[("kn", b, j)])
+        assert np.array_equal(bits(V[slot_blk, j, slot_off]), snap[("vn", b, j)])
+        kb = np.concatenate([snap[("K", b, j)], snap[("kn", b, j)][None]])
+        vb = np.concatenate([snap[("V", b, j)], snap[("vn", b, j)][None]])
+        o_ref, l_ref = oracle.decode(q_h[b, j * G:(j + 1) * G][None], kb[None, None],
                                      vb[None, None], np.array([n], np.int32), c.scale)
         compare(oracle.to_f64(bits(out[b, j * G:(j + 1) * G])), o_ref[0], 2e-2, f"paged b={b} j={j}")
         compare_lse(host(lse[b, j * G:(j + 1) * G]), l_ref[0], 4e-3)

@@ -82,12 +82,13 @@ def test_select_fullsize_sampled_rows():
     scores = torch.randn(B, R, L, generator=g, device="cuda", dtype=torch.float32)
     out = torch.empty(B, R, K, dtype=torch.int32, device="cuda")
     lens = torch.full((B,), L, dtype=torch.int32, device="cuda")
+    units = [(0, 0), (3, 5), (7, 7)]
+    rows = {u: host(scores[u[0]:u[0] + 1, u[1]:u[1] + 1]) for u in units}   # before the call
     kvc.kvc_topk_select(scores, lens, out)
     torch.cuda.synchronize()
     got = host(out)
-    for b, j in [(0, 0), (3, 5), (7, 7)]:
-        row = host(scores[b:b + 1, j:j + 1])
-        want = oracle.topk_select(row, np.array([L]), K)
+    for b, j in units:
+        want = oracle.topk_select(rows[(b, j)], np.array([L]), K)
         assert np.array_equal(got[b, j], want[0, 0]), (b, j)
 
 
