@@ -26,10 +26,7 @@ namespace kvc {
 // ---------------------------------------------------------------------------
 template <int D>
 struct MergeLds {
-  union {
-    float o[4][kMaxGroup][D];          // per-wave accumulators
-    float w[kMaxGroup][kMaxSplits];    // split lse values while merging
-  };
+  float o[4][kMaxGroup][D];            // per-wave accumulators
   float m[4][kMaxGroup];
   float l[4][kMaxGroup];
   int last;
@@ -141,55 +138,99 @@ __device__ void finish_split(const DenseParams& p, int b, int j, int split,
   __syncthreads();
   if (!L.last) return;
 
-  // Last workgroup: stage the split lse values of the G heads in LDS (all
-  // loads in flight together), then sum the partial rows in batches of 4.
-  const size_t bh0 = (size_t)b * p.n_h + (size_t)j * p.G;
-  for (int e = t; e < p.G * nsplit; e += blockDim.x) {
-    const int h2 = e / nsplit, s = e - h2 * nsplit;
-    L.w[h2][s] = load_coherent1(wl, (uint32_t)(((bh0 + h2) * p.P_max + s) * 4));
-  }
-  __syncthreads();
-  if (active) {
-    const size_t base = bh * p.P_max;
-    float M = kNegInf;
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, L.w[hl][s]);
-    const float Mu = (M == kNegInf) ? 0.f : M;
-    float Z = 0.f;
+  // Last workgroup.  Thread row hr (16 rows of 16 threads, CPT columns
+  // each) serves head hr / R and takes every R-th split from hr % R, where
+  // R = 16 / G rows per head when G divides 16 (else 1).  A thread's lse
+  // values and partial rows go out together, eight splits per batch, so a
+  // sequence of up to 8 * R splits is merged in one round trip; the R rows
+  // of a head are then combined through LDS.
+  const int G = p.G;
+  const int R = (16 % G == 0) ? 16 / G : 1;
+  const int hm = hl / R, sg = hl - hm * R;
+  const bool mact = hm < G;
+  const size_t bhm = (size_t)b * p.n_h + (size_t)j * G + hm;
+  float M = kNegInf, Z = 0.f;
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) o[c] = 0.f;
-    for (int s0 = 0; s0 < nsplit; s0 += 4) {
-      f32x4 v[4][CPT / 4];
+  for (int c = 0; c < CPT; ++c) o[c] = 0.f;
+  if (mact) {
+    const size_t base = bhm * p.P_max;
+    for (int s0 = sg; s0 < nsplit; s0 += 8 * R) {
+      float lv[8];
+      f32x4 v[8][CPT / 4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int su = min(s0 + u, nsplit - 1);
+      for (int u = 0; u < 8; ++u) {
+        const int su = min(s0 + u * R, nsplit - 1);
+        lv[u] = load_coherent1(wl, (uint32_t)((base + su) * 4));
 #pragma unroll
         for (int c = 0; c < CPT / 4; ++c)
           v[u][c] = load_coherent4(wo, (uint32_t)(((base + su) * D + c0 + 4 * c) * 4));
       }
+      float bm = kNegInf;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float e = (s0 + u < nsplit) ? __builtin_amdgcn_exp2f(L.w[hl][s0 + u] - Mu) : 0.f;
+      for (int u = 0; u < 8; ++u)
+        if (s0 + u * R < nsplit) bm = fmaxf(bm, lv[u]);
+      const float Mn = fmaxf(M, bm);
+      const float Mu = (Mn == kNegInf) ? 0.f : Mn;
+      const float a = __builtin_amdgcn_exp2f(M - Mu);
+      Z *= a;
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) o[c] *= a;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float e = (s0 + u * R < nsplit) ? __builtin_amdgcn_exp2f(lv[u] - Mu) : 0.f;
         Z += e;
 #pragma unroll
         for (int c = 0; c < CPT / 4; ++c)
 #pragma unroll
           for (int k = 0; k < 4; ++k) o[4 * c + k] += e * v[u][c][k];
       }
+      M = Mn;
     }
+  }
+  if (R > 1) {
+    // (L.o[0] is free: the waves' rows were consumed before the ticket)
+    if (mact) {
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) L.o[0][hl][c0 + c] = o[c];
+      if ((t & 15) == 0) {
+        L.m[0][hl] = M;
+        L.l[0][hl] = Z;
+      }
+    }
+    __syncthreads();
+    if (mact && sg == 0) {
+      float Mt = kNegInf;
+      for (int rr = 0; rr < R; ++rr) Mt = fmaxf(Mt, L.m[0][hl + rr]);
+      const float Mu = (Mt == kNegInf) ? 0.f : Mt;
+      Z = 0.f;
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) o[c] = 0.f;
+      for (int rr = 0; rr < R; ++rr) {
+        const float e = __builtin_amdgcn_exp2f(L.m[0][hl + rr] - Mu);
+        Z += e * L.l[0][hl + rr];
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) o[c] += e * L.o[0][hl + rr][c0 + c];
+      }
+      M = Mt;
+    }
+  }
+  if (mact && sg == 0) {
     const float inv = Z > 0.f ? 1.f / Z : 0.f;
 #pragma unroll
     for (int c = 0; c < CPT; ++c) o[c] *= inv;
-    write_final<OutT, D>(p, bh, o, Z > 0.f ? M + __log2f(Z) : kNegInf);
+    write_final<OutT, D>(p, bhm, o, Z > 0.f ? M + __log2f(Z) : kNegInf);
   }
   if (t == 0) *ticket = 0;
 }
 
 // Length attended by this workgroup.  Plain decode: seq_lens[b] (the caller
 // appended already).  Fused append-and-attend: n = seq_lens[b] is the slot
-// of the new token; the split that owns slot n writes the new K/V row (and,
-// with WAIT_WRITE, waits for it before any of its waves reads it; the MFMA
-// kernel instead replaces that row's registers with k_new/v_new after
-// loading), and the attended length is n + 1.  A full cache
+// of the new token and the attended length is n + 1.  With WAIT_WRITE the
+// split that owns slot n writes the new K/V row here and waits for it before
+// any of its waves reads it back; otherwise (the MFMA kernel) that row is
+// never read from the cache: the splits cover the n cached rows, and the
+// last of them attends the new row from the k_new/v_new registers and
+// stores it to the cache from the same registers.  A full cache
 // (n outside [0, L_max)) writes nothing, attends the stored positions and
 // sets flag bit 0.
 //
@@ -221,7 +262,13 @@ __device__ inline int attended_length(const DenseParams& p, int b, int j, int sp
     ls.unit_prev = 0;
     if (threadIdx.x == 0)
       ls.unit_prev = atomicAdd(p.ws_ucnt + (size_t)b * p.n_kv + j, 1);
-    if (ok && split == dense_num_splits(n_raw + 1, dense_split_size(n_raw + 1, p.S, p.P_max, p.even)) - 1) {
+    // The writer is the last split of the n_raw + 1 attended rows.  Without
+    // WAIT_WRITE the kernel writes the row itself, after its loads are out
+    // (a store of data still being loaded would hold back every later load
+    // of the wave).
+    const int rows = n_raw + 1;
+    if (WAIT_WRITE && ok &&
+        split == dense_num_splits(rows, dense_split_size(rows, p.S, p.P_max, p.even)) - 1) {
       constexpr int U = D * (int)sizeof(T) / 16;    // 16-byte pieces per row
       const size_t unit = (size_t)b * p.n_kv + j;
       const size_t dst = (unit * p.L_max + n_raw) * U;
@@ -230,10 +277,8 @@ __device__ inline int attended_length(const DenseParams& p, int b, int j, int sp
         reinterpret_cast<u32x4*>(p.k)[dst + t] = reinterpret_cast<const u32x4*>(p.k_new)[unit * U + t];
       else if (t < 2 * U)
         reinterpret_cast<u32x4*>(p.v)[dst + t - U] = reinterpret_cast<const u32x4*>(p.v_new)[unit * U + t - U];
-      if constexpr (WAIT_WRITE) {   // otherwise the reader patches the row in registers
-        wait_vm_all();
-        __syncthreads();
-      }
+      wait_vm_all();
+      __syncthreads();
     }
     if (!ok && j == 0 && split == 0 && threadIdx.x == 0 && p.flag) atomicOr(p.flag, 1);
     return ok ? n_raw + 1 : min(max(n_raw, 0), p.L_max);
@@ -408,11 +453,11 @@ __device__ inline void load_paged(Chunk& c, const PageIdx& x, int cs, int end,
   }
 }
 
-// Fused append: the chunk holding the new token's slot takes that row from
-// k_new/v_new (the cache copy is being written concurrently).  Lane (r, g)
-// holds K rows pi(a, r) at columns kk*32 + g*8 and V rows g*8 + e at columns
-// r*8; knr/vnr are its 16-byte pieces of the new rows (loaded once), swapped
-// in with selects so no load is waited on early.
+// Fused append: the new token's row is attended from k_new/v_new, never
+// read back from the cache (whose copy is being written concurrently).  Lane
+// (r, g) holds K rows pi(a, r) at columns kk*32 + g*8 and V rows g*8 + e at
+// columns r*8; knr/vnr are its 16-byte pieces of the new rows (loaded once),
+// placed at chunk row `pos` with selects.
 __device__ inline void patch_new_row(Chunk& c, int pos, const u32x4 (&knr)[4],
                                      const u32x4& vnr, int r, int g) {
 #pragma unroll
@@ -603,10 +648,15 @@ __global__ __launch_bounds__(256, 2) void dense_mfma_kernel(DenseParams p) {
   LengthState ls;
   const int n = attended_length<APPEND, 128, uint16_t, false>(p, b, j, split, ls);
   const int lo = TOPK ? 0 : window_low(p, b, n);    // window mode only (not fused)
-  const int count = TOPK ? p.K : n - lo;
+  // Fused append: the new row (slot n - 1) is attended from registers, so
+  // the splits cover only the rows already in the cache.  A sequence of 4096
+  // cached rows then splits into whole 256-row pieces instead of spilling a
+  // one-row chunk into an extra load round.
+  const bool reg_new = APPEND && ls.ok;
+  const int count = TOPK ? p.K : n - lo - (reg_new ? 1 : 0);
   const int S = dense_split_size(count, p.S, p.P_max, p.even);
   const int nsplit = dense_num_splits(count, S);
-  if (split >= nsplit || count == 0) {
+  if (split >= nsplit || (count == 0 && !reg_new)) {
     if (split == 0) write_empty<uint16_t, 128>(p, b, j);
     complete_length<APPEND>(p, b, j, ls);
     return;
@@ -625,12 +675,15 @@ __global__ __launch_bounds__(256, 2) void dense_mfma_kernel(DenseParams p) {
   // (paged: the whole pool, at most 2^31 bytes, checked on the host)
   const uint32_t pool_bytes =
       PAGED ? ((uint32_t)p.num_blocks * (uint32_t)p.n_kv << p.page_shift) * kRowBytes : 0u;
+  // Rows a load may touch: the attended ones, less the new row of a fused
+  // append (slot n - 1 is never read back; rows past the range read zeros).
+  const uint32_t n_rows = (uint32_t)(n - (reg_new ? 1 : 0));
   const __amdgpu_buffer_rsrc_t kr =
       PAGED ? make_rsrc(p.k, pool_bytes)
-            : make_rsrc((const char*)p.k + unit * unit_bytes, (uint32_t)n * kRowBytes);
+            : make_rsrc((const char*)p.k + unit * unit_bytes, n_rows * kRowBytes);
   const __amdgpu_buffer_rsrc_t vr =
       PAGED ? make_rsrc(p.v, pool_bytes)
-            : make_rsrc((const char*)p.v + unit * unit_bytes, (uint32_t)n * kRowBytes);
+            : make_rsrc((const char*)p.v + unit * unit_bytes, n_rows * kRowBytes);
   // (FP4: the scale rows, 8 bytes per position)
   const __amdgpu_buffer_rsrc_t ksr =
       FP4 ? make_rsrc((const char*)p.k_scales + unit * (size_t)p.L_max * 8, (uint32_t)n * 8u) : kr;
@@ -689,10 +742,6 @@ __global__ __launch_bounds__(256, 2) void dense_mfma_kernel(DenseParams p) {
       expand_chunk(c, x);
       compute_chunk<false>(x, at, end, qop, p.scale_log2, g, st);
     } else {
-      // the chunk holding the new slot takes that row from k_new/v_new
-      if constexpr (APPEND)
-        if (new_slot >= at && new_slot < at + kDenseChunk)
-          patch_new_row(c, new_slot - at, knr, vnr, r, g);
       compute_chunk<TOPK || PAGED>(c, at, end, qop, p.scale_log2, g, st);
     }
   };
@@ -758,6 +807,32 @@ __global__ __launch_bounds__(256, 2) void dense_mfma_kernel(DenseParams p) {
       if (cs >= end) break;
     }
   }
+  if constexpr (APPEND) {
+    // The last split folds in the new row as a one-row chunk, on the wave
+    // with the fewest cached chunks (wave 3 when they are even), and that
+    // wave writes the row to the cache: lanes r = 0 hold all 16 pieces of
+    // the K row, lanes g = 0 all 16 of the V row.
+    const int chunks = (end - start + kDenseChunk - 1) / kDenseChunk;
+    const int new_wave = (chunks & 3) ? (chunks & 3) : 3;
+    if (new_slot >= 0 && split == nsplit - 1 && wave == new_wave) {
+      const size_t dst = (unit * p.L_max + new_slot) * 16;
+      if (r == 0) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) reinterpret_cast<u32x4*>(p.k)[dst + kk * 4 + g] = knr[kk];
+      }
+      if (g == 0) reinterpret_cast<u32x4*>(p.v)[dst + r] = vnr;
+      Chunk c;
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) c.k[a][kk] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) c.v[e] = u32x4{0u, 0u, 0u, 0u};
+      c.vmask = 0xFF;
+      patch_new_row(c, 0, knr, vnr, r, g);
+      compute_chunk<false>(c, new_slot, new_slot + 1, qop, p.scale_log2, g, st);
+    }
+  }
   if constexpr (TOPK || PAGED) {
     if (p.flag && __any(bad) && lane == 0) atomicOr(p.flag, 2);
   }
@@ -772,9 +847,10 @@ __global__ __launch_bounds__(256, 2) void dense_mfma_kernel(DenseParams p) {
   for (int m = 0; m < 8; ++m)
 #pragma unroll
     for (int i = 0; i < 4; ++i) L.o[wave][r][(4 * g + i) * 8 + m] = st.acc[m][i];
-  complete_length<APPEND>(p, b, j, ls);
   __syncthreads();
   finish_split<uint16_t, 128>(p, b, j, split, nsplit, L);
+  // (after the merge: its atomic is off the path to the output)
+  complete_length<APPEND>(p, b, j, ls);
 }
 
 // ---------------------------------------------------------------------------
@@ -927,9 +1003,10 @@ __global__ __launch_bounds__(256) void dense_generic_kernel(DenseParams p) {
 #pragma unroll
     for (int u = 0; u < U; ++u) L.o[wave][h][lane + 64 * u] = o[h][u];
   }
-  complete_length<APPEND>(p, b, j, ls);
   __syncthreads();
   finish_split<T, D>(p, b, j, split, nsplit, L);
+  // (after the merge: its atomic is off the path to the output)
+  complete_length<APPEND>(p, b, j, ls);
 }
 
 // ---------------------------------------------------------------------------

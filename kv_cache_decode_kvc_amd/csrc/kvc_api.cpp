@@ -81,8 +81,10 @@ SplitPlan plan_splits(int kind, int64_t units, int64_t n_max) {
     // no more splits than n_max has minimum-size pieces
     const int64_t P_fill = dense_splits(n_max, kDenseMinEvenSplit);
     if (P > P_fill) P = P_fill;
-    // the splits n_max takes; every shorter length fits in as many
-    P = dense_splits(n_max, dense_split_size((int)n_max, (int)kDenseMinEvenSplit, (int)P, 1));
+    // Every length up to n_max fits in P splits.  P is not trimmed to the
+    // splits n_max itself takes: a fused append attends n_max - 1 cached
+    // rows, which may need all P (4096 rows: 16 x 256, where 4097 takes
+    // 15 x 288).
     return {(int)kDenseMinEvenSplit, P, 1};
   }
   int64_t S = kDenseMinSplit;

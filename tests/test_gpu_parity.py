@@ -116,6 +116,8 @@ DENSE_CASES = [
     (16, 1, 128, "bf16", [5, 300], 512),                 # MQA G=16
     (8, 4, 128, "bf16", [100, 0, 255], 256),             # G=2
     (12, 3, 128, "bf16", [77, 600], 700),                # G=4
+    (15, 5, 128, "bf16", [700, 33], 800),                # G=3 (does not divide 16)
+    (12, 1, 128, "bf16", [1999, 40], 2000),              # G=12, 16 splits: two merge batches
     (8, 2, 64, "bf16", [0, 1, 129, 500], 600),           # generic kernel, bf16 d=64
     (16, 4, 128, "f32", [0, 64, 65, 999], 1000),         # generic kernel, f32 d=128
     (6, 6, 64, "f32", [1, 2, 3], 8),                     # tiny, many empty chunk slots
@@ -142,6 +144,17 @@ def test_dense_split_sweep(split):
     out, lse, *_ = run_dense_step(case, 1 / math.sqrt(128), split=split)
     o_ref, l_ref, *_ = oracle_dense_step(case, 1 / math.sqrt(128))
     compare(host_f64(out), o_ref, 2e-2, f"split {split}")
+    compare_lse(host(lse), l_ref, lse_tol("bf16"))
+
+
+@pytest.mark.parametrize("n_h,n_kv", [(32, 32), (16, 1), (15, 5)])
+def test_dense_many_splits_merge(n_h, n_kv):
+    """Up to 250 splits of 32 positions: the merge takes several batches of
+    partial rows per thread, with 1, 16 and 3 heads per KV head."""
+    case = syn.dense_case(2, n_h, n_kv, 128, 8000, [7999, 300], "bf16", cfg_id=94)
+    out, lse, *_ = run_dense_step(case, 1 / math.sqrt(128), split=32)
+    o_ref, l_ref, *_ = oracle_dense_step(case, 1 / math.sqrt(128))
+    compare(host_f64(out), o_ref, 2e-2, f"many splits {n_h}/{n_kv}")
     compare_lse(host(lse), l_ref, lse_tol("bf16"))
 
 
@@ -396,6 +409,10 @@ FUSED_CASES = [
     (64, 8, 128, "bf16", [0, 31, 255, 256, 1000, 2047, 2048], 2048, 0),   # incl. full cache
     (64, 8, 128, "bf16", [0, 31, 255, 256, 1000, 2047], 2048, 256),
     (16, 1, 128, "bf16", [511, 3], 512, 0),
+    # last splits of 0..4 chunks: every choice of the wave that attends the
+    # new row from registers
+    (16, 2, 128, "bf16", [0, 1, 95, 96, 97, 200, 319, 320], 400, 96),
+    (16, 2, 128, "bf16", [0, 31, 32, 63, 64, 159, 160, 161], 400, 160),
     (8, 2, 64, "bf16", [0, 129, 599, 600], 600, 0),              # generic kernel
     (16, 4, 128, "f32", [0, 999, 64], 1000, 0),                  # generic kernel f32
 ]
