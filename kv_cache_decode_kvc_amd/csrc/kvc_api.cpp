@@ -572,7 +572,7 @@ int kvc_topk_select(const float* scores, const int32_t* seq_lens, const int32_t*
     return KVC_ERR_MISALIGNED;
   if (B == 0) return KVC_OK;
   SelectParams p{scores, seq_lens, pool, idx_out, B, R, L_max, K, pool ? P : 0,
-                 pool ? pool_block : 1, words};
+                 pool ? pool_block : 1, words, select_map_words(L_max)};
   return launch_status(launch_topk_select(p, static_cast<hipStream_t>(stream)));
 }
 

@@ -84,6 +84,12 @@ struct DenseParams {
 
 // Pool bitmap words the selection kernel holds in LDS (one bit per block).
 constexpr int kSelectPoolWords = 12288;
+// Selection map: one bit per position, whole 16384-position steps, for rows
+// of at most 2^18 positions (longer rows take the multi-pass path only).
+constexpr int kSelectMapMax = 1 << 18;
+inline int select_map_words(int L_max) {
+  return L_max > kSelectMapMax ? 0 : (L_max + 16383) / 16384 * 512;
+}
 
 struct SelectParams {
   const float* scores;      // [B, R, L_max]
@@ -91,6 +97,7 @@ struct SelectParams {
   const int32_t* pool;      // [B, R, P] block ids, or null
   int32_t* out;             // [B, R, K]
   int B, R, L_max, K, P, pool_block, pool_words;
+  int sel_words;            // > 0: one-bit-per-position selection map (L_max <= 2^18)
 };
 
 struct MlaParams {

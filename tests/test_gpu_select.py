@@ -58,6 +58,26 @@ def test_select_matches_oracle(kind):
     assert np.array_equal(got, want), np.argwhere(got != want)[:5]
 
 
+@pytest.mark.parametrize("kind", ["overflow", "long"])
+def test_select_multipass_paths(kind):
+    """Rows the one-extra-pass route cannot take: a threshold bin of more
+    than 8192 equal keys (20000 ones among zeros), and rows longer than 2^18
+    positions; both go through the further histogram passes and the ordered
+    row walk."""
+    rng = np.random.default_rng(7 if kind == "overflow" else 8)
+    if kind == "overflow":
+        B, R, L, K = 2, 2, 40000, 1000
+        sc = (rng.random((B, R, L)) < 0.5).astype(np.float32)
+        lens = [40000, 33333]
+    else:
+        B, R, L, K = 1, 2, 300000, 2048
+        sc = rng.standard_normal((B, R, L)).astype(np.float32)
+        lens = [299999]
+    got = run_select(sc, lens, K)
+    want = oracle.topk_select(sc, np.asarray(lens), K)
+    assert np.array_equal(got, want), np.argwhere(got != want)[:5]
+
+
 def test_select_pool_variant():
     rng = np.random.default_rng(5)
     B, R, L, K, blk = 2, 3, 20000, 512, 8
