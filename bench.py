@@ -742,13 +742,13 @@ def read_ceiling(torch, kvc, nbytes=4 << 30, reps=10):
 
 def measured_traffic(name):
     """HBM bytes per launch of the workload's dominant kernel from the
-    committed counter runs (profiles/traffic.json), or None if the kernel
+    committed counter runs (profiles/traffic.json), or None if that kernel's
     sources changed since those counters were taken."""
     try:
         from kv_cache_decode_kvc_amd.profile_summary import source_hash
         with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
             rec = json.load(f).get(name)
-        if not rec or rec["source_sha256"] != source_hash():
+        if not rec or rec["source_sha256"] != source_hash(name):
             return None
         return rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
     except (OSError, ValueError, KeyError):

@@ -60,7 +60,8 @@ constexpr int kWaveCand = kSelCand / kSelWaves;
 __device__ inline uint32_t score_key(float f) {
   uint32_t u = __float_as_uint(f);
   if ((u << 1) == 0) u = 0;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  // negative: all bits flipped; positive: sign bit set
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 
 struct SelLds {
@@ -251,11 +252,23 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(SelectParams p
     __syncthreads();
     uint32_t* myhist = hcopy + (tid >> 7) * kBins;
     stream_row(sr, n, [&](const float (&v)[kSelUnroll], int base) {
+      if (bound && !p.pool && base + kSelStep <= n) {
+        // first pass over a whole step without a pool: every position
+        // counts, so one compare per key (the per-key instruction count is
+        // what bounds these passes: one busy workgroup per compute unit)
+        const uint32_t klb = dlb << 21;
 #pragma unroll
-      for (int u = 0; u < kSelUnroll; ++u) {
-        const uint32_t k = key_of(base + u * kSelThreads + tid, v[u]);
-        if (k != 0u && (k & pmask) == prefix && (k >> 21) >= dlb)
-          atomicAdd(&myhist[(k >> sh) & dmask], 1u);
+        for (int u = 0; u < kSelUnroll; ++u) {
+          const uint32_t k = score_key(v[u]);
+          if (k >= klb) atomicAdd(&myhist[k >> 21], 1u);
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < kSelUnroll; ++u) {
+          const uint32_t k = key_of(base + u * kSelThreads + tid, v[u]);
+          if (k != 0u && (k & pmask) == prefix && (k >> 21) >= dlb)
+            atomicAdd(&myhist[(k >> sh) & dmask], 1u);
+        }
       }
       if (bound && base == 0 && n > kSelStep) {
         __syncthreads();
@@ -289,7 +302,33 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(SelectParams p
     uint32_t* const wkey = ckey + wave * kWaveCand;
     uint32_t* const wpos = cpos + wave * kWaveCand;
     int wc = 0;                       // this wave's list entries so far
+    // above: key > ka; in bin d1: key - kb < span (both empty tests when
+    // every candidate is kept)
+    const uint32_t ka = all ? 0u : ((d1 << 21) | 0x1FFFFFu);
+    const uint32_t kb = d1 << 21;
+    const uint32_t span = all ? 0u : (1u << 21);
     stream_row(sr, n, [&](const float (&v)[kSelUnroll], int base) {
+      if (!p.pool && base + kSelStep <= n) {
+        // whole step without a pool: every position is a candidate
+#pragma unroll
+        for (int u = 0; u < kSelUnroll; ++u) {
+          const uint32_t k = score_key(v[u]);
+          const uint64_t ba = __ballot(k > ka);
+          const bool cand = k - kb < span;
+          const uint64_t bc = __ballot(cand);
+          const int t0 = base + u * kSelThreads + wave * 64;
+          if (lane == 0) *reinterpret_cast<uint64_t*>(sel + (t0 >> 5)) = ba;
+          if (cand) {
+            const int s = wc + __popcll(bc & below);
+            if (s < kWaveCand) {
+              wkey[s] = k;
+              wpos[s] = (uint32_t)(t0 + lane);
+            }
+          }
+          wc += __popcll(bc);
+        }
+        return;
+      }
 #pragma unroll
       for (int u = 0; u < kSelUnroll; ++u) {
         const int t = base + u * kSelThreads + tid;

@@ -9,8 +9,9 @@ DIR are the -d directories of three rocprofv3 runs of the same bench command
 (calls, average/min/max duration) and the HBM bytes per dispatch from the two
 counters, each scaled by what the counter reads for the bench's known-size
 copy (kvc_copy of 1 GiB).  It also records, in profiles/traffic.json, the
-dominant kernel's scaled bytes per launch together with a hash of the kernel
-sources, which bench.py uses only while the sources are unchanged.
+dominant kernel's scaled bytes per launch together with a hash of that
+kernel's sources (its own file, the shared headers and the host side), which
+bench.py uses only while those sources are unchanged.
 """
 from __future__ import annotations
 
@@ -38,12 +39,21 @@ DOMINANT = {
 }
 
 
-def source_hash() -> str:
-    """sha256 over the kernel sources and the public header, in name order."""
+# source file of each workload's dominant kernel
+KERNEL_SOURCE = {w: "decode_dense.hip" for w in DOMINANT}
+KERNEL_SOURCE.update({"C4": "decode_mla.hip", "C5S": "select.hip"})
+# sources every kernel depends on (shared headers and the host side)
+COMMON_SOURCES = ["kvc_device.h", "kvc_internal.h", "kvc_api.cpp"]
+
+
+def source_hash(workload: str) -> str:
+    """sha256 over the public header, the shared sources and the workload's
+    dominant-kernel source, in that order: a change to another kernel's
+    source leaves the recorded counters of this one valid."""
     h = hashlib.sha256()
-    files = [os.path.join(ROOT, "include", "kvc.h")]
     csrc = os.path.join(HERE, "csrc")
-    files += sorted(os.path.join(csrc, f) for f in os.listdir(csrc))
+    files = [os.path.join(ROOT, "include", "kvc.h")]
+    files += [os.path.join(csrc, f) for f in COMMON_SOURCES + [KERNEL_SOURCE[workload]]]
     for f in files:
         h.update(os.path.basename(f).encode())
         with open(f, "rb") as fh:
@@ -128,7 +138,8 @@ def main():
                       f"roofline.kernel_us = {d['roofline']['kernel_us']} (HIP events over back-to-back "
                       f"launches, includes the graph's inter-kernel gap), achieved "
                       f"{d['roofline']['achieved']} GB/s, value {d['value']} GB/s."]
-    lines += ["", f"Kernel sources sha256: `{source_hash()}`", ""]
+    lines += ["", f"Kernel sources sha256 (include/kvc.h, {', '.join(COMMON_SOURCES)}, "
+                  f"{KERNEL_SOURCE[a.workload]}): `{source_hash(a.workload)}`", ""]
     os.makedirs(os.path.dirname(os.path.abspath(a.out)), exist_ok=True)
     with open(a.out, "w") as f:
         f.write("\n".join(lines))
@@ -138,7 +149,7 @@ def main():
     data[a.workload] = {"kernel": dom_name, "fetch_bytes_per_launch": round(fb),
                         "write_bytes_per_launch": round(wb),
                         "avg_us_rocprof": round(dom_stats[2], 3),
-                        "source_sha256": source_hash()}
+                        "source_sha256": source_hash(a.workload)}
     with open(tj, "w") as f:
         json.dump(data, f, indent=1, sort_keys=True)
     print(f"wrote {a.out}")
