@@ -341,8 +341,9 @@ int kvc_decode_attn_topk(const void* q, const void* k_cache,
  * the row's pool entries qualify (entries outside [0, ceil(L_max /
  * pool_block)) are ignored).  Scores are compared exactly (-0 equals +0);
  * NaN scores are outside the contract.  The result is deterministic.
- *   K >= 1; pool mode: P >= 1, pool_block >= 1, ceil(L_max / pool_block)
- *   <= 393216 (else KVC_ERR_UNSUPPORTED).
+ *   K >= 1; L_max < 2^29 (else KVC_ERR_UNSUPPORTED); pool mode: P >= 1,
+ *   pool_block >= 1, ceil(L_max / pool_block) <= 393216 (else
+ *   KVC_ERR_UNSUPPORTED).
  */
 int kvc_topk_select(const float* scores, const int32_t* seq_lens, const int32_t* pool,
                     int P, int pool_block, int32_t* idx_out, int B, int R, int L_max,

@@ -559,6 +559,8 @@ int kvc_topk_select(const float* scores, const int32_t* seq_lens, const int32_t*
                     int P, int pool_block, int32_t* idx_out, int B, int R, int L_max,
                     int K, void* stream) {
   if (B < 0 || R < 1 || L_max < 1 || K < 1) return KVC_ERR_BAD_SHAPE;
+  // rows are read through 32-bit byte offsets (with a step of slack)
+  if (L_max >= kSelectMaxRow) return KVC_ERR_UNSUPPORTED;
   int words = 0;
   if (pool) {
     if (P < 1 || pool_block < 1) return KVC_ERR_BAD_SHAPE;

@@ -84,6 +84,9 @@ struct DenseParams {
 
 // Pool bitmap words the selection kernel holds in LDS (one bit per block).
 constexpr int kSelectPoolWords = 12288;
+// Longest score row the selection kernel reads (positions; its loads use
+// 32-bit byte offsets).
+constexpr int kSelectMaxRow = 1 << 29;
 // Selection map: one bit per position, whole 16384-position steps, for rows
 // of at most 2^18 positions (longer rows take the multi-pass path only).
 constexpr int kSelectMapMax = 1 << 18;

@@ -337,5 +337,7 @@ def test_select_validation(L):
     assert sel(pool=A4, P=0) == -2
     assert sel(pool=A4, P=16, pb=0) == -2
     assert sel(pool=A4, P=16, pb=1, L=1 << 20) == -4     # pool bitmap beyond LDS
+    assert sel(L=1 << 29) == -4                          # rows beyond 32-bit byte offsets
+    assert sel(L=(1 << 29) - 1, B=0) == 0
     assert sel(s=ctypes.c_void_p(0x10002)) == -6
     assert sel(B=0) == 0
