@@ -515,21 +515,24 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_kernel(MlaParams p) {
 
   // Several splits: publish this one; mla_merge_kernel (launched next on
   // the same stream, so the kernel boundary makes the stores visible to every
-  // XCD) combines them.  A split's partial block is in register order: slot k
-  // of lane l of wave w (k = 4 * tile + quad, 64 slots of 4 floats) is at
-  // ((w * 64 + k) * 64 + l) * 4 floats, so every store moves 1 KB contiguous
-  // per wave.
+  // XCD) combines them.  The normalised partial is stored in bf16 (one more
+  // rounding of the same size as the output's; the merge sums in float32),
+  // which halves the partial traffic both ways.  A split's partial block is
+  // in register order: slot k of lane l of wave w (k = 4 * tile + quad, 64
+  // slots of 4 values) is at ((w * 64 + k) * 64 + l) * 4 values, so every
+  // store moves 512 bytes contiguous per wave.
   {
     const size_t unit_hg = (size_t)b * groups + hg;
-    constexpr size_t kBlock = (size_t)NW * 64 * 256;     // floats per split block
-    f32x4* blk = reinterpret_cast<f32x4*>(p.ws_o + (unit_hg * p.P_max + split) * kBlock) +
+    constexpr size_t kBlock = (size_t)NW * 64 * 256;     // values per split block
+    u32x2* blk = reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(p.ws_o) +
+                                          (unit_hg * p.P_max + split) * kBlock) +
                  wave * 64 * 64 + lane;
 #pragma unroll
     for (int t = 0; t < kColTiles; ++t)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4)
-        blk[(4 * t + q4) * 64] = f32x4{acc[t][4 * q4] * inv, acc[t][4 * q4 + 1] * inv,
-                                       acc[t][4 * q4 + 2] * inv, acc[t][4 * q4 + 3] * inv};
+        blk[(4 * t + q4) * 64] = u32x2{pack_bf16x2(acc[t][4 * q4] * inv, acc[t][4 * q4 + 1] * inv),
+                                       pack_bf16x2(acc[t][4 * q4 + 2] * inv, acc[t][4 * q4 + 3] * inv)};
     if (g == 0) p.ws_lse[(unit_hg * p.P_max + split) * kHpw + wave * 32 + r] = lse2;
   }
 }
@@ -578,20 +581,21 @@ void mla_merge_kernel(MlaParams p) {
   }
   const float Mu = (M == kNegInf) ? 0.f : M;
 
-  const f32x4* base = reinterpret_cast<const f32x4*>(p.ws_o + unit_hg * p.P_max * kBlock) +
+  const u32x2* base = reinterpret_cast<const u32x2*>(reinterpret_cast<const uint16_t*>(p.ws_o) +
+                                                     unit_hg * p.P_max * kBlock) +
                       wave * 64 * 64 + lane;
   f32x4 sum[8];
 #pragma unroll
   for (int m = 0; m < 8; ++m) sum[m] = f32x4{0.f, 0.f, 0.f, 0.f};
   float Z = 0.f;
   for (int s0 = 0; s0 < nsplit; s0 += 4) {
-    f32x4 v[4][8];
+    u32x2 v[4][8];
     float ls[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int su = min(s0 + u, nsplit - 1);
       ls[u] = lse_p[(size_t)su * kHpw];
-      const f32x4* blk = base + (size_t)su * (kBlock / 4);
+      const u32x2* blk = base + (size_t)su * (kBlock / 4);
 #pragma unroll
       for (int m = 0; m < 8; ++m) v[u][m] = blk[(8 * part + m) * 64];
     }
@@ -600,7 +604,9 @@ void mla_merge_kernel(MlaParams p) {
       const float w = (s0 + u >= nsplit || ls[u] == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(ls[u] - Mu);
       Z += w;
 #pragma unroll
-      for (int m = 0; m < 8; ++m) sum[m] += w * v[u][m];
+      for (int m = 0; m < 8; ++m)
+        sum[m] += w * f32x4{bf16_lo(v[u][m][0]), bf16_hi(v[u][m][0]),
+                            bf16_lo(v[u][m][1]), bf16_hi(v[u][m][1])};
     }
   }
   const float zi = Z > 0.f ? 1.f / Z : 0.f;

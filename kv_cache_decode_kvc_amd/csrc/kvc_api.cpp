@@ -181,7 +181,8 @@ MlaCheck check_mla_shape(int B, int n_h, int L_max, int d_c, int d_r, int dtype)
   c.P_max = plan.P;
   const int64_t groups = n_h / mla_heads_per_wg(n_h);
   if ((int64_t)B * groups * c.P_max >= kMaxOffset) { c.status = KVC_ERR_BAD_SHAPE; return c; }
-  c.ws = ws_layout((size_t)B * groups, (size_t)B, (size_t)n_h, (size_t)c.P_max, (size_t)d_c);
+  // (partial outputs are bf16: d_c values take the room of d_c / 2 floats)
+  c.ws = ws_layout((size_t)B * groups, (size_t)B, (size_t)n_h, (size_t)c.P_max, (size_t)d_c / 2);
   if (c.ws.total >= (size_t)kMaxOffset) { c.status = KVC_ERR_UNSUPPORTED; return c; }
   return c;
 }

@@ -111,7 +111,7 @@ struct MlaParams {
   float* lse;
   int32_t* ws_cnt;        // [B]
   float* ws_lse;          // [B * n_h * P_max]
-  float* ws_o;            // [B * n_h * P_max * d_c]
+  float* ws_o;            // [B * n_h * P_max * d_c] bf16 normalised partial outputs
   int B, n_h, L_max;
   int S, P_max;
   float scale_log2;
