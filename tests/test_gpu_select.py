@@ -78,6 +78,38 @@ def test_select_multipass_paths(kind):
     assert np.array_equal(got, want), np.argwhere(got != want)[:5]
 
 
+@pytest.mark.parametrize("seed", range(12))
+def test_select_random_sweep(seed):
+    """Seeded shapes across both passes' short and general steps: K from 1
+    to past the row, lengths off the 16384-position step, coarse ties,
+    negative-only and infinite scores, with and without a pool."""
+    rng = np.random.default_rng(1000 + seed)
+    B, R = int(rng.integers(1, 3)), int(rng.integers(1, 4))
+    L = int(rng.choice([700, 16384, 20000, 50001, 70000]))
+    K = int(rng.choice([1, 17, 256, 2048, L, L + 5]))
+    K = max(1, min(K, L))
+    sc = rng.standard_normal((B, R, L)).astype(np.float32)
+    kind = seed % 4
+    if kind == 1:
+        sc = np.round(sc * 8).astype(np.float32) / 8          # coarse ties
+    elif kind == 2:
+        sc = -np.abs(sc) - 1.0                                # every score negative
+    elif kind == 3:
+        sc.reshape(-1)[rng.integers(0, sc.size, 40)] = np.inf
+        sc.reshape(-1)[rng.integers(0, sc.size, 40)] = -np.inf
+    lens = [int(x) for x in rng.integers(0, L + 1, B)]
+    lens[0] = L
+    pool = None
+    if seed % 3 == 2:
+        nblk = -(-L // 8)
+        P = int(min(nblk, 600))
+        pool = np.stack([np.stack([rng.choice(nblk, P, replace=False) for _ in range(R)])
+                         for _ in range(B)]).astype(np.int32)
+    got = run_select(sc, lens, K, pool=pool, pool_block=8)
+    want = oracle.topk_select(sc, np.asarray(lens), K, pool=pool, pool_block=8)
+    assert np.array_equal(got, want), (seed, np.argwhere(got != want)[:5])
+
+
 def test_select_pool_variant():
     rng = np.random.default_rng(5)
     B, R, L, K, blk = 2, 3, 20000, 512, 8
