@@ -645,6 +645,19 @@ __global__ __launch_bounds__(256, 2) void dense_mfma_kernel(DenseParams p) {
   __shared__ MergeLds<128> L;
   int b, j, split;
   decode_unit(p, b, j, split);
+  // Top-k: a split's slots and the list do not depend on the sequence
+  // length, so the list entries of the first two chunks go out before the
+  // length is read (the two round trips overlap).
+  ChunkIdx I0, I1;
+  if constexpr (TOPK) {
+    const int St = dense_split_size(p.K, p.S, p.P_max, p.even);
+    const int l0 = threadIdx.x & 63;
+    const int cs0 = split * St + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * kDenseChunk;
+    const __amdgpu_buffer_rsrc_t ir0 =
+        make_rsrc(p.idx + ((size_t)b * p.n_kv + j) * p.K, (uint32_t)p.K * 4u);
+    load_idx(I0, cs0, ir0, l0 & 15, l0 >> 4);
+    load_idx(I1, cs0 + kDenseChunk * 4, ir0, l0 & 15, l0 >> 4);
+  }
   LengthState ls;
   const int n = attended_length<APPEND, 128, uint16_t, false>(p, b, j, split, ls);
   const int lo = TOPK ? 0 : window_low(p, b, n);    // window mode only (not fused)
@@ -747,11 +760,9 @@ __global__ __launch_bounds__(256, 2) void dense_mfma_kernel(DenseParams p) {
   };
   if constexpr (TOPK) {
     if (cs < end) {
-      // list entries two chunks ahead, rows one chunk ahead
+      // list entries two chunks ahead (the first two loaded at the start),
+      // rows one chunk ahead
       Chunk A, Bc;
-      ChunkIdx I0, I1;
-      load_idx(I0, cs, ir, r, g);
-      load_idx(I1, cs + kStride, ir, r, g);
       load_listed(A, I0, cs, end, n, kr, vr, r, g, bad);
       while (true) {
         load_idx(I0, cs + 2 * kStride, ir, r, g);
