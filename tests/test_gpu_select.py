@@ -78,6 +78,31 @@ def test_select_multipass_paths(kind):
     assert np.array_equal(got, want), np.argwhere(got != want)[:5]
 
 
+@pytest.mark.parametrize("kind", ["equal", "ties", "short", "pool"])
+def test_select_long_rows(kind):
+    """Rows of 140000 positions: every score equal (the lowest K positions;
+    the threshold bin overflows the lists), coarse ties, rows ending early,
+    and a pool."""
+    rng = np.random.default_rng({"equal": 21, "ties": 22, "short": 23, "pool": 25}[kind])
+    B, R, L, K = 2, 3, 140000, 2048
+    sc = rng.standard_normal((B, R, L)).astype(np.float32)
+    lens = [L, 100000]
+    pool = None
+    if kind == "equal":
+        sc[:] = 0.5
+    elif kind == "ties":
+        sc = np.round(sc * 4).astype(np.float32) / 4
+    elif kind == "short":
+        lens = [33000, 70000]
+    elif kind == "pool":
+        nblk = -(-L // 8)
+        pool = np.stack([np.stack([rng.choice(nblk, 2000, replace=False) for _ in range(R)])
+                         for _ in range(B)]).astype(np.int32)
+    got = run_select(sc, lens, K, pool=pool, pool_block=8)
+    want = oracle.topk_select(sc, np.asarray(lens), K, pool=pool, pool_block=8)
+    assert np.array_equal(got, want), (kind, np.argwhere(got != want)[:5])
+
+
 @pytest.mark.parametrize("seed", range(12))
 def test_select_random_sweep(seed):
     """Seeded shapes across both passes' short and general steps: K from 1
