@@ -58,8 +58,8 @@ constexpr int kWaveCand = kSelCand / kSelWaves;
 // Larger score -> larger key; -0 and +0 give the same key.  Every finite or
 // infinite score maps above 0, which marks non-candidates.
 __device__ inline uint32_t score_key(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u << 1) == 0) u = 0;
+  // adding +0 turns -0 into +0 and leaves every other value as it is
+  const uint32_t u = __float_as_uint(f + 0.0f);
   // negative: all bits flipped; positive: sign bit set
   return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
@@ -121,11 +121,12 @@ __device__ inline int find_bin(SelLds& L, int r) {
 }
 
 // r-th largest (1 <= r <= entries matching prefix under pmask) of the list
-// values val(i), i < m, refined digit by digit over the passes (sh, dm);
-// the passes must cover every bit outside pmask.  Returns the value; gt and
-// eq count the matching entries above it and equal to it.
-template <int NP, typename Val>
-__device__ uint32_t list_select(Val val, int m, int r, uint32_t prefix, uint32_t pmask,
+// values; each(f) calls f(value) once for every entry (spread over the
+// workgroup's threads).  Refined digit by digit over the passes (sh, dm),
+// which must cover every bit outside pmask.  Returns the value; gt and eq
+// count the matching entries above it and equal to it.
+template <int NP, typename Each>
+__device__ uint32_t list_select(Each each, int r, uint32_t prefix, uint32_t pmask,
                                 const int (&sh)[NP], const uint32_t (&dm)[NP], SelLds& L,
                                 int& gt, int& eq) {
   gt = 0;
@@ -134,10 +135,9 @@ __device__ uint32_t list_select(Val val, int m, int r, uint32_t prefix, uint32_t
   for (int pass = 0; pass < NP; ++pass) {
     for (int i = threadIdx.x; i < kBins; i += kSelThreads) L.hist[i] = 0u;
     __syncthreads();
-    for (int i = threadIdx.x; i < m; i += kSelThreads) {
-      const uint32_t x = val(i);
+    each([&](uint32_t x) {
       if ((x & pmask) == prefix) atomicAdd(&L.hist[(x >> sh[pass]) & dm[pass]], 1u);
-    }
+    });
     __syncthreads();
     find_bin(L, r);
     const uint32_t d = (uint32_t)L.found_digit;
@@ -199,7 +199,8 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(SelectParams p
   const int row = blockIdx.x;
   const int b = row / p.R;
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // (uniform: scalar addressing)
   const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
   const int n = min(max(p.seq_lens[b], 0), p.L_max);
   const float* sc = p.scores + (size_t)row * p.L_max;
@@ -354,11 +355,11 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(SelectParams p
     bool fits = true;
 #pragma unroll
     for (int w = 0; w < kSelWaves; ++w) fits = fits && L.wcnt[w] <= kWaveCand;
-    // list slot i is in use when it is below its wave region's count; an
-    // unused slot reads as 0, which matches no prefix (every candidate's top
-    // digit is at least 3)
-    auto in_use = [&](int i) { return (i % kWaveCand) < L.wcnt[i / kWaveCand]; };
-    const int m = kSelCand;
+    // every wave walks the entries of its own list region
+    const int wn = min(L.wcnt[wave], kWaveCand);
+    auto each_key = [&](auto&& f) {
+      for (int i = lane; i < wn; i += 64) f(wkey[i]);
+    };
     if (fits) {
       if (!all) {
         // exact threshold among the list, then the first `take` of the keys
@@ -366,20 +367,21 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(SelectParams p
         int gt, eq;
         const int shk[2] = {10, 0};
         const uint32_t dmk[2] = {0x7FFu, 0x3FFu};
-        const uint32_t thr = list_select<2>([&](int i) { return in_use(i) ? ckey[i] : 0u; }, m,
-                                            remaining, prefix, pmask, shk, dmk, L, gt, eq);
+        const uint32_t thr = list_select<2>(each_key, remaining, prefix, pmask, shk, dmk, L, gt, eq);
         const int take = remaining - gt;
         uint32_t pthr = 0u;
         if (take < eq) {
           int g2, e2;
           const int shp[2] = {9, 0};
           const uint32_t dmp[2] = {0x1FFu, 0x1FFu};
-          pthr = list_select<2>([&](int i) { return in_use(i) && ckey[i] == thr ? ~cpos[i] : 0u; },
-                                m, take, 0xFFFC0000u, 0xFFFC0000u, shp, dmp, L, g2, e2);
+          pthr = list_select<2>(
+              [&](auto&& f) {
+                for (int i = lane; i < wn; i += 64) f(wkey[i] == thr ? ~wpos[i] : 0u);
+              },
+              take, 0xFFFC0000u, 0xFFFC0000u, shp, dmp, L, g2, e2);
         }
-        for (int i = tid; i < m; i += kSelThreads) {
-          if (!in_use(i)) continue;
-          const uint32_t k = ckey[i], t = cpos[i];
+        for (int i = lane; i < wn; i += 64) {
+          const uint32_t k = wkey[i], t = wpos[i];
           if (k > thr || (k == thr && ~t >= pthr)) atomicOr(&sel[t >> 5], 1u << (t & 31));
         }
         __syncthreads();
