@@ -219,17 +219,28 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_kernel(MlaParams p) {
   constexpr int kLpt = 36 / NW;        // 1-KB blocks each wave copies per tile
 
   // Block id -> (sequence b, split, head group).  Consecutive block ids go
-  // to the 8 XCDs in turn; every block of sequence b runs on XCD b % 8, so
-  // the splits of a sequence share one L2 (its query comes from HBM once,
-  // and the merge kernel finds the partials there).
+  // to the 8 XCDs in turn.  When B is a multiple of 8, every block of
+  // sequence b runs on XCD b % 8, so the splits of a sequence share one L2
+  // (its query comes from HBM once, and the merge kernel finds the partials
+  // there); otherwise that would give some XCDs one more sequence than
+  // others (B = 12: twice the work on half of them), so blocks are numbered
+  // plainly and every sequence spreads over the XCDs.
   const int groups = p.n_h / kHpw;
   int id = blockIdx.x;
-  const int xcd = id & 7;
-  id >>= 3;
-  const int hg = id % groups;
-  id /= groups;
-  const int split = id % p.P_max;
-  const int b = (id / p.P_max) * 8 + xcd;
+  int b, split, hg;
+  if ((p.B & 7) == 0) {
+    const int xcd = id & 7;
+    id >>= 3;
+    hg = id % groups;
+    id /= groups;
+    split = id % p.P_max;
+    b = (id / p.P_max) * 8 + xcd;
+  } else {
+    hg = id % groups;
+    id /= groups;
+    split = id % p.P_max;
+    b = id / p.P_max;
+  }
   if (b >= p.B) return;
 
   const int tid = threadIdx.x, lane = tid & 63;
