@@ -178,7 +178,7 @@ class MlaWorkload:
         pre_t = torch.tensor(self.pre, dtype=torch.int32)
         self.sl = [pre_t.clone().cuda() for _ in range(self.layers)]
         self.ws = kvc.workspace(kvc.kvc_decode_attn_mla_workspace_size(
-            B, n_h, self.L_max, cfg.d_c, cfg.d_r, kvc.KVC_BF16))
+            B, n_h, self.L_max, cfg.d_c, cfg.d_r))
 
     def step(self):
         for l in range(self.layers):

@@ -28,8 +28,9 @@
  *
  * Conventions for every call:
  *  - All tensor pointers are DEVICE pointers, row-major and contiguous, owned
- *    by the caller.  The library allocates no memory and keeps no per-call
- *    state.  q/k/v/out pointers must be 16-byte aligned; seq_lens, idx, lse
+ *    by the caller.  The library allocates no memory and keeps no state
+ *    between calls (the one exception is the test hook
+ *    kvc_set_split_override, which stays at 0 unless a test sets it).  q/k/v/out pointers must be 16-byte aligned; seq_lens, idx, lse
  *    and flag 4-byte aligned.
  *  - dtype is KVC_F32 or KVC_BF16 and applies to q, caches, new rows and out.
  *    Arithmetic is float32 (exp, sums, products accumulate in float32); bf16
@@ -60,9 +61,12 @@
 extern "C" {
 #endif
 
-/* element types */
-#define KVC_F32 0
-#define KVC_BF16 1
+/* Element types of q, caches, new rows and out (an int-sized enum). */
+#ifdef __cplusplus
+typedef enum kvc_dtype : int { KVC_F32 = 0, KVC_BF16 = 1 } kvc_dtype;
+#else
+typedef enum kvc_dtype { KVC_F32 = 0, KVC_BF16 = 1 } kvc_dtype;
+#endif
 
 /* status codes */
 #define KVC_OK 0
@@ -98,7 +102,7 @@ extern "C" {
  */
 int kvc_append(void* k_cache, void* v_cache, int32_t* seq_lens,
                const void* k_new, const void* v_new,
-               int B, int n_kv, int L_max, int d, int dtype,
+               int B, int n_kv, int L_max, int d, kvc_dtype dtype,
                int32_t* flag, void* stream);
 
 /*
@@ -117,11 +121,11 @@ int kvc_append(void* k_cache, void* v_cache, int32_t* seq_lens,
  *   d in {64, 128}; n_h / n_kv <= 16; L_max * d * elem_bytes < 2^31.
  */
 size_t kvc_decode_attn_workspace_size(int B, int n_h, int n_kv, int L_max,
-                                      int d, int dtype);
+                                      int d, kvc_dtype dtype);
 int kvc_decode_attn(const void* q, const void* k_cache, const void* v_cache,
                     const int32_t* seq_lens, void* out, float* lse,
                     int B, int n_h, int n_kv, int L_max, int d, float scale,
-                    int dtype, void* workspace, size_t ws_bytes, void* stream);
+                    kvc_dtype dtype, void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * kvc_append_decode_attn - kvc_append followed by kvc_decode_attn, in one
@@ -140,12 +144,12 @@ int kvc_decode_attn(const void* q, const void* k_cache, const void* v_cache,
  * counter per sequence) and follows the same zero-fill rule.
  */
 size_t kvc_append_decode_attn_workspace_size(int B, int n_h, int n_kv,
-                                             int L_max, int d, int dtype);
+                                             int L_max, int d, kvc_dtype dtype);
 int kvc_append_decode_attn(const void* q, void* k_cache, void* v_cache,
                            int32_t* seq_lens, const void* k_new,
                            const void* v_new, void* out, float* lse,
                            int B, int n_h, int n_kv, int L_max, int d,
-                           float scale, int dtype, int32_t* flag,
+                           float scale, kvc_dtype dtype, int32_t* flag,
                            void* workspace, size_t ws_bytes, void* stream);
 
 /*
@@ -173,14 +177,14 @@ int kvc_append_decode_attn(const void* q, void* k_cache, void* v_cache,
 int kvc_append_paged(void* k_pool, void* v_pool, const int32_t* block_table,
                      int max_blocks, int32_t* seq_lens, const void* k_new,
                      const void* v_new, int B, int n_kv, int num_blocks,
-                     int block_size, int d, int dtype, int32_t* flag, void* stream);
+                     int block_size, int d, kvc_dtype dtype, int32_t* flag, void* stream);
 size_t kvc_decode_attn_paged_workspace_size(int B, int n_h, int n_kv, int max_blocks,
-                                            int block_size, int d, int dtype);
+                                            int block_size, int d, kvc_dtype dtype);
 int kvc_decode_attn_paged(const void* q, const void* k_pool, const void* v_pool,
                           const int32_t* block_table, int max_blocks,
                           const int32_t* seq_lens, void* out, float* lse, int B,
                           int n_h, int n_kv, int num_blocks, int block_size, int d,
-                          float scale, int dtype, int32_t* flag, void* workspace,
+                          float scale, kvc_dtype dtype, int32_t* flag, void* workspace,
                           size_t ws_bytes, void* stream);
 
 /*
@@ -201,11 +205,11 @@ int kvc_decode_attn_paged(const void* q, const void* k_pool, const void* v_pool,
  *   less).
  */
 size_t kvc_decode_attn_window_workspace_size(int B, int n_h, int n_kv, int L_max,
-                                             int d, int dtype, int window);
+                                             int d, kvc_dtype dtype, int window);
 int kvc_decode_attn_window(const void* q, const void* k_cache, const void* v_cache,
                            const int32_t* seq_lens, const int32_t* win_start,
                            int window, void* out, float* lse, int B, int n_h,
-                           int n_kv, int L_max, int d, float scale, int dtype,
+                           int n_kv, int L_max, int d, float scale, kvc_dtype dtype,
                            void* workspace, size_t ws_bytes, void* stream);
 
 /*
@@ -298,11 +302,11 @@ int kvc_decode_attn_fp4(const void* q, const void* k_codes, const void* k_scales
  *   This build supports dtype KVC_BF16, d_c = 512, d_r = 64, n_h % 64 == 0.
  */
 size_t kvc_decode_attn_mla_workspace_size(int B, int n_h, int L_max, int d_c,
-                                          int d_r, int dtype);
+                                          int d_r);
 int kvc_decode_attn_mla(const void* q, const void* ckv,
                         const int32_t* seq_lens, void* out, float* lse,
                         int B, int n_h, int L_max, int d_c, int d_r,
-                        float scale, int dtype, void* workspace,
+                        float scale, kvc_dtype dtype, void* workspace,
                         size_t ws_bytes, void* stream);
 
 /*
@@ -317,12 +321,12 @@ int kvc_decode_attn_mla(const void* q, const void* ckv,
  *   idx [B, n_kv, K] int32 device.   1 <= K <= L_max.
  */
 size_t kvc_decode_attn_topk_workspace_size(int B, int n_h, int n_kv, int K,
-                                           int d, int dtype);
+                                           int d, kvc_dtype dtype);
 int kvc_decode_attn_topk(const void* q, const void* k_cache,
                          const void* v_cache, const int32_t* seq_lens,
                          const int32_t* idx, int K, void* out, float* lse,
                          int B, int n_h, int n_kv, int L_max, int d,
-                         float scale, int dtype, int32_t* flag,
+                         float scale, kvc_dtype dtype, int32_t* flag,
                          void* workspace, size_t ws_bytes, void* stream);
 
 /*
@@ -353,10 +357,14 @@ int kvc_topk_select(const float* scores, const int32_t* seq_lens, const int32_t*
 const char* kvc_status_string(int status);
 
 /*
- * Positions handled by one workgroup before results are merged across
- * workgroups.  0 restores the built-in policy; other values are rounded up
- * to the kernel granularity.  Process-wide; meant for tests and tuning, not
- * for concurrent use with decode calls.  Returns KVC_ERR_BAD_ARG if negative.
+ * Test and tuning hook, not part of the attention interface: the positions
+ * one workgroup handles before results are merged across workgroups.  0 (the
+ * initial value) restores the built-in policy; other values are rounded up
+ * to the kernel granularity.  This is the library's only state: it is
+ * process-wide and applies to every later workspace query and decode call,
+ * so a query and the call that uses its workspace must see the same
+ * setting.  Do not change it while decode calls may be enqueued from other
+ * threads.  Returns KVC_ERR_BAD_ARG if negative.
  */
 int kvc_set_split_override(int positions);
 

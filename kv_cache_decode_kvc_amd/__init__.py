@@ -11,7 +11,6 @@ Build the library with ``python -m kv_cache_decode_kvc_amd.build``.
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -62,7 +61,7 @@ def lib() -> ctypes.CDLL:
         "kvc_append_decode_attn_workspace_size": (_Z, [_I, _I, _I, _I, _I, _I]),
         "kvc_append_decode_attn": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I,
                                         _I, _F, _I, _P, _P, _Z, _P]),
-        "kvc_decode_attn_mla_workspace_size": (_Z, [_I, _I, _I, _I, _I, _I]),
+        "kvc_decode_attn_mla_workspace_size": (_Z, [_I, _I, _I, _I, _I]),
         "kvc_decode_attn_mla": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
                                      _F, _I, _P, _Z, _P]),
         "kvc_decode_attn_topk_workspace_size": (_Z, [_I, _I, _I, _I, _I, _I]),
@@ -143,6 +142,14 @@ def _ws(ws):
     return (None, 0) if ws is None else (_ptr(ws), ws.numel() * ws.element_size())
 
 
+def _scale(scale, where):
+    """The score scale is the caller's (no default: the library applies
+    exactly the factor it is given)."""
+    if scale is None:
+        raise TypeError(f"{where}: scale is required (e.g. 1/sqrt(d) for plain attention)")
+    return float(scale)
+
+
 # ---------------------------------------------------------------- calls
 def kvc_status_string(status: int) -> str:
     return lib().kvc_status_string(status).decode()
@@ -185,7 +192,7 @@ def kvc_decode_attn(q, k_cache, v_cache, seq_lens, out, lse=None, scale=None,
     """Dense decode attention; q/out [B, n_h, d], caches [B, n_kv, L_max, d]."""
     B, n_h, d = q.shape
     _, n_kv, L_max, _ = k_cache.shape
-    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    scale = _scale(scale, "kvc_decode_attn")
     wp, wn = _ws(workspace)
     st = lib().kvc_decode_attn(_ptr(q), _ptr(k_cache), _ptr(v_cache),
                                _ptr(seq_lens), _ptr(out), _ptr(lse), B, n_h,
@@ -205,7 +212,7 @@ def kvc_append_decode_attn(q, k_cache, v_cache, seq_lens, k_new, v_new, out,
     including it, bump seq_lens -- one kernel launch."""
     B, n_h, d = q.shape
     _, n_kv, L_max, _ = k_cache.shape
-    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    scale = _scale(scale, "kvc_append_decode_attn")
     wp, wn = _ws(workspace)
     st = lib().kvc_append_decode_attn(_ptr(q), _ptr(k_cache), _ptr(v_cache),
                                       _ptr(seq_lens), _ptr(k_new), _ptr(v_new),
@@ -215,8 +222,8 @@ def kvc_append_decode_attn(q, k_cache, v_cache, seq_lens, k_new, v_new, out,
     _check(st, "kvc_append_decode_attn")
 
 
-def kvc_decode_attn_mla_workspace_size(B, n_h, L_max, d_c, d_r, dtype) -> int:
-    return lib().kvc_decode_attn_mla_workspace_size(B, n_h, L_max, d_c, d_r, dtype)
+def kvc_decode_attn_mla_workspace_size(B, n_h, L_max, d_c, d_r) -> int:
+    return lib().kvc_decode_attn_mla_workspace_size(B, n_h, L_max, d_c, d_r)
 
 
 def kvc_decode_attn_mla(q, ckv, seq_lens, out, lse=None, scale=None,
@@ -227,7 +234,7 @@ def kvc_decode_attn_mla(q, ckv, seq_lens, out, lse=None, scale=None,
     L_max = ckv.shape[-2]
     d_c = out.shape[-1]
     d_r = D - d_c
-    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    scale = _scale(scale, "kvc_decode_attn_mla")
     wp, wn = _ws(workspace)
     st = lib().kvc_decode_attn_mla(_ptr(q), _ptr(ckv), _ptr(seq_lens), _ptr(out),
                                    _ptr(lse), B, n_h, L_max, d_c, d_r, scale,
@@ -245,7 +252,7 @@ def kvc_decode_attn_topk(q, k_cache, v_cache, seq_lens, idx, out, lse=None,
     B, n_h, d = q.shape
     _, n_kv, L_max, _ = k_cache.shape
     K = idx.shape[-1]
-    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    scale = _scale(scale, "kvc_decode_attn_topk")
     wp, wn = _ws(workspace)
     st = lib().kvc_decode_attn_topk(_ptr(q), _ptr(k_cache), _ptr(v_cache),
                                     _ptr(seq_lens), _ptr(idx), K, _ptr(out),
@@ -265,7 +272,7 @@ def kvc_decode_attn_window(q, k_cache, v_cache, seq_lens, out, window, win_start
     the earliest); shapes as kvc_decode_attn."""
     B, n_h, d = q.shape
     _, n_kv, L_max, _ = k_cache.shape
-    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    scale = _scale(scale, "kvc_decode_attn_window")
     wp, wn = _ws(workspace)
     st = lib().kvc_decode_attn_window(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens),
                                       _ptr(win_start), window, _ptr(out), _ptr(lse), B, n_h,
@@ -297,7 +304,7 @@ def kvc_decode_attn_paged(q, k_pool, v_pool, block_table, seq_lens, out, lse=Non
     B, n_h, d = q.shape
     num_blocks, n_kv, beta, _ = k_pool.shape
     max_blocks = block_table.shape[1]
-    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    scale = _scale(scale, "kvc_decode_attn_paged")
     wp, wn = _ws(workspace)
     st = lib().kvc_decode_attn_paged(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table),
                                      max_blocks, _ptr(seq_lens), _ptr(out), _ptr(lse), B, n_h,
@@ -357,7 +364,7 @@ def kvc_decode_attn_fp8(q, k_cache, v_cache, seq_lens, out, k_scale, v_scale,
         raise TypeError("q/out must be bfloat16")
     B, n_h, d = q.shape
     _, n_kv, L_max, _ = k_cache.shape
-    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    scale = _scale(scale, "kvc_decode_attn_fp8")
     wp, wn = _ws(workspace)
     st = lib().kvc_decode_attn_fp8(_ptr(q), _ptr(k_cache), _ptr(v_cache),
                                    _ptr(seq_lens), _ptr(out), _ptr(lse), B, n_h,
@@ -400,7 +407,7 @@ def kvc_decode_attn_fp4(q, k_codes, k_scales, v_codes, v_scales, seq_lens, out, 
         raise TypeError("q/out must be bfloat16")
     B, n_h, d = q.shape
     _, n_kv, L_max, _ = k_codes.shape
-    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    scale = _scale(scale, "kvc_decode_attn_fp4")
     wp, wn = _ws(workspace)
     st = lib().kvc_decode_attn_fp4(_ptr(q), _ptr(k_codes), _ptr(k_scales), _ptr(v_codes),
                                    _ptr(v_scales), _ptr(seq_lens), _ptr(out), _ptr(lse), B,

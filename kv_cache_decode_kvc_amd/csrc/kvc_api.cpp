@@ -221,7 +221,7 @@ int kvc_split_positions(int kind, int B, int units, int n_max) {
 
 int kvc_append(void* k_cache, void* v_cache, int32_t* seq_lens,
                const void* k_new, const void* v_new, int B, int n_kv,
-               int L_max, int d, int dtype, int32_t* flag, void* stream) {
+               int L_max, int d, kvc_dtype dtype, int32_t* flag, void* stream) {
   if (!good_dtype(dtype)) return KVC_ERR_BAD_DTYPE;
   if (B < 0 || n_kv < 1 || L_max < 1 || d < 1) return KVC_ERR_BAD_SHAPE;
   if ((int64_t)n_kv * d >= kMaxOffset) return KVC_ERR_BAD_SHAPE;
@@ -274,13 +274,13 @@ int kvc_append_fp4(void* k_codes, void* k_scales, void* v_codes, void* v_scales,
 }
 
 size_t kvc_decode_attn_workspace_size(int B, int n_h, int n_kv, int L_max,
-                                      int d, int dtype) {
+                                      int d, kvc_dtype dtype) {
   const DenseCheck c = check_dense_shape(B, n_h, n_kv, L_max, d, dtype, 0, false);
   return c.status == KVC_OK ? c.ws.total : 0;
 }
 
 size_t kvc_decode_attn_topk_workspace_size(int B, int n_h, int n_kv, int K,
-                                           int d, int dtype) {
+                                           int d, kvc_dtype dtype) {
   // The workspace depends on K, not on L_max; any L_max >= K gives the same.
   const DenseCheck c = check_dense_shape(B, n_h, n_kv, K < 1 ? 1 : K, d, dtype, K, true);
   return c.status == KVC_OK ? c.ws.total : 0;
@@ -289,7 +289,7 @@ size_t kvc_decode_attn_topk_workspace_size(int B, int n_h, int n_kv, int K,
 static int dense_common(const void* q, const void* k_cache, const void* v_cache,
                         const int32_t* seq_lens, const int32_t* idx, int K,
                         void* out, float* lse, int B, int n_h, int n_kv,
-                        int L_max, int d, float scale, int dtype, int32_t* flag,
+                        int L_max, int d, float scale, kvc_dtype dtype, int32_t* flag,
                         void* workspace, size_t ws_bytes, void* stream,
                         bool topk, const void* k_new = nullptr,
                         const void* v_new = nullptr, bool fused = false,
@@ -360,7 +360,7 @@ static int dense_common(const void* q, const void* k_cache, const void* v_cache,
 }
 
 size_t kvc_append_decode_attn_workspace_size(int B, int n_h, int n_kv, int L_max,
-                                             int d, int dtype) {
+                                             int d, kvc_dtype dtype) {
   const DenseCheck c = check_dense_shape(B, n_h, n_kv, L_max, d, dtype, 0, false, true);
   return c.status == KVC_OK ? c.ws.total : 0;
 }
@@ -369,7 +369,7 @@ int kvc_append_decode_attn(const void* q, void* k_cache, void* v_cache,
                            int32_t* seq_lens, const void* k_new,
                            const void* v_new, void* out, float* lse, int B,
                            int n_h, int n_kv, int L_max, int d, float scale,
-                           int dtype, int32_t* flag, void* workspace,
+                           kvc_dtype dtype, int32_t* flag, void* workspace,
                            size_t ws_bytes, void* stream) {
   return dense_common(q, k_cache, v_cache, seq_lens, nullptr, 0, out, lse, B,
                       n_h, n_kv, L_max, d, scale, dtype, flag, workspace,
@@ -378,7 +378,7 @@ int kvc_append_decode_attn(const void* q, void* k_cache, void* v_cache,
 
 int kvc_decode_attn(const void* q, const void* k_cache, const void* v_cache,
                     const int32_t* seq_lens, void* out, float* lse, int B,
-                    int n_h, int n_kv, int L_max, int d, float scale, int dtype,
+                    int n_h, int n_kv, int L_max, int d, float scale, kvc_dtype dtype,
                     void* workspace, size_t ws_bytes, void* stream) {
   return dense_common(q, k_cache, v_cache, seq_lens, nullptr, 0, out, lse, B,
                       n_h, n_kv, L_max, d, scale, dtype, nullptr, workspace,
@@ -389,7 +389,7 @@ int kvc_decode_attn_topk(const void* q, const void* k_cache,
                          const void* v_cache, const int32_t* seq_lens,
                          const int32_t* idx, int K, void* out, float* lse,
                          int B, int n_h, int n_kv, int L_max, int d,
-                         float scale, int dtype, int32_t* flag,
+                         float scale, kvc_dtype dtype, int32_t* flag,
                          void* workspace, size_t ws_bytes, void* stream) {
   return dense_common(q, k_cache, v_cache, seq_lens, idx, K, out, lse, B, n_h,
                       n_kv, L_max, d, scale, dtype, flag, workspace, ws_bytes,
@@ -397,7 +397,7 @@ int kvc_decode_attn_topk(const void* q, const void* k_cache,
 }
 
 size_t kvc_decode_attn_window_workspace_size(int B, int n_h, int n_kv, int L_max,
-                                             int d, int dtype, int window) {
+                                             int d, kvc_dtype dtype, int window) {
   if (window < 1) return 0;
   const DenseCheck c = check_dense_shape(B, n_h, n_kv, L_max, d, dtype, 0, false, false, window);
   return c.status == KVC_OK ? c.ws.total : 0;
@@ -406,7 +406,7 @@ size_t kvc_decode_attn_window_workspace_size(int B, int n_h, int n_kv, int L_max
 int kvc_decode_attn_window(const void* q, const void* k_cache, const void* v_cache,
                            const int32_t* seq_lens, const int32_t* win_start,
                            int window, void* out, float* lse, int B, int n_h,
-                           int n_kv, int L_max, int d, float scale, int dtype,
+                           int n_kv, int L_max, int d, float scale, kvc_dtype dtype,
                            void* workspace, size_t ws_bytes, void* stream) {
   if (window < 1) return KVC_ERR_BAD_ARG;
   return dense_common(q, k_cache, v_cache, seq_lens, nullptr, 0, out, lse, B,
@@ -435,7 +435,7 @@ static int check_paged(int B, int n_kv, int max_blocks, int num_blocks, int bloc
 }
 
 size_t kvc_decode_attn_paged_workspace_size(int B, int n_h, int n_kv, int max_blocks,
-                                            int block_size, int d, int dtype) {
+                                            int block_size, int d, kvc_dtype dtype) {
   if (page_shift_of(block_size) < 0 || max_blocks < 1 ||
       (int64_t)max_blocks * block_size >= kMaxOffset)
     return 0;
@@ -447,7 +447,7 @@ int kvc_decode_attn_paged(const void* q, const void* k_pool, const void* v_pool,
                           const int32_t* block_table, int max_blocks,
                           const int32_t* seq_lens, void* out, float* lse, int B,
                           int n_h, int n_kv, int num_blocks, int block_size, int d,
-                          float scale, int dtype, int32_t* flag, void* workspace,
+                          float scale, kvc_dtype dtype, int32_t* flag, void* workspace,
                           size_t ws_bytes, void* stream) {
   if (!good_dtype(dtype)) return KVC_ERR_BAD_DTYPE;
   int shift = 0;
@@ -465,7 +465,7 @@ int kvc_decode_attn_paged(const void* q, const void* k_pool, const void* v_pool,
 int kvc_append_paged(void* k_pool, void* v_pool, const int32_t* block_table,
                      int max_blocks, int32_t* seq_lens, const void* k_new,
                      const void* v_new, int B, int n_kv, int num_blocks,
-                     int block_size, int d, int dtype, int32_t* flag, void* stream) {
+                     int block_size, int d, kvc_dtype dtype, int32_t* flag, void* stream) {
   if (!good_dtype(dtype)) return KVC_ERR_BAD_DTYPE;
   int shift = 0;
   const int st = check_paged(B, n_kv, max_blocks, num_blocks, block_size, d, elem_bytes(dtype), shift);
@@ -523,15 +523,17 @@ int kvc_decode_attn_fp4(const void* q, const void* k_codes, const void* k_scales
 }
 
 size_t kvc_decode_attn_mla_workspace_size(int B, int n_h, int L_max, int d_c,
-                                          int d_r, int dtype) {
-  const MlaCheck c = check_mla_shape(B, n_h, L_max, d_c, d_r, dtype);
+                                          int d_r) {
+  // (the latent kernel exists for bf16 only; its workspace does not depend
+  // on the element type)
+  const MlaCheck c = check_mla_shape(B, n_h, L_max, d_c, d_r, KVC_BF16);
   return c.status == KVC_OK ? c.ws.total : 0;
 }
 
 int kvc_decode_attn_mla(const void* q, const void* ckv,
                         const int32_t* seq_lens, void* out, float* lse, int B,
                         int n_h, int L_max, int d_c, int d_r, float scale,
-                        int dtype, void* workspace, size_t ws_bytes,
+                        kvc_dtype dtype, void* workspace, size_t ws_bytes,
                         void* stream) {
   const MlaCheck c = check_mla_shape(B, n_h, L_max, d_c, d_r, dtype);
   if (c.status != KVC_OK) return c.status;

@@ -139,7 +139,7 @@ def test_mla_validation(L):
     assert ml(out=A8) == -6
     assert ml(scale=float("nan")) == -8
     assert ml(B=0) == 0
-    assert L.kvc_decode_attn_mla_workspace_size(64, 128, 8193, 512, 64, kvc.KVC_BF16) > 0
+    assert L.kvc_decode_attn_mla_workspace_size(64, 128, 8193, 512, 64) > 0
 
 
 def test_topk_validation(L):
@@ -341,3 +341,31 @@ def test_select_validation(L):
     assert sel(L=(1 << 29) - 1, B=0) == 0
     assert sel(s=ctypes.c_void_p(0x10002)) == -6
     assert sel(B=0) == 0
+
+
+def test_header_enum_and_signatures():
+    """The element-type enum's values are the binding's codes, and the
+    latent workspace query takes the five shape arguments only."""
+    text = open(HEADER).read()
+    assert re.search(r"typedef enum kvc_dtype\s*(:\s*int\s*)?\{\s*KVC_F32 = 0, KVC_BF16 = 1\s*\}", text)
+    assert (kvc.KVC_F32, kvc.KVC_BF16) == (0, 1)
+    decl = re.search(r"size_t kvc_decode_attn_mla_workspace_size\(([^)]*)\)", text).group(1)
+    assert [a.split()[-1] for a in decl.split(",")] == ["B", "n_h", "L_max", "d_c", "d_r"]
+    # every call that takes an element type declares it as kvc_dtype
+    flat = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    assert "int dtype" not in flat
+
+
+def test_binding_requires_scale():
+    """The score scale is always the caller's: the binding computes no
+    default (it fails before touching any device pointer)."""
+    import torch
+    q = torch.zeros(1, 8, 128)
+    kc = torch.zeros(1, 2, 16, 128)
+    sl = torch.zeros(1, dtype=torch.int32)
+    for call in (lambda: kvc.kvc_decode_attn(q, kc, kc, sl, q),
+                 lambda: kvc.kvc_append_decode_attn(q, kc, kc, sl, q, q, q),
+                 lambda: kvc.kvc_decode_attn_window(q, kc, kc, sl, q, 4),
+                 lambda: kvc.kvc_decode_attn_topk(q, kc, kc, sl, sl.view(1, 1, 1), q)):
+        with pytest.raises(TypeError, match="scale is required"):
+            call()

@@ -199,7 +199,8 @@ def test_fp8_graph_replay_matches_oracle_loop():
     torch.cuda.synchronize()
     with torch.cuda.graph(g, stream=s):
         kvc.kvc_append_fp8(k8, v8, sl, kn, vn, k_scale, v_scale)
-        kvc.kvc_decode_attn_fp8(q, k8, v8, sl, out, k_scale, v_scale, workspace=ws)
+        kvc.kvc_decode_attn_fp8(q, k8, v8, sl, out, k_scale, v_scale,
+                                    scale=1 / math.sqrt(d), workspace=ws)
     k_o, v_o, sl_o = case["k8"].copy(), case["v8"].copy(), case["seq_lens"].copy()
     for step in range(3):
         g.replay()

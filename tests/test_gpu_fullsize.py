@@ -233,8 +233,7 @@ def test_fullsize_mla_layer():
     sl = torch.tensor(pre, dtype=torch.int32, device="cuda")
     out = torch.empty(c.B, c.n_h, c.d_c, dtype=torch.bfloat16, device="cuda")
     lse = torch.empty(c.B, c.n_h, dtype=torch.float32, device="cuda")
-    ws = kvc.workspace(kvc.kvc_decode_attn_mla_workspace_size(c.B, c.n_h, L_max, c.d_c, c.d_r,
-                                                              kvc.KVC_BF16))
+    ws = kvc.workspace(kvc.kvc_decode_attn_mla_workspace_size(c.B, c.n_h, L_max, c.d_c, c.d_r))
     kvc.kvc_append(C, None, sl, cn, None)
     kvc.kvc_decode_attn_mla(q, C, sl, out, lse, scale=c.scale, workspace=ws)
     torch.cuda.synchronize()

@@ -80,7 +80,8 @@ def test_paged_append_then_decode(n_h, n_kv, lens, beta, max_blocks, split):
     lse = torch.empty(B, n_h, dtype=torch.float32, device="cuda")
     kvc.kvc_set_split_override(split)
     ws = kvc.workspace(kvc.kvc_decode_attn_paged_workspace_size(B, n_h, n_kv, max_blocks, beta, d, 1))
-    kvc.kvc_decode_attn_paged(q, kp, vp, tab, sl, out, lse, flag=flag, workspace=ws)
+    kvc.kvc_decode_attn_paged(q, kp, vp, tab, sl, out, lse, scale=1 / math.sqrt(d), flag=flag,
+                              workspace=ws)
     torch.cuda.synchronize()
     if ws is not None:
         assert int(ws[:4 * B * n_kv].view(torch.int32).abs().sum()) == 0, "tickets not reset"
@@ -113,7 +114,7 @@ def test_paged_shared_prefix_and_bad_blocks():
     flag = torch.zeros(1, dtype=torch.int32, device="cuda")
     ws = kvc.workspace(kvc.kvc_decode_attn_paged_workspace_size(B, n_h, n_kv, mb, beta, d, 1))
     kvc.kvc_decode_attn_paged(q, dev(case["k_pool"]), dev(case["v_pool"]), dev(tab), dev(sl), out,
-                              lse, flag=flag, workspace=ws)
+                              lse, scale=1 / math.sqrt(d), flag=flag, workspace=ws)
     torch.cuda.synchronize()
     o_ref, l_ref, f_ref = oracle.decode_paged(case["q"], case["k_pool"], case["v_pool"], tab, sl,
                                               1 / math.sqrt(d))

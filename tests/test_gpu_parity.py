@@ -251,7 +251,8 @@ def test_topk_bad_indices_and_exact_selection():
     out = torch.empty_like(q)
     flag = torch.zeros(1, dtype=torch.int32, device="cuda")
     ws = kvc.workspace(kvc.kvc_decode_attn_topk_workspace_size(B, n_h, n_kv, K, d, 1))
-    kvc.kvc_decode_attn_topk(q, kc, vc, sl, dev(idx), out, None, flag=flag, workspace=ws)
+    kvc.kvc_decode_attn_topk(q, kc, vc, sl, dev(idx), out, None, scale=0.1, flag=flag,
+                             workspace=ws)
     torch.cuda.synchronize()
     o_ref, _, f_ref = oracle.decode_topk(case["q"], case["k_cache"], case["v_cache"], case["seq_lens"], idx, 0.1)
     assert f_ref == oracle.FLAG_BAD_INDEX and int(host(flag)[0]) == f_ref
@@ -287,7 +288,7 @@ def test_mla_parity(B, n_h, pre, L_max, split):
     out = torch.empty(B, n_h, 512, dtype=torch.bfloat16, device="cuda")
     lse = torch.empty(B, n_h, dtype=torch.float32, device="cuda")
     kvc.kvc_set_split_override(split)
-    ws = kvc.workspace(kvc.kvc_decode_attn_mla_workspace_size(B, n_h, L_max, 512, 64, 1))
+    ws = kvc.workspace(kvc.kvc_decode_attn_mla_workspace_size(B, n_h, L_max, 512, 64))
     kvc.kvc_decode_attn_mla(q, ckv, sl, out, lse, scale=1 / 24, workspace=ws)
     torch.cuda.synchronize()
     c4 = case["ckv"][:, None].copy()
@@ -321,7 +322,7 @@ def test_mla_score_jump(n_h, split):
     out = torch.empty(B, n_h, 512, dtype=torch.bfloat16, device="cuda")
     lse = torch.empty(B, n_h, dtype=torch.float32, device="cuda")
     kvc.kvc_set_split_override(split)
-    ws = kvc.workspace(kvc.kvc_decode_attn_mla_workspace_size(B, n_h, L_max, 512, 64, 1))
+    ws = kvc.workspace(kvc.kvc_decode_attn_mla_workspace_size(B, n_h, L_max, 512, 64))
     kvc.kvc_decode_attn_mla(q, ckv_d, sl, out, lse, scale=1 / 24, workspace=ws)
     torch.cuda.synchronize()
     o_ref, l_ref = oracle.decode_mla(qb, ckv, case["seq_lens"], 512, 64, 1 / 24)
@@ -354,7 +355,7 @@ def test_causal_loop_on_gpu():
         kvc.kvc_append(kc, vc, sl, dev(K[t][None]), dev(V[t][None]))
         q = dev(Q[t][None])
         out = torch.empty_like(q)
-        kvc.kvc_decode_attn(q, kc, vc, sl, out, None, workspace=ws)
+        kvc.kvc_decode_attn(q, kc, vc, sl, out, None, scale=1 / math.sqrt(d), workspace=ws)
         outs.append(out)
     torch.cuda.synchronize()
     got = np.stack([host_f64(o)[0] for o in outs])
@@ -372,7 +373,7 @@ def test_graph_replay_matches_eager():
     out = torch.empty_like(q)
     ws = kvc.workspace(kvc.kvc_decode_attn_workspace_size(4, 64, 8, 1024, 128, 1))
     kvc.kvc_append(kc, vc, sl, kn, vn)
-    kvc.kvc_decode_attn(q, kc, vc, sl, out, None, workspace=ws)
+    kvc.kvc_decode_attn(q, kc, vc, sl, out, None, scale=1 / math.sqrt(128), workspace=ws)
     torch.cuda.synchronize()
     eager = out.clone()
     s = torch.cuda.Stream()
@@ -381,7 +382,7 @@ def test_graph_replay_matches_eager():
     torch.cuda.synchronize()
     with torch.cuda.graph(g, stream=s):
         kvc.kvc_append(kc, vc, sl, kn, vn)
-        kvc.kvc_decode_attn(q, kc, vc, sl, out, None, workspace=ws)
+        kvc.kvc_decode_attn(q, kc, vc, sl, out, None, scale=1 / math.sqrt(128), workspace=ws)
     for rep in range(4):
         kc.copy_(kc0); vc.copy_(vc0); sl.copy_(sl0); out.zero_()
         torch.cuda.synchronize()
@@ -466,7 +467,8 @@ def test_fused_graph_replay_and_repeat():
     g = torch.cuda.CUDAGraph()
     torch.cuda.synchronize()
     with torch.cuda.graph(g, stream=s):
-        kvc.kvc_append_decode_attn(q, kc, vc, sl, kn, vn, out, workspace=ws)
+        kvc.kvc_append_decode_attn(q, kc, vc, sl, kn, vn, out, scale=1 / math.sqrt(d),
+                                   workspace=ws)
     kc_o, vc_o, sl_o = case["k_cache"].copy(), case["v_cache"].copy(), case["seq_lens"].copy()
     for step in range(3):
         g.replay()

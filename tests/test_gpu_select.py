@@ -185,7 +185,7 @@ def test_select_then_sparse_decode():
     flag = torch.zeros(1, dtype=torch.int32, device="cuda")
     ws = kvc.workspace(kvc.kvc_decode_attn_topk_workspace_size(B, n_h, n_kv, K, d, 1))
     kvc.kvc_decode_attn_topk(q, dev(case["k_cache"]), dev(case["v_cache"]), sl, idx, out,
-                             flag=flag, workspace=ws)
+                             scale=1 / math.sqrt(d), flag=flag, workspace=ws)
     torch.cuda.synchronize()
     sel = oracle.topk_select(sc, np.asarray(lens), K)
     assert np.array_equal(host(idx), sel)

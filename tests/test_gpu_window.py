@@ -87,7 +87,8 @@ def test_window_one_is_newest_value_row():
     out = torch.empty_like(q)
     ws = kvc.workspace(kvc.kvc_decode_attn_window_workspace_size(B, n_h, n_kv, L_max, d, 1, 1))
     kvc.kvc_decode_attn_window(q, dev(case["k_cache"]), dev(case["v_cache"]),
-                               dev(np.asarray(lens, np.int32)), out, 1, workspace=ws)
+                               dev(np.asarray(lens, np.int32)), out, 1,
+                               scale=1 / math.sqrt(d), workspace=ws)
     torch.cuda.synchronize()
     got = host(out)
     G = n_h // n_kv
