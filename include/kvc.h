@@ -48,8 +48,10 @@
  *  - Workspace: decode calls that split the positions of a sequence across
  *    workgroups need a device workspace of the size the matching *_workspace
  *    _size call returns (0 means none).  It must be zero-filled before its
- *    first use; every call leaves it zero-filled again.  Calls that may run
- *    at the same time need separate workspaces.
+ *    first use; every call returns the counters it holds to zero (the rest is
+ *    scratch that each call writes before reading), so a workspace is reused
+ *    without clearing.  Calls that may run at the same time need separate
+ *    workspaces.
  */
 #ifndef KVC_H
 #define KVC_H
@@ -376,9 +378,11 @@ int kvc_split_positions(int kind, int B, int units, int n_max);
 
 /*
  * Diagnostics for bandwidth measurement (not part of the attention path).
- * kvc_stream_read reads `bytes` (multiple of 16) from src with 16-byte loads
- * and writes one float per workgroup to sink (so the loads are kept);
- * sink needs kvc_stream_read_sink_floats(bytes) floats.
+ * kvc_stream_read reads `bytes` (multiple of 16) from src the way the decode
+ * kernels read cache rows (each workgroup one contiguous slab, 16-byte
+ * buffer loads with the non-temporal policy) and writes one float per
+ * workgroup to sink (so the loads are kept); sink needs
+ * kvc_stream_read_sink_floats(bytes) floats.
  * kvc_copy copies `bytes` (multiple of 16) from src to dst.
  */
 size_t kvc_stream_read_sink_floats(size_t bytes);

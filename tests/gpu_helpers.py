@@ -55,3 +55,51 @@ def compare_lse(got, want, tol=1e-3, what="lse"):
     if (~ninf).any():
         d = np.abs(got[~ninf] - want[~ninf]).max()
         assert d <= tol, f"{what}: {d}"
+
+
+GUARD_BYTE = 0xA5
+
+
+class Guarded:
+    """A device buffer between two guard bands (a 256-byte band before it,
+    4 KiB after), filled with GUARD_BYTE, to catch writes outside the
+    buffer.  The buffer itself starts as NaN (float types; caught by the
+    finite check of any row left unwritten), as zeros (`zero=True`, the
+    workspace rule) or as GUARD_BYTE (integer types).  The lead band keeps
+    the buffer 256-byte aligned (torch allocations are)."""
+
+    LEAD = 256
+    TRAIL = 4096
+
+    def __init__(self, shape, dtype, zero=False):
+        import torch
+        self.shape = tuple(shape)
+        n = 1
+        for s in self.shape:
+            n *= s
+        esz = torch.empty(0, dtype=dtype).element_size()
+        self.nbytes = n * esz
+        self.raw = torch.full((self.LEAD + self.nbytes + self.TRAIL,), GUARD_BYTE,
+                              dtype=torch.uint8, device="cuda")
+        body = self.raw[self.LEAD:self.LEAD + self.nbytes]
+        self.t = body.view(dtype).view(self.shape)
+        if zero:
+            self.t.zero_()
+        elif dtype.is_floating_point:
+            self.t.fill_(float("nan"))
+
+    def check(self, what=""):
+        import torch
+        torch.cuda.synchronize()
+        lead = self.raw[:self.LEAD]
+        trail = self.raw[self.LEAD + self.nbytes:]
+        assert bool((lead == GUARD_BYTE).all()), f"{what}: write before the buffer"
+        assert bool((trail == GUARD_BYTE).all()), f"{what}: write after the buffer"
+
+
+def guarded_workspace(nbytes):
+    """A zero-filled workspace inside guard bands (None if nbytes is 0)."""
+    import torch
+    if nbytes == 0:
+        return None
+    return Guarded((nbytes,), torch.uint8, zero=True)
