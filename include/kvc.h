@@ -80,6 +80,7 @@ typedef enum kvc_dtype { KVC_F32 = 0, KVC_BF16 = 1 } kvc_dtype;
 #define KVC_ERR_MISALIGNED (-6)  /* pointer alignment rule broken */
 #define KVC_ERR_HIP (-7)         /* HIP launch error */
 #define KVC_ERR_BAD_ARG (-8)     /* non-finite scale, negative split override, ... */
+#define KVC_ERR_SCRATCH (-9)     /* the call does not fit the library's static scratch */
 
 /* device-side condition bits */
 #define KVC_FLAG_CACHE_FULL 1 /* append found seq_lens[b] outside [0, L_max) */
@@ -153,6 +154,33 @@ int kvc_append_decode_attn(const void* q, void* k_cache, void* v_cache,
                            int B, int n_h, int n_kv, int L_max, int d,
                            float scale, kvc_dtype dtype, int32_t* flag,
                            void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * kvc_append_decode_attn_noalloc - kvc_append_decode_attn without a
+ * workspace argument and without any allocation, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  The split counters and partials live in a
+ * scratch array the library holds in device memory, one copy per GPU (32 MiB,
+ * kept until the process ends).  Each call clears the counters it uses on
+ * `stream` (a small kernel launch before the attention kernel; no memset, so
+ * the call can be captured in a graph) and then runs exactly the kernels of
+ * kvc_append_decode_attn, with the same results.
+ *
+ * Limits: B * n_kv <= 16384, and the split partials (B * n_h * splits
+ * values of lse and of d floats of output, splits as the workspace query
+ * of kvc_append_decode_attn would plan them) within 32 MiB less 192 KiB:
+ * e.g. 32 sequences of 64 query heads, d = 128, up to 32768 positions.
+ * A call beyond them returns KVC_ERR_SCRATCH before anything is enqueued.
+ * Every call on one GPU shares that GPU's scratch: calls that may overlap
+ * on one GPU (on different streams, or from different threads) race and
+ * must be serialised by the caller.  Arguments otherwise as for
+ * kvc_append_decode_attn.
+ */
+int kvc_append_decode_attn_noalloc(const void* q, void* k_cache, void* v_cache,
+                                   int32_t* seq_lens, const void* k_new, const void* v_new,
+                                   void* out, float* lse, int B, int n_h, int n_kv, int L_max,
+                                   int d, float scale, kvc_dtype dtype, int32_t* flag,
+                                   void* stream);
 
 /*
  * Paged cache (guide, "The allocator, not the algorithm": fixed-size blocks

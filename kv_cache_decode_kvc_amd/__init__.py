@@ -27,7 +27,7 @@ KVC_KIND_MLA = 2
 STATUS = {0: "KVC_OK", -1: "KVC_ERR_NULL_PTR", -2: "KVC_ERR_BAD_SHAPE",
           -3: "KVC_ERR_BAD_DTYPE", -4: "KVC_ERR_UNSUPPORTED",
           -5: "KVC_ERR_WORKSPACE", -6: "KVC_ERR_MISALIGNED", -7: "KVC_ERR_HIP",
-          -8: "KVC_ERR_BAD_ARG"}
+          -8: "KVC_ERR_BAD_ARG", -9: "KVC_ERR_SCRATCH"}
 
 
 class KvcError(RuntimeError):
@@ -61,6 +61,8 @@ def lib() -> ctypes.CDLL:
         "kvc_append_decode_attn_workspace_size": (_Z, [_I, _I, _I, _I, _I, _I]),
         "kvc_append_decode_attn": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I,
                                         _I, _F, _I, _P, _P, _Z, _P]),
+        "kvc_append_decode_attn_noalloc": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I,
+                                                _I, _F, _I, _P, _P]),
         "kvc_decode_attn_mla_workspace_size": (_Z, [_I, _I, _I, _I, _I]),
         "kvc_decode_attn_mla": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
                                      _F, _I, _P, _Z, _P]),
@@ -220,6 +222,20 @@ def kvc_append_decode_attn(q, k_cache, v_cache, seq_lens, k_new, v_new, out,
                                       d, scale, _dtype_code(q), _ptr(flag), wp, wn,
                                       _stream(stream))
     _check(st, "kvc_append_decode_attn")
+
+
+def kvc_append_decode_attn_noalloc(q, k_cache, v_cache, seq_lens, k_new, v_new, out,
+                                   lse=None, scale=None, flag=None, stream=None):
+    """kvc_append_decode_attn on the library's own scratch: no workspace,
+    nothing allocated by the call."""
+    B, n_h, d = q.shape
+    _, n_kv, L_max, _ = k_cache.shape
+    scale = _scale(scale, "kvc_append_decode_attn_noalloc")
+    st = lib().kvc_append_decode_attn_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                              _ptr(seq_lens), _ptr(k_new), _ptr(v_new),
+                                              _ptr(out), _ptr(lse), B, n_h, n_kv, L_max, d,
+                                              scale, _dtype_code(q), _ptr(flag), _stream(stream))
+    _check(st, "kvc_append_decode_attn_noalloc")
 
 
 def kvc_decode_attn_mla_workspace_size(B, n_h, L_max, d_c, d_r) -> int:

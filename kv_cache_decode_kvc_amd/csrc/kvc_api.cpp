@@ -202,6 +202,7 @@ const char* kvc_status_string(int status) {
     case KVC_ERR_MISALIGNED: return "pointer alignment rule broken";
     case KVC_ERR_HIP: return "HIP launch error";
     case KVC_ERR_BAD_ARG: return "bad argument (non-finite scale or negative override)";
+    case KVC_ERR_SCRATCH: return "the call needs more scratch than the library's static buffer holds";
     default: return "unknown status";
   }
 }
@@ -298,7 +299,7 @@ static int dense_common(const void* q, const void* k_cache, const void* v_cache,
                         const int32_t* block_table = nullptr, int max_blocks = 0,
                         int num_blocks = 0, int page_shift = 0,
                         const void* k_scales = nullptr, const void* v_scales = nullptr,
-                        bool fp4 = false) {
+                        bool fp4 = false, bool use_static = false) {
   // FP8 caches: q and out are bf16; the shape rules are those of bf16 with
   // d = 128 (checked by the caller).
   const DenseCheck c = check_dense_shape(B, n_h, n_kv, L_max, d, dtype, K, topk, fused, window);
@@ -317,8 +318,17 @@ static int dense_common(const void* q, const void* k_cache, const void* v_cache,
       (win_start && !aligned(win_start, 4)))
     return KVC_ERR_MISALIGNED;
   if (B == 0) return KVC_OK;
-  const int ws_status = check_workspace(c.ws, workspace, ws_bytes);
-  if (ws_status != KVC_OK) return ws_status;
+  const int64_t units = (int64_t)B * n_kv;
+  if (use_static) {
+    // the library's scratch replaces the workspace: the call must fit it
+    const size_t rows = (size_t)B * n_h * c.P_max;
+    const size_t partials = c.P_max > 1 ? round_up(rows * sizeof(float), 256) + rows * d * sizeof(float) : 0;
+    if (units > kStaticCounterWords || partials > kStaticScratchBytes - kStaticPartialOff)
+      return KVC_ERR_SCRATCH;
+  } else {
+    const int ws_status = check_workspace(c.ws, workspace, ws_bytes);
+    if (ws_status != KVC_OK) return ws_status;
+  }
 
   DenseParams p{};
   p.q = q;
@@ -330,7 +340,26 @@ static int dense_common(const void* q, const void* k_cache, const void* v_cache,
   p.idx = topk ? idx : nullptr; p.out = out; p.lse = lse;
   p.flag = (topk || fused) ? flag : nullptr;
   p.B = B; p.n_h = n_h; p.n_kv = n_kv; p.G = n_h / n_kv; p.L_max = L_max;
-  fill_ws(p, c.ws, workspace, (size_t)c.P_max, fused);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (use_static) {
+    void* base = nullptr;
+    if (static_scratch(&base) != hipSuccess) return KVC_ERR_HIP;
+    int32_t* w = static_cast<int32_t*>(base);
+    char* part = static_cast<char*>(base) + kStaticPartialOff;
+    p.ws_cnt = nullptr; p.ws_lse = nullptr; p.ws_o = nullptr; p.ws_bcnt = nullptr; p.ws_ucnt = nullptr;
+    if (c.P_max > 1) {
+      p.ws_cnt = w;
+      p.ws_lse = reinterpret_cast<float*>(part);
+      p.ws_o = reinterpret_cast<float*>(part + round_up((size_t)B * n_h * c.P_max * sizeof(float), 256));
+    }
+    if (fused) {
+      p.ws_bcnt = w + kStaticCounterWords;
+      p.ws_ucnt = w + 2 * kStaticCounterWords;
+    }
+    if (launch_clear_static_counters(base, (int)units, B, s) != hipSuccess) return KVC_ERR_HIP;
+  } else {
+    fill_ws(p, c.ws, workspace, (size_t)c.P_max, fused);
+  }
   p.d = d; p.K = topk ? K : 0; p.S = c.S; p.P_max = (int)c.P_max; p.even = c.even;
   p.scale_log2 = scale * 1.4426950408889634f;
   p.out_scale = 1.f;
@@ -342,9 +371,8 @@ static int dense_common(const void* q, const void* k_cache, const void* v_cache,
   p.page_shift = page_shift;
   if (block_table) {
     p.flag = flag;
-    return launch_status(launch_dense_paged(p, static_cast<hipStream_t>(stream)));
+    return launch_status(launch_dense_paged(p, s));
   }
-  hipStream_t s = static_cast<hipStream_t>(stream);
   if (fp4) {
     p.k_scales = k_scales;
     p.v_scales = v_scales;
@@ -374,6 +402,17 @@ int kvc_append_decode_attn(const void* q, void* k_cache, void* v_cache,
   return dense_common(q, k_cache, v_cache, seq_lens, nullptr, 0, out, lse, B,
                       n_h, n_kv, L_max, d, scale, dtype, flag, workspace,
                       ws_bytes, stream, false, k_new, v_new, true);
+}
+
+int kvc_append_decode_attn_noalloc(const void* q, void* k_cache, void* v_cache,
+                                   int32_t* seq_lens, const void* k_new, const void* v_new,
+                                   void* out, float* lse, int B, int n_h, int n_kv, int L_max,
+                                   int d, float scale, kvc_dtype dtype, int32_t* flag,
+                                   void* stream) {
+  return dense_common(q, k_cache, v_cache, seq_lens, nullptr, 0, out, lse, B, n_h, n_kv, L_max,
+                      d, scale, dtype, flag, nullptr, 0, stream, false, k_new, v_new, true,
+                      false, 1.f, 1.f, 0, nullptr, nullptr, 0, 0, 0, nullptr, nullptr, false,
+                      /*use_static=*/true);
 }
 
 int kvc_decode_attn(const void* q, const void* k_cache, const void* v_cache,

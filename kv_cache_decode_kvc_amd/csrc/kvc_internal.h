@@ -169,6 +169,19 @@ inline WsLayout ws_layout(size_t units, size_t B, size_t n_h, size_t P_max,
   return w;
 }
 
+// The no-allocation entry point's scratch (static_scratch.hip): one
+// library-owned device array per GPU.  Three counter arrays of
+// kStaticCounterWords int32 (split tickets, per-sequence arrivals, per-unit
+// arrivals), then the split partials (lse, outputs) from kStaticPartialOff.
+constexpr size_t kStaticScratchBytes = (size_t)32 << 20;
+constexpr int kStaticCounterWords = 16384;
+constexpr size_t kStaticPartialOff = 3 * (size_t)kStaticCounterWords * sizeof(int32_t);
+// Device address of this device's scratch (looked up once per device).
+hipError_t static_scratch(void** ptr);
+// Zero the counter words a call uses (tickets and unit arrivals [0, units),
+// sequence arrivals [0, B)) on the call's stream.
+hipError_t launch_clear_static_counters(void* base, int units, int B, hipStream_t s);
+
 // Kernel launchers (defined in the .hip sources).
 hipError_t launch_append(const AppendParams& p, hipStream_t s);
 hipError_t launch_append_fp8(const AppendParams& p, hipStream_t s);

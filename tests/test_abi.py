@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_status_strings(L):
-    for code in range(-8, 1):
+    for code in range(-9, 1):
         assert kvc.kvc_status_string(code)
     assert kvc.kvc_status_string(-99) == "unknown status"
 
@@ -369,3 +369,31 @@ def test_binding_requires_scale():
                  lambda: kvc.kvc_decode_attn_topk(q, kc, kc, sl, sl.view(1, 1, 1), q)):
         with pytest.raises(TypeError, match="scale is required"):
             call()
+
+
+def test_noalloc_limits_and_validation(L):
+    """The no-allocation fused call checks arguments like the workspace
+    variant and rejects calls that do not fit the library's scratch
+    (KVC_ERR_SCRATCH), all before any HIP call."""
+    def na(**kw):
+        a = dict(q=A16, k=A16, v=A16, sl=A4, kn=A16, vn=A16, out=A16, lse=NULL, B=2, n_h=8,
+                 n_kv=2, L_max=64, d=128, scale=0.1, dt=kvc.KVC_BF16, flag=NULL, stream=NULL)
+        a.update(kw)
+        return L.kvc_append_decode_attn_noalloc(a["q"], a["k"], a["v"], a["sl"], a["kn"], a["vn"],
+                                                a["out"], a["lse"], a["B"], a["n_h"], a["n_kv"],
+                                                a["L_max"], a["d"], a["scale"], a["dt"], a["flag"],
+                                                a["stream"])
+    assert na(kn=NULL) == -1
+    assert na(n_h=7) == -2
+    assert na(dt=7) == -3
+    assert na(d=96) == -4
+    assert na(q=A8) == -6
+    assert na(scale=float("nan")) == -8
+    assert na(B=0) == 0
+    # more (sequence, KV head) units than counter slots
+    assert na(B=2049, n_h=64, n_kv=8, L_max=4096) == -9
+    # split partials beyond the scratch: 64 sequences x 128 heads at 32768
+    assert na(B=64, n_h=128, n_kv=8, L_max=32768) == -9
+    # the benchmark's GQA layer shape fits (its own workspace is below 32 MiB)
+    need = L.kvc_append_decode_attn_workspace_size(32, 64, 8, 32807, 128, kvc.KVC_BF16)
+    assert 0 < need < 32 << 20
