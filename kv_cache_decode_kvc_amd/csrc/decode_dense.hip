@@ -993,21 +993,35 @@ __global__ __launch_bounds__(256) void dense_generic_kernel(DenseParams p) {
 #pragma unroll
       for (int u = 0; u < U; ++u) o[h][u] *= alpha;
     }
+    // Value rows eight at a time, all eight loads in flight before the
+    // multiply-adds (one row per position serialised each load's latency).
+    // A slot past the block or not attended loads the split's first row (or
+    // row 0 for top-k, which the allocation always holds) and is skipped.
     const int nrows = min(64, end - blk);
-    for (int tt = 0; tt < nrows; ++tt) {
-      const int vt = __builtin_amdgcn_readlane((int)valid, tt);
-      if (!vt) continue;
-      const int rt = __builtin_amdgcn_readlane(row, tt);
-      const T* vrow = vb + (size_t)rt * D;
-      float v[U];
+    const int safe = TOPK ? 0 : start;
+    for (int t0 = 0; t0 < nrows; t0 += 8) {
+      float v[8][U];
+      bool ok[8];
 #pragma unroll
-      for (int u = 0; u < U; ++u) v[u] = ld_f32<T>(vrow + lane + 64 * u);
+      for (int e = 0; e < 8; ++e) {
+        const int tt = min(t0 + e, nrows - 1);
+        ok[e] = t0 + e < nrows && __builtin_amdgcn_readlane((int)valid, tt) != 0;
+        const int rt = ok[e] ? __builtin_amdgcn_readlane(row, tt) : safe;
+        const T* vrow = vb + (size_t)rt * D;
 #pragma unroll
-      for (int h = 0; h < kMaxGroup; ++h) {
-        if (h >= G) continue;
-        const float pt = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pw[h]), tt));
+        for (int u = 0; u < U; ++u) v[e][u] = ld_f32<T>(vrow + lane + 64 * u);
+      }
 #pragma unroll
-        for (int u = 0; u < U; ++u) o[h][u] += pt * v[u];
+      for (int e = 0; e < 8; ++e) {
+        if (!ok[e]) continue;
+#pragma unroll
+        for (int h = 0; h < kMaxGroup; ++h) {
+          if (h >= G) continue;
+          const float pt =
+              __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pw[h]), t0 + e));
+#pragma unroll
+          for (int u = 0; u < U; ++u) o[h][u] += pt * v[e][u];
+        }
       }
     }
   }
