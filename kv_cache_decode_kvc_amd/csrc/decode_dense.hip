@@ -648,29 +648,40 @@ template <bool FP8, bool FP4> struct ChunkOf { using T = Chunk; };
 template <> struct ChunkOf<true, false> { using T = ChunkF8; };
 template <> struct ChunkOf<false, true> { using T = ChunkF4; };
 
-template <bool TOPK, bool APPEND, bool FP8 = false, bool PAGED = false, bool FP4 = false>
-__global__ __launch_bounds__(256, 2) void dense_mfma_kernel(DenseParams p) {
+// Persistent form: thread 0 takes the next item index from the device
+// counter right before the split merge (whose round trips hide the
+// atomic's) and leaves it in LDS; nothing is held through the main loop.
+struct NextItem {
+  int32_t* counter;   // null: one item per workgroup
+  int base;
+  int* slot;          // LDS
+};
+
+__device__ inline int fetch_next_begin(const NextItem& nx) {
+  return (nx.counter && threadIdx.x == 0) ? nx.base + atomicAdd(nx.counter, 1) : 0;
+}
+__device__ inline void fetch_next_end(const NextItem& nx, int v) {
+  if (nx.counter && threadIdx.x == 0) *nx.slot = v;
+}
+
+// One item of the MFMA kernels: (sequence b, KV head j, split) once the
+// attended length n is known (for the fused call also the length state);
+// for top-k the first two chunks' list entries are already in flight in I0
+// and I1.  Ends after the split merge; the caller owns the length bump.
+//
+// LAZY_NEW (persistent form): the new row of a fused append is attended by
+// split 0 instead of the last split, and its pieces are loaded only after
+// split 0's main loop, so they hold no registers through it.  (Split 0 is
+// drawn early, so the extra round trip stays off the end of the launch; the
+// one-workgroup-per-split form keeps them prefetched in the last, shortest
+// split, where a launch of one round waits for its slowest split.)
+template <bool TOPK, bool APPEND, bool FP8, bool PAGED, bool FP4, bool LAZY_NEW = false>
+__device__ __forceinline__ void dense_mfma_item(const DenseParams& p, int b, int j, int split,
+                                                int n, const LengthState& ls, MergeLds<128>& L,
+                                                ChunkIdx& I0, ChunkIdx& I1, const NextItem& nx) {
   static_assert(!FP8 || (!TOPK && !APPEND), "FP8 caches: plain decode only");
   static_assert(!PAGED || (!TOPK && !APPEND && !FP8), "paged caches: plain decode only");
   static_assert(!FP4 || (!TOPK && !APPEND && !FP8 && !PAGED), "FP4 caches: plain decode only");
-  __shared__ MergeLds<128> L;
-  int b, j, split;
-  decode_unit(p, b, j, split);
-  // Top-k: a split's slots and the list do not depend on the sequence
-  // length, so the list entries of the first two chunks go out before the
-  // length is read (the two round trips overlap).
-  ChunkIdx I0, I1;
-  if constexpr (TOPK) {
-    const int St = dense_split_size(p.K, p.S, p.P_max, p.even);
-    const int l0 = threadIdx.x & 63;
-    const int cs0 = split * St + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * kDenseChunk;
-    const __amdgpu_buffer_rsrc_t ir0 =
-        make_rsrc(p.idx + ((size_t)b * p.n_kv + j) * p.K, (uint32_t)p.K * 4u);
-    load_idx(I0, cs0, ir0, l0 & 15, l0 >> 4);
-    load_idx(I1, cs0 + kDenseChunk * 4, ir0, l0 & 15, l0 >> 4);
-  }
-  LengthState ls;
-  const int n = attended_length<APPEND, 128, uint16_t, false>(p, b, j, split, ls);
   const int lo = TOPK ? 0 : window_low(p, b, n);    // window mode only (not fused)
   // Fused append: the new row (slot n - 1) is attended from registers, so
   // the splits cover only the rows already in the cache.  A sequence of 4096
@@ -681,8 +692,9 @@ __global__ __launch_bounds__(256, 2) void dense_mfma_kernel(DenseParams p) {
   const int S = dense_split_size(count, p.S, p.P_max, p.even);
   const int nsplit = dense_num_splits(count, S);
   if (split >= nsplit || (count == 0 && !reg_new)) {
+    const int nxt = fetch_next_begin(nx);
     if (split == 0) write_empty<uint16_t, 128>(p, b, j);
-    complete_length<APPEND>(p, b, j, ls);
+    fetch_next_end(nx, nxt);
     return;
   }
   int start, end;
@@ -701,7 +713,10 @@ __global__ __launch_bounds__(256, 2) void dense_mfma_kernel(DenseParams p) {
       PAGED ? ((uint32_t)p.num_blocks * (uint32_t)p.n_kv << p.page_shift) * kRowBytes : 0u;
   // Rows a load may touch: the attended ones, less the new row of a fused
   // append (slot n - 1 is never read back; rows past the range read zeros).
-  const uint32_t n_rows = (uint32_t)(n - (reg_new ? 1 : 0));
+  // (read-first-lane: a select on the length state may land in a vector
+  // register, and a buffer range in one makes each load a read-first-lane
+  // loop)
+  const uint32_t n_rows = (uint32_t)__builtin_amdgcn_readfirstlane(n - (reg_new ? 1 : 0));
   const __amdgpu_buffer_rsrc_t kr =
       PAGED ? make_rsrc(p.k, pool_bytes)
             : make_rsrc((const char*)p.k + unit * unit_bytes, n_rows * kRowBytes);
@@ -744,9 +759,9 @@ __global__ __launch_bounds__(256, 2) void dense_mfma_kernel(DenseParams p) {
   // fused append: slot of the new row (or -1), and its source rows
   const int new_slot = (APPEND && ls.ok) ? ls.n_raw : -1;
   u32x4 knr[4], vnr;
-  if constexpr (APPEND) {
-    const u32x4* kn = reinterpret_cast<const u32x4*>(p.k_new) + unit * 16;
-    const u32x4* vn = reinterpret_cast<const u32x4*>(p.v_new) + unit * 16;
+  const u32x4* kn = reinterpret_cast<const u32x4*>(p.k_new) + unit * 16;
+  const u32x4* vn = reinterpret_cast<const u32x4*>(p.v_new) + unit * 16;
+  if constexpr (APPEND && !LAZY_NEW) {
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) knr[kk] = kn[kk * 4 + g];
     vnr = vn[r];
@@ -830,13 +845,18 @@ __global__ __launch_bounds__(256, 2) void dense_mfma_kernel(DenseParams p) {
     }
   }
   if constexpr (APPEND) {
-    // The last split folds in the new row as a one-row chunk, on the wave
-    // with the fewest cached chunks (wave 3 when they are even), and that
-    // wave writes the row to the cache: lanes r = 0 hold all 16 pieces of
-    // the K row, lanes g = 0 all 16 of the V row.
+    // The last split (split 0 with LAZY_NEW) folds in the new row as a
+    // one-row chunk, on the wave with the fewest cached chunks (wave 3 when
+    // they are even), and that wave writes the row to the cache: lanes r = 0
+    // hold all 16 pieces of the K row, lanes g = 0 all 16 of the V row.
     const int chunks = (end - start + kDenseChunk - 1) / kDenseChunk;
     const int new_wave = (chunks & 3) ? (chunks & 3) : 3;
-    if (new_slot >= 0 && split == nsplit - 1 && wave == new_wave) {
+    if (new_slot >= 0 && split == (LAZY_NEW ? 0 : nsplit - 1) && wave == new_wave) {
+      if constexpr (LAZY_NEW) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) knr[kk] = kn[kk * 4 + g];
+        vnr = vn[r];
+      }
       const size_t dst = (unit * p.L_max + new_slot) * 16;
       if (r == 0) {
 #pragma unroll
@@ -870,9 +890,186 @@ __global__ __launch_bounds__(256, 2) void dense_mfma_kernel(DenseParams p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) L.o[wave][r][(4 * g + i) * 8 + m] = st.acc[m][i];
   __syncthreads();
+  const int nxt = fetch_next_begin(nx);
   finish_split<uint16_t, 128>(p, b, j, split, nsplit, L);
+  fetch_next_end(nx, nxt);
+}
+
+// One workgroup per (sequence, KV head, split of the longest possible
+// length); splits past a sequence's length write nothing (split 0 of an
+// empty sequence writes the zero row).
+template <bool TOPK, bool APPEND, bool FP8 = false, bool PAGED = false, bool FP4 = false>
+__global__ __launch_bounds__(256, 2) void dense_mfma_kernel(DenseParams p) {
+  __shared__ MergeLds<128> L;
+  int b, j, split;
+  decode_unit(p, b, j, split);
+  // Top-k: a split's slots and the list do not depend on the sequence
+  // length, so the list entries of the first two chunks go out before the
+  // length is read (the two round trips overlap).
+  ChunkIdx I0, I1;
+  if constexpr (TOPK) {
+    const int St = dense_split_size(p.K, p.S, p.P_max, p.even);
+    const int l0 = threadIdx.x & 63;
+    const int cs0 = split * St + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * kDenseChunk;
+    const __amdgpu_buffer_rsrc_t ir0 =
+        make_rsrc(p.idx + ((size_t)b * p.n_kv + j) * p.K, (uint32_t)p.K * 4u);
+    load_idx(I0, cs0, ir0, l0 & 15, l0 >> 4);
+    load_idx(I1, cs0 + kDenseChunk * 4, ir0, l0 & 15, l0 >> 4);
+  }
+  LengthState ls;
+  const int n = attended_length<APPEND, 128, uint16_t, false>(p, b, j, split, ls);
+  dense_mfma_item<TOPK, APPEND, FP8, PAGED, FP4>(p, b, j, split, n, ls, L, I0, I1,
+                                                 NextItem{nullptr, 0, nullptr});
   // (after the merge: its atomic is off the path to the output)
   complete_length<APPEND>(p, b, j, ls);
+}
+
+// ---------------------------------------------------------------------------
+// Persistent form for large problems (fixed split size S): a grid of about
+// two workgroups per compute unit, each taking (sequence, KV head, split)
+// items from a device counter until none are left.
+//
+// Each workgroup first reads every sequence's length (and window start)
+// into LDS and derives the item list from them: all units' whole splits of
+// S positions first, then every unit's last, shorter split (or its one
+// empty item), so the items drawn last are the short ones and the final
+// workgroups finish close together.  Against one workgroup per (unit,
+// split) of the longest possible length, no workgroup is launched for a
+// split past its sequence's length, the length is read once per workgroup
+// instead of once per item, and the fused call needs no arrival counters:
+// every workgroup reads the lengths before it takes its first item and
+// counts itself done after its last, so the workgroup that counts last
+// (a device-scope counter) knows that every workgroup has read the old
+// lengths, writes the new ones and resets the counters.  No workgroup
+// waits for another, so correctness does not depend on how many workgroups
+// are resident at once.
+// ---------------------------------------------------------------------------
+__device__ inline int last_at_or_below(const int* a, int n, int k) {
+  // largest u in [0, n) with a[u] <= k (a non-decreasing, a[0] <= k)
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a[mid] <= k) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+template <bool APPEND, bool FP8 = false, bool PAGED = false, bool FP4 = false>
+__global__ __launch_bounds__(256, 2) void dense_persist_kernel(DenseParams p) {
+  __shared__ MergeLds<128> L;
+  __shared__ int s_nraw[kPersistMaxB];          // lengths as read
+  __shared__ int s_cnt[kPersistMaxB];           // positions the splits of a unit cover
+  __shared__ int s_full[kPersistMaxUnits + 1];  // exclusive prefix over units: whole splits
+  __shared__ int s_part[kPersistMaxUnits + 1];  // exclusive prefix over units: last items
+  __shared__ uint32_t s_scan[256];
+  __shared__ int s_next;
+
+  const int tid = threadIdx.x;
+  const int B = p.B, n_kv = p.n_kv, units = p.B * p.n_kv, S = p.S;
+  for (int b = tid; b < B; b += 256) {
+    const int n_raw = p.seq_lens[b];
+    int count;
+    if constexpr (APPEND) {
+      // the new row is attended from registers: the splits cover the cached rows
+      count = (n_raw >= 0 && n_raw < p.L_max) ? n_raw : min(max(n_raw, 0), p.L_max);
+    } else {
+      const int n = min(max(n_raw, 0), p.L_max);
+      count = n - window_low(p, b, n);
+    }
+    s_nraw[b] = n_raw;
+    s_cnt[b] = count;
+  }
+  __syncthreads();
+  // per unit: count / S whole splits and one last item (a shorter split, or
+  // the empty item of a unit with nothing cached); exclusive prefix sums,
+  // each thread a run of units, the two counts packed (whole << 12 | last:
+  // at most 2048 units of at most 256 whole splits, so the sums stay below
+  // 2^31 + 2^12)
+  const int per = (units + 255) / 256;
+  const int u0 = min(tid * per, units), u1 = min(u0 + per, units);
+  uint32_t packed = 0;
+  for (int u = u0; u < u1; ++u) {
+    const int c = s_cnt[u / n_kv];
+    packed += ((uint32_t)(c / S) << 12) + ((c % S != 0 || c == 0) ? 1u : 0u);
+  }
+  s_scan[tid] = packed;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    const uint32_t x = tid >= off ? s_scan[tid - off] : 0u;
+    __syncthreads();
+    s_scan[tid] += x;
+    __syncthreads();
+  }
+  {
+    const uint32_t ex = tid ? s_scan[tid - 1] : 0u;
+    int sf = (int)(ex >> 12), sp = (int)(ex & 4095u);
+    for (int u = u0; u < u1; ++u) {
+      const int c = s_cnt[u / n_kv];
+      s_full[u] = sf;
+      s_part[u] = sp;
+      sf += c / S;
+      sp += (c % S != 0 || c == 0) ? 1 : 0;
+    }
+    if (tid == 0) {
+      s_full[units] = (int)(s_scan[255] >> 12);
+      s_part[units] = (int)(s_scan[255] & 4095u);
+    }
+  }
+  __syncthreads();
+  const int total_full = s_full[units];
+  const int total = total_full + s_part[units];
+
+  ChunkIdx I0, I1;    // (top-k only; unused here)
+  int k = blockIdx.x;
+  const NextItem nx{p.ws_sched, (int)gridDim.x, &s_next};
+  while (k < total) {
+    int u, split;
+    if (k < total_full) {
+      u = last_at_or_below(s_full, units, k);
+      split = k - s_full[u];
+    } else {
+      u = last_at_or_below(s_part, units, k - total_full);
+      split = s_cnt[u / n_kv] / S;
+    }
+    u = __builtin_amdgcn_readfirstlane(u);
+    split = __builtin_amdgcn_readfirstlane(split);
+    const int b = u / n_kv, j = u - b * n_kv;
+    // (uniform values: a length in a vector register would make every
+    // buffer descriptor divergent, and each load a read-first-lane loop)
+    LengthState ls;
+    ls.n_raw = __builtin_amdgcn_readfirstlane(s_nraw[b]);
+    ls.ok = ls.n_raw >= 0 && ls.n_raw < p.L_max;
+    ls.unit_prev = 0;
+    int n;
+    if constexpr (APPEND) {
+      n = ls.ok ? ls.n_raw + 1 : min(max(ls.n_raw, 0), p.L_max);
+      if (!ls.ok && j == 0 && split == 0 && tid == 0 && p.flag) atomicOr(p.flag, 1);
+    } else {
+      n = min(max(ls.n_raw, 0), p.L_max);
+    }
+    n = __builtin_amdgcn_readfirstlane(n);
+    dense_mfma_item<false, APPEND, FP8, PAGED, FP4, true>(p, b, j, split, n, ls, L, I0, I1, nx);
+    __syncthreads();
+    k = __builtin_amdgcn_readfirstlane(s_next);
+    __syncthreads();   // every wave has read s_next before thread 0 writes it again
+  }
+  // Done: the workgroup that counts last writes the new lengths (fused
+  // call) and resets the counters for the next call.
+  if (tid == 0) s_next = atomicAdd(p.ws_sched + 1, 1) == (int)gridDim.x - 1;
+  __syncthreads();
+  if (s_next) {
+    if constexpr (APPEND) {
+      for (int b = tid; b < B; b += 256) {
+        const int n_raw = s_nraw[b];
+        if (n_raw >= 0 && n_raw < p.L_max) p.seq_lens_rw[b] = n_raw + 1;
+      }
+    }
+    if (tid == 0) {
+      p.ws_sched[0] = 0;
+      p.ws_sched[1] = 0;
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1052,29 +1249,46 @@ static dim3 dense_grid(const DenseParams& p) {
   return dim3((unsigned)((size_t)p.B * p.n_kv * p.P_max));
 }
 
+// Persistent grid: two workgroups per compute unit (the kernels'
+// occupancy), never more than there can be items.
+static dim3 persist_grid(const DenseParams& p) {
+  const size_t most = (size_t)p.B * p.n_kv * p.P_max;
+  const size_t g = (size_t)kPersistWgs < most ? (size_t)kPersistWgs : most;
+  return dim3((unsigned)g);
+}
+
+template <bool APPEND, bool FP8, bool PAGED, bool FP4>
+static void launch_mfma_t(const DenseParams& p, hipStream_t s) {
+  if (p.persist)
+    hipLaunchKernelGGL((dense_persist_kernel<APPEND, FP8, PAGED, FP4>), persist_grid(p), dim3(256),
+                       0, s, p);
+  else
+    hipLaunchKernelGGL((dense_mfma_kernel<false, APPEND, FP8, PAGED, FP4>), dense_grid(p),
+                       dim3(256), 0, s, p);
+}
+
 hipError_t launch_dense_mfma(const DenseParams& p, bool topk, bool append, hipStream_t s) {
   if (topk)
     hipLaunchKernelGGL((dense_mfma_kernel<true, false>), dense_grid(p), dim3(256), 0, s, p);
   else if (append)
-    hipLaunchKernelGGL((dense_mfma_kernel<false, true>), dense_grid(p), dim3(256), 0, s, p);
+    launch_mfma_t<true, false, false, false>(p, s);
   else
-    hipLaunchKernelGGL((dense_mfma_kernel<false, false>), dense_grid(p), dim3(256), 0, s, p);
+    launch_mfma_t<false, false, false, false>(p, s);
   return hipGetLastError();
 }
 
 hipError_t launch_dense_paged(const DenseParams& p, hipStream_t s) {
-  hipLaunchKernelGGL((dense_mfma_kernel<false, false, false, true>), dense_grid(p), dim3(256), 0, s, p);
+  launch_mfma_t<false, false, true, false>(p, s);
   return hipGetLastError();
 }
 
 hipError_t launch_dense_fp8(const DenseParams& p, hipStream_t s) {
-  hipLaunchKernelGGL((dense_mfma_kernel<false, false, true>), dense_grid(p), dim3(256), 0, s, p);
+  launch_mfma_t<false, true, false, false>(p, s);
   return hipGetLastError();
 }
 
 hipError_t launch_dense_fp4(const DenseParams& p, hipStream_t s) {
-  hipLaunchKernelGGL((dense_mfma_kernel<false, false, false, false, true>), dense_grid(p),
-                     dim3(256), 0, s, p);
+  launch_mfma_t<false, false, false, true>(p, s);
   return hipGetLastError();
 }
 

@@ -99,6 +99,7 @@ struct DenseCheck {
   int S;
   int64_t P_max;
   int even;
+  int persist;
   WsLayout ws;
 };
 
@@ -107,7 +108,7 @@ struct DenseCheck {
 DenseCheck check_dense_shape(int B, int n_h, int n_kv, int L_max, int d,
                              int dtype, int K, bool topk, bool fused = false,
                              int window = 0) {
-  DenseCheck c{KVC_OK, 0, 1, 0, {}};
+  DenseCheck c{KVC_OK, 0, 1, 0, 0, {}};
   if (!good_dtype(dtype)) { c.status = KVC_ERR_BAD_DTYPE; return c; }
   if (B < 0 || n_h < 1 || n_kv < 1 || L_max < 1 || d < 1) {
     c.status = KVC_ERR_BAD_SHAPE; return c;
@@ -126,7 +127,12 @@ DenseCheck check_dense_shape(int B, int n_h, int n_kv, int L_max, int d,
   c.P_max = plan.P;
   c.even = plan.even;
   if (units * c.P_max >= kMaxOffset) { c.status = KVC_ERR_BAD_SHAPE; return c; }
-  c.ws = ws_layout((size_t)units, (size_t)B, (size_t)n_h, (size_t)c.P_max, (size_t)d, fused);
+  // Large problems (fixed split size) on the MFMA kernels run in the
+  // persistent form when the lengths and per-unit item counts fit its LDS.
+  c.persist = !c.even && !topk && dtype == KVC_BF16 && d == 128 && B <= kPersistMaxB &&
+              units <= kPersistMaxUnits;
+  c.ws = ws_layout((size_t)units, (size_t)B, (size_t)n_h, (size_t)c.P_max, (size_t)d, fused,
+                   c.persist != 0);
   if (c.ws.total >= (size_t)kMaxOffset) { c.status = KVC_ERR_UNSUPPORTED; return c; }
   return c;
 }
@@ -144,7 +150,9 @@ int launch_status(hipError_t e) { return e == hipSuccess ? KVC_OK : KVC_ERR_HIP;
 void fill_ws(DenseParams& p, const WsLayout& ws, void* workspace, size_t P_max,
              bool fused) {
   p.ws_cnt = nullptr; p.ws_lse = nullptr; p.ws_o = nullptr; p.ws_bcnt = nullptr;
+  p.ws_sched = nullptr;
   char* base = static_cast<char*>(workspace);
+  if (p.persist) p.ws_sched = reinterpret_cast<int32_t*>(base + ws.sched_off);
   if (P_max > 1) {
     p.ws_cnt = reinterpret_cast<int32_t*>(base + ws.cnt_off);
     p.ws_lse = reinterpret_cast<float*>(base + ws.lse_off);
@@ -340,6 +348,7 @@ static int dense_common(const void* q, const void* k_cache, const void* v_cache,
   p.idx = topk ? idx : nullptr; p.out = out; p.lse = lse;
   p.flag = (topk || fused) ? flag : nullptr;
   p.B = B; p.n_h = n_h; p.n_kv = n_kv; p.G = n_h / n_kv; p.L_max = L_max;
+  p.persist = c.persist;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (use_static) {
     void* base = nullptr;
@@ -356,6 +365,7 @@ static int dense_common(const void* q, const void* k_cache, const void* v_cache,
       p.ws_bcnt = w + kStaticCounterWords;
       p.ws_ucnt = w + 2 * kStaticCounterWords;
     }
+    p.ws_sched = p.persist ? w + kStaticSchedOff / sizeof(int32_t) : nullptr;
     if (launch_clear_static_counters(base, (int)units, B, s) != hipSuccess) return KVC_ERR_HIP;
   } else {
     fill_ws(p, c.ws, workspace, (size_t)c.P_max, fused);

@@ -80,7 +80,19 @@ struct DenseParams {
   // scale of every 16 channels [B, n_kv, L_max, d/16]
   const void* k_scales;
   const void* v_scales;
+  // persistent form (fixed split size, MFMA kernels): [0] next item, [1]
+  // workgroups done; both zero between calls
+  int persist;
+  int32_t* ws_sched;
 };
+
+// Persistent dense kernels: lengths and per-unit item counts live in LDS,
+// so the form is used up to these sizes (beyond them, one workgroup per
+// unit and split).  kPersistWgs workgroups: two per compute unit of a
+// 256-CU MI355X.
+constexpr int kPersistMaxB = 1024;
+constexpr int kPersistMaxUnits = 2048;
+constexpr int kPersistWgs = 512;
 
 // Pool bitmap words the selection kernel holds in LDS (one bit per block).
 constexpr int kSelectPoolWords = 12288;
@@ -118,7 +130,7 @@ struct MlaParams {
 };
 
 struct WsLayout {
-  size_t cnt_off, lse_off, o_off, bcnt_off, total;
+  size_t cnt_off, lse_off, o_off, bcnt_off, sched_off, total;
 };
 
 inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -150,9 +162,10 @@ __host__ __device__ inline void dense_split_range(int n, int S, int split, int& 
 
 // Workspace: [tickets per unit][partial lse][partial outputs] when a
 // sequence can need several splits, then (fused append-and-attend only) one
-// arrival counter per sequence followed by one per unit.
+// arrival counter per sequence followed by one per unit, then (persistent
+// form) a 256-byte block holding the two scheduling counters.
 inline WsLayout ws_layout(size_t units, size_t B, size_t n_h, size_t P_max,
-                          size_t d, bool fused = false) {
+                          size_t d, bool fused = false, bool persist = false) {
   WsLayout w{};
   size_t end = 0;
   if (P_max > 1) {
@@ -165,6 +178,10 @@ inline WsLayout ws_layout(size_t units, size_t B, size_t n_h, size_t P_max,
     w.bcnt_off = end;
     end += round_up((B + units) * sizeof(int32_t), 256);
   }
+  if (persist) {
+    w.sched_off = end;
+    end += 256;
+  }
   w.total = end;
   return w;
 }
@@ -175,7 +192,10 @@ inline WsLayout ws_layout(size_t units, size_t B, size_t n_h, size_t P_max,
 // arrivals), then the split partials (lse, outputs) from kStaticPartialOff.
 constexpr size_t kStaticScratchBytes = (size_t)32 << 20;
 constexpr int kStaticCounterWords = 16384;
-constexpr size_t kStaticPartialOff = 3 * (size_t)kStaticCounterWords * sizeof(int32_t);
+// (the two scheduling counters of the persistent form follow the three
+// counter arrays, in a 256-byte block of their own)
+constexpr size_t kStaticSchedOff = 3 * (size_t)kStaticCounterWords * sizeof(int32_t);
+constexpr size_t kStaticPartialOff = kStaticSchedOff + 256;
 // Device address of this device's scratch (looked up once per device).
 hipError_t static_scratch(void** ptr);
 // Zero the counter words a call uses (tickets and unit arrivals [0, units),

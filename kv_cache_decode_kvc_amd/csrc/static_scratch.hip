@@ -6,8 +6,9 @@
 // is a host-side stand-in, not a device address.
 //
 // Layout (kvc_internal.h): three counter arrays of kStaticCounterWords
-// int32 each (split tickets, per-sequence arrivals, per-unit arrivals), then
-// the split partials (lse, outputs) from kStaticPartialOff.  Each call
+// int32 each (split tickets, per-sequence arrivals, per-unit arrivals), the
+// persistent form's two scheduling counters, then the split partials (lse,
+// outputs) from kStaticPartialOff.  Each call
 // clears the counter words it will use before its main kernel (a small fill
 // kernel, so the call stays capturable in a HIP graph); the partials are
 // written before they are read.
@@ -28,14 +29,15 @@ std::mutex g_mu;
 void* g_addr[kMaxDevices];   // device address of `scratch` on each device (null: not looked up)
 
 __global__ __launch_bounds__(256) void clear_counters_kernel(int32_t* tickets, int32_t* seq_arrivals,
-                                                             int32_t* unit_arrivals, int units,
-                                                             int B) {
+                                                             int32_t* unit_arrivals, int32_t* sched,
+                                                             int units, int B) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i < units) {
     tickets[i] = 0;
     unit_arrivals[i] = 0;
   }
   if (i < B) seq_arrivals[i] = 0;
+  if (i < 2) sched[i] = 0;
 }
 
 }  // namespace
@@ -60,7 +62,8 @@ hipError_t launch_clear_static_counters(void* base, int units, int B, hipStream_
   int32_t* w = static_cast<int32_t*>(base);
   const int n = units > B ? units : B;
   hipLaunchKernelGGL(clear_counters_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
-                     w, w + kStaticCounterWords, w + 2 * kStaticCounterWords, units, B);
+                     w, w + kStaticCounterWords, w + 2 * kStaticCounterWords,
+                     w + kStaticSchedOff / sizeof(int32_t), units, B);
   return hipGetLastError();
 }
 
