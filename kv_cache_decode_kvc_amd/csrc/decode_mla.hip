@@ -303,14 +303,14 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_kernel(MlaParams p) {
     }
   }
 
-  // The first tiles (one per stage) go out right after the query loads, so
-  // the two latencies overlap; the query loads come first so that waiting
-  // for a tile also covers them.
+  // The first two tiles go out right after the query loads, so the two
+  // latencies overlap; the query loads come first so that waiting for a tile
+  // also covers them.  Tiles 2 and 3 follow during the first chunk's scores:
+  // with every workgroup starting at once, a smaller first burst lets the
+  // first tile (and the query) land sooner.
   auto issue_first = [&]() {
     issue_tile<kLpt>(smem, cr, start, blk0, lane);
-#pragma unroll
-    for (int k = 1; k < kStages; ++k)
-      if (nchunks > k) issue_tile<kLpt>(smem + k * kTileB, cr, start + k * kMlaChunk, blk0, lane);
+    if (nchunks > 1) issue_tile<kLpt>(smem + kTileB, cr, start + kMlaChunk, blk0, lane);
   };
 
   bf16x8 qop[kQRegs];
@@ -332,7 +332,7 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_kernel(MlaParams p) {
   // The copy of a later tile (when dma) is issued one block every NW
   // k-steps (kLpt = 36 / NW blocks per wave): each block occupies the address unit for a while, and spread
   // out its issue hides behind the MFMAs instead of stalling the wave.
-  auto scores = [&](uint32_t toff, bool dma, char* dstage, int dcs) {
+  auto scores = [&](uint32_t toff, bool dma, char* dstage, int dcs, bool dma2) {
     uint32_t qb[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
@@ -360,7 +360,17 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_kernel(MlaParams p) {
         asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(s) : "v"(aop), "v"(bop));
       else
         asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(aop), "v"(bop));
-      if (k % NW == 1 && dma) issue_block(dstage, cr, dcs, blk0 + k / NW, lane);
+      if (dma2) {
+        // two tiles (the first chunk): all of the first before any of the
+        // second, so that the in-order vector memory counter waits below
+        // still mean "these tiles landed"
+        constexpr int h = NW / 2;
+        if (k % h == h - 1)
+          issue_block(dstage + (k < kKSteps / 2 ? 0 : kTileB), cr,
+                      dcs + (k < kKSteps / 2 ? 0 : kMlaChunk), blk0 + (k % (kKSteps / 2)) / h, lane);
+      } else if (k % NW == 1 && dma) {
+        issue_block(dstage, cr, dcs, blk0 + k / NW, lane);
+      }
       const int kn = k + kQkAhead;
       if (kn < kKSteps) {
         A[k % kQkAhead] = lds_load16(smem, qb[kn & 3] + (kn >> 2) * 128);
@@ -394,17 +404,17 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_kernel(MlaParams p) {
     l_run = 0.f;
     if (!first_pass) issue_first();
     first_pass = false;
-    // (tile k >= 4 is issued during the scores of chunk k - 3, into the
-    // stage of chunk k - 4)
+    // (tiles 2 and 3 are issued during the scores of chunk 0, tile k >= 4
+    // during those of chunk k - 3, into the stage of chunk k - 4)
 
     float m_seen = m_ref;     // largest score of this head in this pass
     bool restart = false;
     for (int c = 0; c < nchunks; ++c) {
       const int cs = start + c * kMlaChunk;
-      // Tile c landed (tiles issued after it: c + 1 and c + 2, and c + 3 on
+      // Tile c landed (tiles issued after it: c + 1 and c + 2, only c + 1 on
       // the first chunk, may still be in flight); every wave is done with the
       // stage of chunk c - 1 and has cast its vote on it.
-      const int after = c == 0 ? min(kStages - 1, nchunks - 1) : min(kStages - 2, nchunks - 1 - c);
+      const int after = c == 0 ? min(1, nchunks - 1) : min(kStages - 2, nchunks - 1 - c);
       if (after >= 3) wait_vmcnt<3 * kLpt>();
       else if (after == 2) wait_vmcnt<2 * kLpt>();
       else if (after == 1) wait_vmcnt<kLpt>();
@@ -414,22 +424,11 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_kernel(MlaParams p) {
       // chunk's scores, so the read's latency hides behind the MFMAs)
       const u32x4 vw = *reinterpret_cast<const u32x4*>(s_vote[(c - 1) & 1]);
       const uint32_t toff = (uint32_t)((c % kStages) * kTileB);
-      const f32x16 S = scores(toff, c >= 1 && c + kStages - 1 < nchunks,
-                              smem + ((c + kStages - 1) % kStages) * kTileB,
-                              cs + (kStages - 1) * kMlaChunk);
+      const bool first = c == 0;
+      const f32x16 S = scores(toff, first ? nchunks > 2 : c + kStages - 1 < nchunks,
+                              smem + ((first ? 2 : c + kStages - 1) % kStages) * kTileB,
+                              cs + (first ? 2 : kStages - 1) * kMlaChunk, first && nchunks > 3);
       if (c > 0 && !scan && !scanned && any_vote4<NW>(vw)) { restart = true; break; }
-
-      // the first value MFMAs' reads go out ahead of the softmax
-      uint32_t tb[2][2];
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int cp = 0; cp < 2; ++cp) {
-          tb[t][cp] = toff + wtr[t][cp];
-          asm volatile("" : "+v"(tb[t][cp]));
-        }
-      u32x2 trlo[kPvBuf], trhi[kPvBuf];
-      pv_head(std::make_integer_sequence<int, kPvAhead>{}, trlo, trhi, tb);
 
       // weights of this lane's 16 positions of head r
       float sv[16];
@@ -449,6 +448,21 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_kernel(MlaParams p) {
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sv[i]);
       m_seen = fmaxf(m_seen, mx);
       if (scan) continue;
+
+      // the first value MFMAs' reads go out ahead of the rest of the softmax
+      // (only on a pass that uses them: a read left in flight into registers
+      // the compiler takes as free could overwrite them)
+      uint32_t tb[2][2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int cp = 0; cp < 2; ++cp) {
+          tb[t][cp] = toff + wtr[t][cp];
+          asm volatile("" : "+v"(tb[t][cp]));
+        }
+      u32x2 trlo[kPvBuf], trhi[kPvBuf];
+      pv_head(std::make_integer_sequence<int, kPvAhead>{}, trlo, trhi, tb);
+
       if (__builtin_amdgcn_readfirstlane(__float_as_int(m_ref)) == __float_as_int(kNegInf)) {
         // first valid chunk (nothing accumulated yet); the empty asm keeps
         // the exchange inside this branch
