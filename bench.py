@@ -773,7 +773,7 @@ class SelectWorkload(Workload):
     head, the 2048 highest of 131072 indexer scores (float32, seeded N(0,1)),
     32 index sets over 16 distinct score buffers (512 MB)."""
 
-    kernel = "topk_select_kernel"
+    kernel = "seg_select_kernel"
     unit_name = "score rows"
     NBUF = 16
 
@@ -789,10 +789,12 @@ class SelectWorkload(Workload):
         self.lens = torch.full((B,), L, dtype=torch.int32, device="cuda")
         self.out = [torch.empty(B, R, cfg.K, dtype=torch.int32, device="cuda")
                     for _ in range(self.layers)]
+        self.ws = kvc.workspace(kvc.kvc_topk_select_workspace_size(B, R, L, cfg.K))
 
     def step(self):
         for l in range(self.layers):
-            self.kvc.kvc_topk_select(self.S[l % self.NBUF], self.lens, self.out[l])
+            self.kvc.kvc_topk_select(self.S[l % self.NBUF], self.lens, self.out[l],
+                                     workspace=self.ws)
 
     decode_only = step
     kernel_only = step

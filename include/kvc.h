@@ -378,10 +378,19 @@ int kvc_decode_attn_topk(const void* q, const void* k_cache,
  *   K >= 1; L_max < 2^29 (else KVC_ERR_UNSUPPORTED); pool mode: P >= 1,
  *   pool_block >= 1, ceil(L_max / pool_block) <= 393216 (else
  *   KVC_ERR_UNSUPPORTED).
+ * Workspace (optional, same rules as the decode calls): with workspace !=
+ * NULL, no pool and a non-zero kvc_topk_select_workspace_size, each row is
+ * cut into segments spread over the compute units (a workspace smaller than
+ * the queried size is KVC_ERR_WORKSPACE, one not 256-byte aligned
+ * KVC_ERR_MISALIGNED); with workspace == NULL, in pool mode, or when the
+ * query returns 0 (rows longer than 2^18 positions, or enough rows to fill
+ * the device), one workgroup takes each row.  The result is the same either
+ * way.
  */
+size_t kvc_topk_select_workspace_size(int B, int R, int L_max, int K);
 int kvc_topk_select(const float* scores, const int32_t* seq_lens, const int32_t* pool,
                     int P, int pool_block, int32_t* idx_out, int B, int R, int L_max,
-                    int K, void* stream);
+                    int K, void* workspace, size_t ws_bytes, void* stream);
 
 /* Text for a status code (static storage). */
 const char* kvc_status_string(int status);

@@ -76,7 +76,8 @@ def lib() -> ctypes.CDLL:
         "kvc_decode_attn_paged_workspace_size": (_Z, [_I, _I, _I, _I, _I, _I, _I]),
         "kvc_decode_attn_paged": (_I, [_P, _P, _P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _I,
                                        _F, _I, _P, _P, _Z, _P]),
-        "kvc_topk_select": (_I, [_P, _P, _P, _I, _I, _P, _I, _I, _I, _I, _P]),
+        "kvc_topk_select_workspace_size": (_Z, [_I, _I, _I, _I]),
+        "kvc_topk_select": (_I, [_P, _P, _P, _I, _I, _P, _I, _I, _I, _I, _P, _Z, _P]),
         "kvc_append_fp8": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _F, _P, _P]),
         "kvc_decode_attn_fp8_workspace_size": (_Z, [_I, _I, _I, _I, _I]),
         "kvc_decode_attn_fp8": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I,
@@ -329,18 +330,25 @@ def kvc_decode_attn_paged(q, k_pool, v_pool, block_table, seq_lens, out, lse=Non
     _check(st, "kvc_decode_attn_paged")
 
 
-def kvc_topk_select(scores, seq_lens, idx_out, pool=None, pool_block=8, stream=None):
+def kvc_topk_select_workspace_size(B, R, L_max, K) -> int:
+    return lib().kvc_topk_select_workspace_size(B, R, L_max, K)
+
+
+def kvc_topk_select(scores, seq_lens, idx_out, pool=None, pool_block=8, workspace=None,
+                    stream=None):
     """K highest-scoring positions per row of scores [B, R, L_max] (float32)
     into idx_out [B, R, K] (int32), ascending, -1 padded; optional pool
-    [B, R, P] of pool_block-position block ids."""
+    [B, R, P] of pool_block-position block ids; optional workspace (see
+    kvc_topk_select_workspace_size) for the segmented form."""
     import torch
     if scores.dtype != torch.float32 or idx_out.dtype != torch.int32:
         raise TypeError("scores must be float32 and idx_out int32")
     B, R, L_max = scores.shape
     K = idx_out.shape[-1]
     P = 0 if pool is None else pool.shape[-1]
+    wp, wn = _ws(workspace)
     st = lib().kvc_topk_select(_ptr(scores), _ptr(seq_lens), _ptr(pool), P, pool_block,
-                               _ptr(idx_out), B, R, L_max, K, _stream(stream))
+                               _ptr(idx_out), B, R, L_max, K, wp, wn, _stream(stream))
     _check(st, "kvc_topk_select")
 
 

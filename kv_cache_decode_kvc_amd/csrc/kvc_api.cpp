@@ -607,9 +607,14 @@ int kvc_decode_attn_mla(const void* q, const void* ckv,
   return launch_status(launch_mla(p, static_cast<hipStream_t>(stream)));
 }
 
+size_t kvc_topk_select_workspace_size(int B, int R, int L_max, int K) {
+  if (B < 1 || R < 1 || L_max < 1 || K < 1 || L_max >= kSelectMaxRow) return 0;
+  return select_seg_plan((int64_t)B * R, L_max).bytes;
+}
+
 int kvc_topk_select(const float* scores, const int32_t* seq_lens, const int32_t* pool,
                     int P, int pool_block, int32_t* idx_out, int B, int R, int L_max,
-                    int K, void* stream) {
+                    int K, void* workspace, size_t ws_bytes, void* stream) {
   if (B < 0 || R < 1 || L_max < 1 || K < 1) return KVC_ERR_BAD_SHAPE;
   // rows are read through 32-bit byte offsets (with a step of slack)
   if (L_max >= kSelectMaxRow) return KVC_ERR_UNSUPPORTED;
@@ -625,8 +630,24 @@ int kvc_topk_select(const float* scores, const int32_t* seq_lens, const int32_t*
       (pool && !aligned(pool, 4)))
     return KVC_ERR_MISALIGNED;
   if (B == 0) return KVC_OK;
-  SelectParams p{scores, seq_lens, pool, idx_out, B, R, L_max, K, pool ? P : 0,
-                 pool ? pool_block : 1, words, select_map_words(L_max)};
+  SelectParams p{};
+  p.scores = scores; p.seq_lens = seq_lens; p.pool = pool; p.out = idx_out;
+  p.B = B; p.R = R; p.L_max = L_max; p.K = K; p.P = pool ? P : 0;
+  p.pool_block = pool ? pool_block : 1; p.pool_words = words;
+  p.sel_words = select_map_words(L_max);
+  p.S = 1;
+  // the segmented form: a workspace of at least the queried size, no pool
+  const SelectSegPlan sp = select_seg_plan((int64_t)B * R, L_max);
+  if (workspace && !pool && sp.bytes > 0) {
+    if (ws_bytes < sp.bytes) return KVC_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return KVC_ERR_MISALIGNED;
+    char* base = static_cast<char*>(workspace);
+    p.S = sp.S; p.seg_len = sp.seg_len;
+    p.ws_cnt = reinterpret_cast<int32_t*>(base + sp.cnt_off);
+    p.ws_info = reinterpret_cast<int32_t*>(base + sp.info_off);
+    p.ws_cand = reinterpret_cast<uint32_t*>(base + sp.cand_off);
+    p.ws_ccnt = reinterpret_cast<int32_t*>(base + sp.ccnt_off);
+  }
   return launch_status(launch_topk_select(p, static_cast<hipStream_t>(stream)));
 }
 

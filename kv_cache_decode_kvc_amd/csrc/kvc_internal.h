@@ -113,7 +113,31 @@ struct SelectParams {
   int32_t* out;             // [B, R, K]
   int B, R, L_max, K, P, pool_block, pool_words;
   int sel_words;            // > 0: one-bit-per-position selection map (L_max <= 2^18)
+  // Segmented form (S >= 2): each row cut into S segments of seg_len
+  // positions, spread over the compute units (workspace pointers below).
+  int S, seg_len;
+  int32_t* ws_cnt;          // [rows] arrival counters (returned to zero)
+  int32_t* ws_info;         // [rows] the row's sampled lower bound of its K-th largest key
+  uint32_t* ws_cand;        // [rows, S, 16 waves, kSelSegCapw, 2] (key, position)
+  int32_t* ws_ccnt;         // [rows, S, 16 waves] candidates per wave
 };
+
+// Segmented selection: with a workspace, no pool and rows of at most
+// kSelectMapMax positions, a row is cut into segments of whole
+// 16384-position steps so that about kSelSegTargetWgs workgroups share the
+// rows (one workgroup per row keeps only `rows` compute units busy).  Each
+// wave of a segment keeps up to kSelSegCapw candidates (keys at or above a
+// sampled lower bound of the row's threshold); a row with more, or whose
+// bound turns out too high, is finished by the one-workgroup algorithm.
+constexpr int kSelSegTargetWgs = 256;
+constexpr int kSelSegCapw = 128;
+constexpr int kSelSegWaves = 16;
+struct SelectSegPlan {
+  int S = 1, seg_len = 0;
+  size_t cnt_off = 0, info_off = 0, cand_off = 0, ccnt_off = 0;
+  size_t bytes = 0;         // 0: no segmented form
+};
+SelectSegPlan select_seg_plan(int64_t rows, int L_max);
 
 struct MlaParams {
   const void* q;

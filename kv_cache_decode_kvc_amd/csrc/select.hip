@@ -32,6 +32,26 @@
 // Every pass over the row prefetches the next 16384 scores while it works on
 // the current ones.  No sort, no global atomics: the result is
 // deterministic.
+//
+// Segmented form (a workspace given, no pool, rows of at most 2^18
+// positions): one workgroup per row leaves most compute units idle when
+// there are few rows, so each row is cut into segments of whole
+// 16384-position steps, about 512 workgroups in all, one kernel:
+//  - every workgroup of a row reads the same 1/32 sample of it (64
+//    positions of every 2048) and takes a lower bound of the row's K-th
+//    largest key that leaves, in expectation, about K + 4 standard
+//    deviations' worth of keys above it;
+//  - it writes the keys of its segment at or above the bound, with
+//    positions, to per-wave candidate lists (no atomics);
+//  - the last workgroup of the row to finish (a ticket) gathers all the
+//    candidates into LDS, finds the exact K-th largest among them (8-bit
+//    digits, one wave scanning each 256-bin histogram), breaks ties by
+//    position, marks the chosen positions in a map and writes them out in
+//    order.  A row whose lists overflowed, or whose bound left fewer than K
+//    keys above it, is finished by the one-workgroup algorithm above
+//    instead.
+// The chosen set is the same as the one-workgroup algorithm's (the
+// selection is defined uniquely), so the output is too.
 
 #include "kvc_device.h"
 #include "kvc_internal.h"
@@ -64,6 +84,28 @@ __device__ inline uint32_t score_key(float f) {
   return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 
+// hist[bin] += 1 for every lane with `on` (lanes that do not reach the
+// call do not count).  LDS atomics on one address are served one lane at a
+// time, and candidate lists often share a few leading digits: up to three
+// times, the lanes whose bin equals the first remaining lane's add their
+// count in one atomic; the lanes left after that add one each.
+__device__ inline void hist_add(uint32_t* hist, uint32_t bin, bool on) {
+  const int lane = threadIdx.x & 63;
+  bool left = on;
+#pragma unroll
+  for (int round = 0; round < 3; ++round) {
+    const uint64_t act = __ballot(left);
+    if (act == 0) return;
+    const int first = __ffsll((long long)act) - 1;
+    const uint32_t b0 = (uint32_t)__builtin_amdgcn_readlane((int)bin, first);
+    const bool same = left && bin == b0;
+    const uint64_t group = __ballot(same);
+    if (lane == first) atomicAdd(&hist[b0], (uint32_t)__popcll(group));
+    left = left && !same;
+  }
+  if (left) atomicAdd(&hist[bin], 1u);
+}
+
 struct SelLds {
   uint32_t hist[kBins];
   int wsum[kSelWaves];
@@ -74,16 +116,26 @@ struct SelLds {
   int pre[kSelUnroll][kSelWaves][2];   // write-out: (above, equal) counts per (step slice, wave)
 };
 
+// Inclusive scan over the 64 lanes of a wave with data-parallel-primitive
+// moves (vector ALU, no LDS round trips): prefix within each row of 16
+// lanes by shifts of 1, 2, 4, 8 (lanes whose source falls before the row
+// start add 0), then row 15's total into rows 1 and 3 and lane 31's into
+// rows 2 and 3.
+__device__ inline int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);   // row_bcast:15 -> rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);   // row_bcast:31 -> rows 2, 3
+  return v;
+}
+
 // Exclusive scan of one int per thread over the workgroup; returns the
 // exclusive prefix and sets `total`.  Uses wsum (wave totals).
 __device__ inline int block_exclusive_scan(int x, SelLds& L, int& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int v = x;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(v, o);
-    if (lane >= o) v += y;
-  }
+  const int v = wave_incl_scan(x);
   if (lane == 63) L.wsum[wave] = v;
   __syncthreads();
   int wprefix = 0, tot = 0;
@@ -126,9 +178,10 @@ __device__ inline int find_bin(SelLds& L, int r) {
 // which must cover every bit outside pmask.  Returns the value; gt and eq
 // count the matching entries above it and equal to it.
 template <int NP, typename Each>
-__device__ uint32_t list_select(Each each, int r, uint32_t prefix, uint32_t pmask,
-                                const int (&sh)[NP], const uint32_t (&dm)[NP], SelLds& L,
-                                int& gt, int& eq) {
+__device__ __forceinline__ uint32_t list_select(Each each, int r, uint32_t prefix,
+                                                uint32_t pmask, const int (&sh)[NP],
+                                                const uint32_t (&dm)[NP], SelLds& L, int& gt,
+                                                int& eq) {
   gt = 0;
   eq = 0;
 #pragma unroll
@@ -184,19 +237,40 @@ __device__ inline void stream_row(__amdgpu_buffer_rsrc_t sr, int n, F&& f) {
   }
 }
 
-}  // namespace
+// Ordered write-out from a one-bit-per-position map of the row's first n
+// positions: thread t takes consecutive words, one scan gives its offset;
+// slots past the kept count are -1.
+__device__ inline void write_out_map(const uint32_t* sel, int n, int32_t* out, int K,
+                                     SelLds& L) {
+  const int tid = threadIdx.x;
+  const int W = (n + 31) >> 5;
+  const int wpt = (W + kSelThreads - 1) / kSelThreads;
+  const int w0 = tid * wpt;
+  int cnt = 0;
+  for (int w = w0; w < w0 + wpt && w < W; ++w) cnt += __popc(sel[w]);
+  int kept = 0;
+  int off = block_exclusive_scan(cnt, L, kept);
+  for (int w = w0; w < w0 + wpt && w < W; ++w) {
+    uint32_t bits = sel[w];
+    while (bits) {
+      out[off++] = w * 32 + __builtin_ctz(bits);
+      bits &= bits - 1u;
+    }
+  }
+  for (int i = kept + tid; i < K; i += kSelThreads) out[i] = -1;
+}
 
-__global__ __launch_bounds__(kSelThreads) void topk_select_kernel(SelectParams p) {
-  __shared__ SelLds L;
+// The one-workgroup algorithm for one row (dyn: the dynamic LDS of
+// launch_topk_select's one-workgroup kernel).
+__device__ __forceinline__ void select_row(const SelectParams& p, const int row, SelLds& L,
+                                           uint32_t* dyn) {
   // dynamic LDS: kHistCopies histograms (later the candidate list), the
   // selection map (sel_words), then (pool mode) one bit per block
-  extern __shared__ uint32_t dyn[];
   uint32_t* hcopy = dyn;
   uint32_t* ckey = dyn;
   uint32_t* cpos = dyn + kSelCand;
   uint32_t* sel = dyn + kHistCopies * kBins;
   uint32_t* pool_bits = sel + p.sel_words;
-  const int row = blockIdx.x;
   const int b = row / p.R;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -386,22 +460,8 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(SelectParams p
         }
         __syncthreads();
       }
-      // ordered write-out from the map: thread t takes consecutive words
-      const int W = (n + 31) >> 5;
-      const int wpt = (W + kSelThreads - 1) / kSelThreads;
-      const int w0 = tid * wpt;
-      int cnt = 0;
-      for (int w = w0; w < w0 + wpt && w < W; ++w) cnt += __popc(sel[w]);
-      int kept = 0;
-      int off = block_exclusive_scan(cnt, L, kept);
-      for (int w = w0; w < w0 + wpt && w < W; ++w) {
-        uint32_t bits = sel[w];
-        while (bits) {
-          out[off++] = w * 32 + __builtin_ctz(bits);
-          bits &= bits - 1u;
-        }
-      }
-      for (int i = kept + tid; i < p.K; i += kSelThreads) out[i] = -1;
+      // ordered write-out from the map
+      write_out_map(sel, n, out, p.K, L);
       return;
     }
     // the list overflowed: the list area is the histograms again below
@@ -471,19 +531,399 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(SelectParams p
   for (int i = kept + tid; i < p.K; i += kSelThreads) out[i] = -1;
 }
 
+__global__ __launch_bounds__(kSelThreads) void topk_select_kernel(SelectParams p) {
+  __shared__ SelLds L;
+  extern __shared__ __attribute__((aligned(16))) uint32_t dyn[];
+  select_row(p, blockIdx.x, L, dyn);
+}
+
+// ---------------------------------------------------------------- segmented
+// Segment `seg` of row `row`: positions [s0, s0 + sn) of the row (sn may be
+// 0 past the row's length).
+struct SegPos {
+  int row, seg, b, n, s0, sn;
+};
+
+__device__ inline SegPos seg_pos(const SelectParams& p) {
+  SegPos q;
+  q.row = blockIdx.x / p.S;
+  q.seg = blockIdx.x - q.row * p.S;
+  q.b = q.row / p.R;
+  q.n = min(max(p.seq_lens[q.b], 0), p.L_max);
+  q.s0 = q.seg * p.seg_len;
+  q.sn = min(max(q.n - q.s0, 0), p.seg_len);
+  return q;
+}
+
+// Sampled positions: 64 consecutive positions at the start of every
+// 2048-position block of the row (1/32 of it, spread over the whole row).
+constexpr int kSampleRun = 64;
+constexpr int kSampleEvery = 2048;
+// (key, position) pairs the finishing workgroup holds in LDS
+constexpr int kFinCand = kHistCopies * kBins / 2;
+constexpr int kFinPer = kFinCand / kSelThreads;
+
+// r-th largest digit of a 2048-bin histogram h (16-byte aligned): wave 0
+// scans the bins from the top, 32 per lane (eight 16-byte reads), one wave
+// prefix sum, then the lane holding the r-th entry walks its 32 bins; the
+// digit and the counts above it and in it go to L.found_*; one barrier.
+// Valid when r <= the histogram's total.
+__device__ inline void find_bin_wave(const uint32_t* h, SelLds& L, int r) {
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const int lo = kBins - 32 * (lane + 1);        // this lane's bins lo .. lo + 31
+    int qs[8], sum = 0;                            // sums of its eight groups of four
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const u32x4 c = *reinterpret_cast<const u32x4*>(h + lo + 4 * i);
+      qs[i] = (int)(c[0] + c[1] + c[2] + c[3]);
+      sum += qs[i];
+    }
+    const int incl = wave_incl_scan(sum);
+    int above = incl - sum;
+    if (above < r && r <= incl) {
+      int g = 0;                                   // the group holding the r-th entry, from the top
+#pragma unroll
+      for (int i = 7; i >= 0; --i) {
+        if (g == 0 && r <= above + qs[i]) g = i + 1;
+        else if (g == 0) above += qs[i];
+      }
+      const u32x4 c = *reinterpret_cast<const u32x4*>(h + lo + 4 * (g - 1));
+#pragma unroll
+      for (int j = 3; j >= 0; --j) {
+        const int cnt = (int)c[j];
+        if (above < r && r <= above + cnt) {
+          L.found_digit = lo + 4 * (g - 1) + j;
+          L.found_above = above;
+          L.found_count = cnt;
+        }
+        above += cnt;
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// r-th largest of the values get(i) (i < kFinPer; counted where ok(i))
+// matching prefix under pmask, refined digit by digit at the shifts sh and
+// masks dm (which must cover every bit outside pmask; digits below 2048).
+// Two 2048-bin histograms h0, h1 alternate: each pass counts into one while
+// the other is cleared for the next; the caller clears h0 (with a barrier
+// after).  Two barriers per pass.  Returns the value; gt and eq count the
+// matching values above it and equal to it.
+template <int NP, typename Get, typename Ok>
+__device__ __forceinline__ uint32_t reg_select(Get get, Ok ok, int r, uint32_t prefix,
+                                               uint32_t pmask, const int (&sh)[NP],
+                                               const uint32_t (&dm)[NP], uint32_t* h0,
+                                               uint32_t* h1, SelLds& L, int& gt, int& eq) {
+  gt = 0;
+  eq = 0;
+#pragma unroll
+  for (int pass = 0; pass < NP; ++pass) {
+    uint32_t* h = (pass & 1) ? h1 : h0;
+    uint32_t* hn = (pass & 1) ? h0 : h1;
+#pragma unroll
+    for (int i = 0; i < kFinPer; ++i) {
+      const uint32_t x = get(i);
+      hist_add(h, (x >> sh[pass]) & dm[pass], ok(i) && (x & pmask) == prefix);
+    }
+    if (pass + 1 < NP)
+      for (int i = threadIdx.x; i < kBins; i += kSelThreads) hn[i] = 0u;
+    __syncthreads();
+    find_bin_wave(h, L, r);
+    const uint32_t d = (uint32_t)L.found_digit;
+    const int a = L.found_above, c = L.found_count;
+    r -= a;
+    gt += a;
+    eq = c;
+    prefix |= d << sh[pass];
+    pmask |= dm[pass] << sh[pass];
+  }
+  return prefix;
+}
+
+// The row's sample as each lane loads it: block c = wave + 16 u (u < 8) of
+// the row, position 2048 c + lane (rows of at most 2^18 positions have at
+// most 128 blocks).  Loads past the row read zeros.
+constexpr int kSampleLoads = kSelectMapMax / kSampleEvery / kSelWaves;
+
+__device__ inline void sample_load(const SelectParams& p, int row, int n,
+                                   uint32_t (&v)[kSampleLoads]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const __amdgpu_buffer_rsrc_t sr = make_rsrc(p.scores + (size_t)row * p.L_max, (uint32_t)n * 4u);
+#pragma unroll
+  for (int u = 0; u < kSampleLoads; ++u)
+    v[u] = __builtin_amdgcn_raw_buffer_load_b32(
+        sr, (uint32_t)(((wave + u * kSelWaves) * kSampleEvery + lane) * 4), 0, 0);
+}
+
+// Lower bound of the row's K-th largest key from its sample (every
+// workgroup of the row computes the same one): the lower edge of the
+// top-digit bin holding the sample's r-th largest key, r = K / 32 plus four
+// standard deviations of a binomial count of that size, so that in
+// expectation comfortably more than K keys of the row lie at or above it,
+// but not many more.  0 when the sample has fewer than r keys (every valid
+// key is then a candidate).  Whether the bound really leaves K keys above it
+// is checked once the candidates are counted.
+__device__ inline uint32_t row_bound(const SelectParams& p, int n, const uint32_t (&v)[kSampleLoads],
+                                     SelLds& L) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid; i < kBins; i += kSelThreads) L.hist[i] = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < kSampleLoads; ++u) {
+    const int t = (wave + u * kSelWaves) * kSampleEvery + lane;
+    hist_add(L.hist, score_key(__uint_as_float(v[u])) >> 21, t < n);
+  }
+  __syncthreads();
+  const float mean = (float)p.K / (float)(kSampleEvery / kSampleRun);
+  const int r = (int)ceilf(mean + 4.f * sqrtf(mean)) + 1;
+  const int total = find_bin(L, r);
+  const uint32_t lb = total >= r ? ((uint32_t)L.found_digit << 21) : 0u;
+  __syncthreads();
+  return lb;
+}
+
+// One workgroup per row: the row's bound from its sample (to ws_info).
+__global__ __launch_bounds__(kSelThreads) void seg_bound_kernel(SelectParams p) {
+  __shared__ SelLds L;
+  const int row = blockIdx.x;
+  const int n = min(max(p.seq_lens[row / p.R], 0), p.L_max);
+  uint32_t smp[kSampleLoads];
+  sample_load(p, row, n, smp);
+  const uint32_t lb = row_bound(p, n, smp, L);
+  if (threadIdx.x == 0) p.ws_info[row] = (int32_t)lb;
+}
+
+// The workgroup of (row, segment): the row's bound, then every valid key of
+// the segment at or above it, with its position, into this wave's candidate
+// list (collected in LDS, then written out whole with device-coherent
+// stores; no atomics).  The last of the row's workgroups to finish (a
+// device-scope ticket) selects among all of them.
+__global__ __launch_bounds__(kSelThreads) void seg_select_kernel(SelectParams p) {
+  __shared__ SelLds L;
+  __shared__ int s_last;
+  __shared__ int s_off[kSelSegWaves * 32 + 1];   // list offsets per (segment, wave); S <= 32
+  extern __shared__ __attribute__((aligned(16))) uint32_t dyn[];
+  const SegPos q = seg_pos(p);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  // the segment's first two steps in flight, then the row's bound (from
+  // seg_bound_kernel)
+  const __amdgpu_buffer_rsrc_t sr =
+      make_rsrc(p.scores + (size_t)q.row * p.L_max + q.s0, (uint32_t)q.sn * 4u);
+  constexpr int kQ = kSelUnroll / 4;       // 16-byte loads per lane and step
+  u32x4 st0[kQ], st1[kQ];
+  auto load_step = [&](u32x4 (&v)[kQ], int base) {
+#pragma unroll
+    for (int i = 0; i < kQ; ++i)
+      v[i] = __builtin_amdgcn_raw_buffer_load_b128(sr, tid * 16u,
+                                                   (uint32_t)(base + i * kSelThreads * 4) * 4u, 0);
+  };
+  load_step(st0, 0);
+  load_step(st1, kSelStep);
+  const uint32_t lb = (uint32_t)p.ws_info[q.row];
+
+  const __amdgpu_buffer_rsrc_t wc_r = make_rsrc(p.ws_cand, kWsRecords);
+  const __amdgpu_buffer_rsrc_t wn_r = make_rsrc(p.ws_ccnt, kWsRecords);
+  const int nreg = p.S * kSelSegWaves;
+  const uint32_t row_cand = (uint32_t)((size_t)q.row * nreg * kSelSegCapw * 8);
+  {
+    const int region = q.seg * kSelSegWaves + wave;       // within the row
+    const uint32_t cbase = row_cand + (uint32_t)(region * kSelSegCapw * 8);
+    u32x2* stage = reinterpret_cast<u32x2*>(dyn) + wave * kSelSegCapw;   // this wave's list
+    int wc = 0;
+    // key >= lb as a float compare (one instruction per position; the key
+    // is formed only for the candidates): lb's score, or -inf when every
+    // score qualifies
+    float lbf = -__builtin_huge_valf();
+    if (lb & 0x80000000u) lbf = __uint_as_float(lb & 0x7FFFFFFFu);          // >= +0
+    else if (lb != 0u && ((~lb >> 23) & 0xFFu) != 0xFFu) lbf = __uint_as_float(~lb);
+    // v[i][j]: position base + 4 (i * kSelThreads + tid) + j of the segment
+    auto process = [&](const u32x4 (&v)[kQ], int base) {
+      const bool whole = base + kSelStep <= q.sn;
+#pragma unroll
+      for (int i = 0; i < kQ; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int t = base + 4 * (i * kSelThreads + tid) + j;
+          const float f = __uint_as_float(v[i][j]);
+          const bool c = f >= lbf && (whole || t < q.sn);
+          const uint64_t bc = __ballot(c);
+          if (c) {
+            const int slot = wc + __popcll(bc & below);
+            if (slot < kSelSegCapw) stage[slot] = u32x2{score_key(f), (uint32_t)(q.s0 + t)};
+          }
+          wc += __popcll(bc);
+        }
+    };
+    process(st0, 0);
+    if (q.sn > kSelStep) process(st1, kSelStep);
+    // longer segments: the remaining steps, each loaded while the previous
+    // one is processed
+    for (int base = 2 * kSelStep; base < q.sn; base += 2 * kSelStep) {
+      load_step(st0, base);
+      load_step(st1, base + kSelStep);
+      process(st0, base);
+      if (base + kSelStep < q.sn) process(st1, base + kSelStep);
+    }
+    // (the wave's own LDS writes are complete for its own reads below)
+    const int kept = wc < kSelSegCapw ? wc : kSelSegCapw;
+    for (int i = lane; i < kept; i += 64)
+      __builtin_amdgcn_raw_buffer_store_b64(stage[i], wc_r, cbase + (uint32_t)(i * 8), 0,
+                                            kCoherent);
+    if (lane == 0)
+      __builtin_amdgcn_raw_buffer_store_b32((uint32_t)wc, wn_r,
+                                            (uint32_t)(((size_t)q.row * nreg + region) * 4), 0,
+                                            kCoherent);
+  }
+  wait_vm_all();
+  __syncthreads();
+  if (tid == 0) s_last = atomicAdd(&p.ws_cnt[q.row], 1) == p.S - 1;
+  __syncthreads();
+  if (!s_last) return;
+
+  // ---- the row's last workgroup: select among all the candidates
+  if (tid == 0) p.ws_cnt[q.row] = 0;
+  const int n = q.n;
+  const int c = tid < nreg ? (int)__builtin_amdgcn_raw_buffer_load_b32(
+                                 wn_r, (uint32_t)(((size_t)q.row * nreg + tid) * 4), 0, kCoherent)
+                           : 0;
+  const int over = __syncthreads_or(c > kSelSegCapw);
+  int total = 0;
+  const int off = block_exclusive_scan(c, L, total);
+  // every valid key was collected when the bound is 0
+  const bool all = lb == 0u && total <= p.K;
+  if (over || total > kFinCand || (total < p.K && lb != 0u)) {
+    // a list overflowed, too many candidates for the LDS, or the bound left
+    // fewer than K keys above it: the one-workgroup algorithm
+    select_row(p, q.row, L, dyn);
+    return;
+  }
+  if (tid < nreg) s_off[tid] = off;
+  if (tid == 0) s_off[nreg] = total;
+  uint32_t* ck = dyn;
+  uint32_t* cp = dyn + kFinCand;
+  uint32_t* sel = dyn + kHistCopies * kBins;
+  const int W = (n + 31) >> 5;
+  for (int w = tid; w < W; w += kSelThreads) sel[w] = 0u;
+  __syncthreads();
+  // gather: wave w copies lists w, w + 16, ... (at most kSelSegCapw entries
+  // each: two per lane), all of its loads in flight together; list r's
+  // entries go to s_off[r] onwards
+  {
+    for (int r0 = wave; r0 < nreg; r0 += kSelWaves * 4) {
+      u32x2 v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int r = r0 + (j >> 1) * kSelWaves, i = lane + (j & 1) * 64;
+        const bool ok = r < nreg && i < s_off[min(r + 1, nreg)] - s_off[min(r, nreg)];
+        // (slots past a list's count load its first slot, unused)
+        v[j] = __builtin_amdgcn_raw_buffer_load_b64(
+            wc_r, row_cand + (uint32_t)(((ok ? r : 0) * kSelSegCapw + (ok ? i : 0)) * 8), 0,
+            kCoherent);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int r = r0 + (j >> 1) * kSelWaves, i = lane + (j & 1) * 64;
+        if (r < nreg && i < s_off[r + 1] - s_off[r]) {
+          ck[s_off[r] + i] = v[j][0];
+          cp[s_off[r] + i] = v[j][1];
+        }
+      }
+    }
+  }
+  __syncthreads();
+  // each thread's candidates in registers: entries tid + i * kSelThreads
+  uint32_t rk[kFinPer], rp[kFinPer];
+#pragma unroll
+  for (int i = 0; i < kFinPer; ++i) {
+    const int e = tid + i * kSelThreads;
+    rk[i] = e < total ? ck[e] : 0u;
+    rp[i] = e < total ? cp[e] : 0u;
+  }
+  auto valid = [&](int i) { return tid + i * kSelThreads < total; };
+  // (the candidate area is free again: two histograms there)
+  uint32_t* h0 = dyn;
+  uint32_t* h1 = dyn + kBins;
+  __syncthreads();
+  for (int i = tid; i < kBins; i += kSelThreads) h0[i] = 0u;
+  __syncthreads();
+  uint32_t thr = 0u, pthr = 0u;
+  if (!all) {
+    int gt, eq;
+    const int shk[3] = {21, 10, 0};
+    const uint32_t dmk[3] = {0x7FFu, 0x7FFu, 0x3FFu};
+    thr = reg_select<3>([&](int i) { return rk[i]; }, valid, p.K, 0u, 0u, shk, dmk, h0, h1, L,
+                        gt, eq);
+    const int take = p.K - gt;
+    if (take < eq) {
+      // equal keys: the lowest positions (largest ~position; positions are
+      // below 2^18, so ~position starts with 14 one bits)
+      for (int i = tid; i < kBins; i += kSelThreads) h0[i] = 0u;
+      __syncthreads();
+      int g2, e2;
+      const int shp[2] = {7, 0};
+      const uint32_t dmp[2] = {0x7FFu, 0x7Fu};
+      pthr = reg_select<2>([&](int i) { return rk[i] == thr ? ~rp[i] : 0u; }, valid, take,
+                           0xFFFC0000u, 0xFFFC0000u, shp, dmp, h0, h1, L, g2, e2);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kFinPer; ++i)
+    if (valid(i) && (all || rk[i] > thr || (rk[i] == thr && ~rp[i] >= pthr)))
+      atomicOr(&sel[rp[i] >> 5], 1u << (rp[i] & 31));
+  __syncthreads();
+  write_out_map(sel, n, p.out + (size_t)q.row * p.K, p.K, L);
+}
+
+}  // namespace
+
+SelectSegPlan select_seg_plan(int64_t rows, int L_max) {
+  SelectSegPlan sp;
+  if (rows < 1 || L_max > kSelectMapMax) return sp;
+  const int64_t steps = (L_max + kSelStep - 1) / kSelStep;
+  int64_t want = (kSelSegTargetWgs + rows - 1) / rows;
+  if (want > steps) want = steps;
+  if (want > 32) want = 32;
+  if (want < 2) return sp;
+  const int64_t seg_steps = (steps + want - 1) / want;
+  sp.seg_len = (int)(seg_steps * kSelStep);
+  sp.S = (int)((L_max + sp.seg_len - 1) / sp.seg_len);
+  if (sp.S < 2) { sp = SelectSegPlan{}; return sp; }
+  size_t off = 0;
+  auto take = [&](size_t bytes) { const size_t o = off; off += round_up(bytes, 256); return o; };
+  sp.cnt_off = take((size_t)rows * 4);          // arrival counters (zeroed once, kept zero)
+  sp.info_off = take((size_t)rows * 4);
+  sp.cand_off = take((size_t)rows * sp.S * kSelSegWaves * kSelSegCapw * 8);
+  sp.ccnt_off = take((size_t)rows * sp.S * kSelSegWaves * 4);
+  sp.bytes = off;
+  return sp;
+}
+
 hipError_t launch_topk_select(const SelectParams& p, hipStream_t s) {
   const size_t dyn = ((size_t)kHistCopies * kBins + p.sel_words +
                       (p.pool ? (size_t)p.pool_words : 0)) * 4;
   static bool attr_set = false;
   if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute(
-        (const void*)topk_select_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-        (int)((kHistCopies * kBins + kSelectMapMax / 32 + kSelectPoolWords) * 4));
+    const int most = (int)((kHistCopies * kBins + kSelectMapMax / 32 + kSelectPoolWords) * 4);
+    hipError_t e = hipFuncSetAttribute((const void*)topk_select_kernel,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, most);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute((const void*)seg_select_kernel,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, most);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL(topk_select_kernel, dim3((unsigned)((size_t)p.B * p.R)), dim3(kSelThreads),
-                     dyn, s, p);
+  const unsigned rows = (unsigned)((size_t)p.B * p.R);
+  if (p.S >= 2) {
+    const unsigned segs = rows * (unsigned)p.S;
+    hipLaunchKernelGGL(seg_bound_kernel, dim3(rows), dim3(kSelThreads), 0, s, p);
+    hipLaunchKernelGGL(seg_select_kernel, dim3(segs), dim3(kSelThreads), dyn, s, p);
+  } else {
+    hipLaunchKernelGGL(topk_select_kernel, dim3(rows), dim3(kSelThreads), dyn, s, p);
+  }
   return hipGetLastError();
 }
 

@@ -326,10 +326,19 @@ def test_paged_validation(L):
 def test_select_validation(L):
     def sel(**kw):
         a = dict(s=A4, sl=A4, pool=NULL, P=0, pb=8, out=A4, B=2, R=8, L=131072, K=2048,
-                 stream=NULL)
+                 ws=NULL, wn=0, stream=NULL)
         a.update(kw)
         return L.kvc_topk_select(a["s"], a["sl"], a["pool"], a["P"], a["pb"], a["out"], a["B"],
-                                 a["R"], a["L"], a["K"], a["stream"])
+                                 a["R"], a["L"], a["K"], a["ws"], a["wn"], a["stream"])
+    need = L.kvc_topk_select_workspace_size(2, 8, 131072, 2048)
+    assert need > 0
+    assert sel(ws=A16, wn=need - 1) == -5                  # workspace too small
+    assert sel(ws=ctypes.c_void_p(0x10010), wn=need) == -6  # workspace not 256-byte aligned
+    # the one-workgroup form needs none: long rows, a device-filling row count
+    assert L.kvc_topk_select_workspace_size(2, 8, (1 << 18) + 1, 2048) == 0
+    assert L.kvc_topk_select_workspace_size(64, 8, 131072, 2048) == 0
+    assert L.kvc_topk_select_workspace_size(4, 4, 16384, 100) == 0    # one step per row
+    assert L.kvc_topk_select_workspace_size(0, 8, 131072, 2048) == 0
     assert sel(s=NULL) == -1
     assert sel(out=NULL) == -1
     assert sel(K=0) == -2

@@ -31,13 +31,56 @@ def _gpu_only():
     torch.cuda.synchronize()
 
 
-def run_select(scores, lens, K, pool=None, pool_block=8):
+def run_select(scores, lens, K, pool=None, pool_block=8, ws=False):
+    """ws: pass a workspace (the segmented form where the shape has one)."""
     B, R, L = scores.shape
     out = torch.full((B, R, K), 12345, dtype=torch.int32, device="cuda")
+    w = kvc.workspace(kvc.kvc_topk_select_workspace_size(B, R, L, K)) if ws else None
     kvc.kvc_topk_select(dev(scores), dev(np.asarray(lens, np.int32)), out,
-                        pool=None if pool is None else dev(pool), pool_block=pool_block)
+                        pool=None if pool is None else dev(pool), pool_block=pool_block,
+                        workspace=w)
     torch.cuda.synchronize()
     return host(out)
+
+
+# Rows of several 16384-position steps take the segmented form when a
+# workspace is given: both forms against the oracle.
+SEG_CASES = [
+    # (kind, R, L, lens, K)
+    ("normal", 4, 70000, [70000, 33000], 2048),
+    ("normal", 2, 40000, [16384, 16385, 0, 32769], 700),   # segment edges, an empty row
+    ("coarse", 4, 50000, [50000, 49999], 2048),            # many equal keys at the threshold
+    ("ties", 4, 50000, [50000, 20000], 2048),              # lists overflow: whole-row fallback
+    ("zeros", 4, 40000, [40000], 500),                     # -0 and +0 equal
+    ("few", 2, 50000, [1500, 2048, 2049], 2048),           # fewer than, exactly, one more than K
+    ("normal", 1, 262144, [262144], 4096),                 # the longest row of the form
+    ("lastmax", 2, 40000, [32769, 32770, 32771, 39999], 300),   # top scores in the row's last 3
+]
+
+
+@pytest.mark.parametrize("kind,R,L,lens,K", SEG_CASES)
+@pytest.mark.parametrize("ws", [False, True])
+def test_select_segmented_matches_oracle(kind, R, L, lens, K, ws):
+    rng = np.random.default_rng(sum(map(ord, kind)) * 7919 + R * 131 + L + K)
+    B = len(lens)
+    sc = rng.standard_normal((B, R, L)).astype(np.float32)
+    if kind == "coarse":
+        sc = (np.round(sc * 64) / 64).astype(np.float32)
+    elif kind == "ties":
+        sc = rng.integers(0, 4, size=(B, R, L)).astype(np.float32)
+    elif kind == "zeros":
+        sc = np.where(rng.random((B, R, L)) < 0.5, np.float32(0.0), np.float32(-0.0)).astype(np.float32)
+        sc[:, :, ::9] = 1.0
+    elif kind == "lastmax":
+        # the highest scores sit in the last positions of each row (lengths
+        # not multiples of 4: a 16-byte load straddles the end)
+        for b, n in enumerate(lens):
+            sc[b, :, n - 3:n] = np.float32(50.0) + np.arange(3, dtype=np.float32)
+    if ws:
+        assert kvc.kvc_topk_select_workspace_size(B, R, L, K) > 0
+    got = run_select(sc, lens, K, ws=ws)
+    want = oracle.topk_select(sc, np.asarray(lens), K)
+    assert np.array_equal(got, want), np.argwhere(got != want)[:5]
 
 
 @pytest.mark.parametrize("kind", ["normal", "ties", "zeros", "short"])
@@ -150,8 +193,10 @@ def test_select_pool_variant():
     assert np.array_equal(got, want)
 
 
-def test_select_fullsize_sampled_rows():
-    """The sparse workload's shape: 8 sequences x 8 KV heads, 2048 of 131072."""
+@pytest.mark.parametrize("ws", [False, True])
+def test_select_fullsize_sampled_rows(ws):
+    """The sparse workload's shape: 8 sequences x 8 KV heads, 2048 of 131072
+    (with a workspace: the segmented form, as timed)."""
     c = syn.C5
     B, R, L, K = c.B, c.n_kv, c.pre_len, c.K
     g = torch.Generator(device="cuda")
@@ -161,7 +206,10 @@ def test_select_fullsize_sampled_rows():
     lens = torch.full((B,), L, dtype=torch.int32, device="cuda")
     units = [(0, 0), (3, 5), (7, 7)]
     rows = {u: host(scores[u[0]:u[0] + 1, u[1]:u[1] + 1]) for u in units}   # before the call
-    kvc.kvc_topk_select(scores, lens, out)
+    w = kvc.workspace(kvc.kvc_topk_select_workspace_size(B, R, L, K)) if ws else None
+    if ws:
+        assert w is not None
+    kvc.kvc_topk_select(scores, lens, out, workspace=w)
     torch.cuda.synchronize()
     got = host(out)
     for b, j in units:
