@@ -150,6 +150,8 @@ class DenseWorkload(Workload):
     def kernel(self):
         c = self.cfg
         if c.dtype == syn.BF16 and c.d == 128:
+            if c.B * c.n_kv >= 64:   # the long GQA layer: the persistent form
+                return "dense_persist_kernel<true, false, false, false> (append + attend)"
             return "dense_mfma_kernel<false, true, false, false, false> (append + attend)"
         return "dense_generic_kernel<float, %d, false, true> (append + attend)" % c.d
 
@@ -384,7 +386,7 @@ class Fp8DenseWorkload(DenseWorkload):
     one float32 scale per tensor).  A layer-step is kvc_append_fp8 then
     kvc_decode_attn_fp8."""
 
-    kernel = "dense_mfma_kernel<false, false, true, false, false> (fp8 E4M3 cache)"
+    kernel = "dense_persist_kernel<false, true, false, false> (fp8 E4M3 cache)"
     kernel_appends = False
     K_SCALE = 1.0 / 64      # N(0,1) / (1/64) stays within +-448
     V_SCALE = 1.0 / 64
@@ -486,7 +488,7 @@ class Fp4DenseWorkload(DenseWorkload):
     [B, n_kv, L_max, d/16]).  A layer-step is kvc_append_fp4 then
     kvc_decode_attn_fp4."""
 
-    kernel = "dense_mfma_kernel<false, false, false, false, true> (fp4 E2M1 cache)"
+    kernel = "dense_persist_kernel<false, false, false, true> (fp4 E2M1 cache)"
     kernel_appends = False
 
     def __init__(self, cfg, slack, torch, kvc):
@@ -669,7 +671,7 @@ class PagedWorkload(DenseWorkload):
     block table per layer buffer.  A layer-step is kvc_append_paged then
     kvc_decode_attn_paged."""
 
-    kernel = "dense_mfma_kernel<false, false, false, true, false> (paged, 16-position blocks)"
+    kernel = "dense_persist_kernel<false, false, true, false> (paged, 16-position blocks)"
     kernel_appends = False
     unit_name = "sequences (all KV heads)"
     BETA = 16
@@ -773,7 +775,7 @@ class SelectWorkload(Workload):
     head, the 2048 highest of 131072 indexer scores (float32, seeded N(0,1)),
     32 index sets over 16 distinct score buffers (512 MB)."""
 
-    kernel = "seg_select_kernel"
+    kernel = "seg_bound_kernel + seg_select_kernel"
     unit_name = "score rows"
     NBUF = 16
 

@@ -27,15 +27,16 @@ COPY_BYTES = 1 << 30
 
 # dominant kernel of each bench workload (substring of the demangled name)
 DOMINANT = {
+    "C1": "dense_generic_kernel<float, 64, false, true>",
     "C2": "dense_mfma_kernel<false, true, false, false, false>",
-    "C3": "dense_mfma_kernel<false, true, false, false, false>",
+    "C3": "dense_persist_kernel<true, false, false, false>",
     "C4": "mla_kernel",
     "C5": "dense_mfma_kernel<true, false, false, false, false>",
-    "C3F8": "dense_mfma_kernel<false, false, true, false, false>",
-    "C3F4": "dense_mfma_kernel<false, false, false, false, true>",
+    "C3F8": "dense_persist_kernel<false, true, false, false>",
+    "C3F4": "dense_persist_kernel<false, false, false, true>",
     "C3W128": "dense_mfma_kernel<false, false, false, false, false>",
-    "C3P16": "dense_mfma_kernel<false, false, false, true, false>",
-    "C5S": "topk_select_kernel",
+    "C3P16": "dense_persist_kernel<false, false, true, false>",
+    "C5S": "seg_select_kernel",
 }
 
 
@@ -62,7 +63,18 @@ def source_hash(workload: str) -> str:
 
 
 def _short(name: str) -> str:
-    return name.replace("void ", "").split("(")[0]
+    """Demangled name without "void " and the argument list (the
+    parenthesised group that ends the name; "(anonymous namespace)" and
+    parentheses inside the arguments are kept out of the way)."""
+    name = name.replace("void ", "").strip()
+    if name.endswith(")"):
+        depth = 0
+        for i in range(len(name) - 1, -1, -1):
+            depth += name[i] == ")"
+            depth -= name[i] == "("
+            if depth == 0:
+                return name[:i]
+    return name
 
 
 def _counters(path: str):
