@@ -50,7 +50,11 @@
  *    _size call returns (0 means none).  It must be zero-filled before its
  *    first use; every call returns the counters it holds to zero (the rest is
  *    scratch that each call writes before reading), so a workspace is reused
- *    without clearing.  Calls that may run at the same time need separate
+ *    without clearing by calls with the same shape arguments (and the same
+ *    split override).  Where the counters sit depends on those arguments:
+ *    before a call with other ones, zero-fill the workspace again (a stale
+ *    counter gives wrong results for that call, not an access outside the
+ *    buffers).  Calls that may run at the same time need separate
  *    workspaces.
  */
 #ifndef KVC_H

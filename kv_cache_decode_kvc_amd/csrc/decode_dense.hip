@@ -1038,7 +1038,10 @@ __global__ __launch_bounds__(256, 2) void dense_persist_kernel(DenseParams p) {
   ChunkIdx I0, I1;    // (top-k only; unused here)
   int k = blockIdx.x;
   const NextItem nx{p.ws_sched, (int)gridDim.x, &s_next};
-  while (k < total) {
+  // (an unsigned test: a counter left non-zero by a workspace that was not
+  // zero-filled for this call's layout gives wrong results, never an item
+  // index outside the list)
+  while ((unsigned)k < (unsigned)total) {
     int u, split;
     if (k < total_full) {
       u = last_at_or_below(s_full, units, k);

@@ -201,12 +201,27 @@ __device__ __forceinline__ void pv_head(std::integer_sequence<int, Js...>, u32x2
   (pv_issue<Js>(lo, hi, tb), ...);
 }
 
-template <int... Js>
+// Value MFMA J, then (J = 0, 2, .., 10) piece J / 2 of the softmax's
+// remaining vector work, which issues while the matrix unit is busy.
+template <int J, class F>
+__device__ __forceinline__ void pv_step_w(f32x16 (&acc)[kColTiles], const bf16x8 (&pop)[2],
+                                          u32x2 (&lo)[kPvBuf], u32x2 (&hi)[kPvBuf],
+                                          const uint32_t (&tb)[2][2], F&& w) {
+  pv_step<J>(acc, pop, lo, hi, tb);
+  if constexpr (J <= 10 && J % 2 == 0) {
+    w(J / 2);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// (pieces 1..4 complete pop[1] before MFMA kColTiles, the first to read it)
+template <int... Js, class F>
 __device__ __forceinline__ void pv_all(std::integer_sequence<int, Js...>,
                                        f32x16 (&acc)[kColTiles], const bf16x8 (&pop)[2],
                                        u32x2 (&lo)[kPvBuf], u32x2 (&hi)[kPvBuf],
-                                       const uint32_t (&tb)[2][2]) {
-  (pv_step<Js>(acc, pop, lo, hi, tb), ...);
+                                       const uint32_t (&tb)[2][2], F&& w) {
+  static_assert(kColTiles > 10, "pop[1] is complete before its first reader");
+  (pv_step_w<Js>(acc, pop, lo, hi, tb, w), ...);
 }
 
 }  // namespace
@@ -469,33 +484,51 @@ __global__ __launch_bounds__(NW * 64, 1) void mla_kernel(MlaParams p) {
         asm volatile("" ::: "memory");
         m_ref = fmaxf(mx, __shfl_xor(mx, 32));
       }
-      // (every lane writes the wave's vote; a score this far above the
-      // reference may overflow the weights below, and the vote discards the
-      // pass)
-      const bool over = mx > m_ref + kMlaRefMargin;
-      const int vote = __any(over) ? 1 : 0;
-      s_vote[c & 1][wave] = vote;
       const float m_use = (m_ref == kNegInf) ? 0.f : m_ref;
+      // Weights of this lane's positions of k-step s2 of the value product,
+      // in pairs.  Only k-step 0's are computed before the value product;
+      // the rest of the softmax's vector work (k-step 1's weights, the sums
+      // of the rounded weights in order, the vote) issues between k-step
+      // 0's matrix instructions, which read only pop[0].
       bf16x8 pop[2];
       const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
       float psum = 0.f;
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        uint32_t pp[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          pp[e] = pack_bf16x2(__builtin_amdgcn_exp2f(sv[8 * s2 + 2 * e] - m_use),
-                              __builtin_amdgcn_exp2f(sv[8 * s2 + 2 * e + 1] - m_use));
-          psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pp[e]), ones, psum, false);
+      uint32_t pp[2][4];
+      auto weights = [&](int s2, int e) {
+        pp[s2][e] = pack_bf16x2(__builtin_amdgcn_exp2f(sv[8 * s2 + 2 * e] - m_use),
+                                __builtin_amdgcn_exp2f(sv[8 * s2 + 2 * e + 1] - m_use));
+        if (e == 3) {
+          const u32x4 pv = {pp[s2][0], pp[s2][1], pp[s2][2], pp[s2][3]};
+          pop[s2] = as_bf16x8(pv);
         }
-        const u32x4 pv = {pp[0], pp[1], pp[2], pp[3]};
-        pop[s2] = as_bf16x8(pv);
-      }
-      l_run += psum;      // the rounded weights' sum (bf16 dot with ones)
+      };
+      auto sums = [&](int s2) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pp[s2][e]), ones, psum,
+                                                 false);
+      };
+#pragma unroll
+      for (int e = 0; e < 4; ++e) weights(0, e);
 
       // weighted sum of the latents of chunk c
       __builtin_amdgcn_sched_barrier(0);
-      pv_all(std::make_integer_sequence<int, kPvSteps>{}, acc, pop, trlo, trhi, tb);
+      pv_all(std::make_integer_sequence<int, kPvSteps>{}, acc, pop, trlo, trhi, tb,
+             [&](int step) {
+               if (step == 0) {
+                 sums(0);
+               } else if (step <= 4) {
+                 weights(1, step - 1);
+               } else {
+                 sums(1);
+                 // (every lane writes the wave's vote; a score this far
+                 // above the reference may overflow the weights, and the
+                 // vote discards the pass)
+                 const int vote = __any(mx > m_ref + kMlaRefMargin) ? 1 : 0;
+                 s_vote[c & 1][wave] = vote;
+               }
+             });
+      l_run += psum;      // the rounded weights' sum (bf16 dot with ones)
     }
     if (scan) {
       scan = false;
