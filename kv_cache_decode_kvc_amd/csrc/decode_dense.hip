@@ -947,8 +947,9 @@ __global__ __launch_bounds__(256, 2) void dense_mfma_kernel(DenseParams p) {
 // Each workgroup first reads every sequence's length (and window start)
 // into LDS and derives the item list from them: all units' whole splits of
 // S positions first, then every unit's last, shorter split (or its one
-// empty item), so the items drawn last are the short ones and the final
-// workgroups finish close together.  Against one workgroup per (unit,
+// empty item), those in four classes by length, longest first, so the items
+// drawn last are the shortest and the final workgroups finish close
+// together.  Against one workgroup per (unit,
 // split) of the longest possible length, no workgroup is launched for a
 // split past its sequence's length, the length is read once per workgroup
 // instead of once per item, and the fused call needs no arrival counters:
@@ -969,6 +970,23 @@ __device__ inline int last_at_or_below(const int* a, int n, int k) {
   }
   return lo;
 }
+// The same over 16-bit field q of packed prefixes.
+__device__ inline int last_at_or_below16(const uint64_t* a, int n, int q, int k) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if ((int)((a[mid] >> (16 * q)) & 0xFFFF) <= k) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+// Length class of a unit's last item: 3 for a remainder of at least 3S/4
+// down to 0 for one under S/4 (and the empty item); -1: no last item.
+__device__ inline int last_class(int c, int S) {
+  const int rem = c % S;
+  if (rem == 0) return c == 0 ? 0 : -1;
+  return (int)(((int64_t)rem * 4) / S);
+}
 
 template <bool APPEND, bool FP8 = false, bool PAGED = false, bool FP4 = false>
 __global__ __launch_bounds__(256, 2) void dense_persist_kernel(DenseParams p) {
@@ -976,8 +994,11 @@ __global__ __launch_bounds__(256, 2) void dense_persist_kernel(DenseParams p) {
   __shared__ int s_nraw[kPersistMaxB];          // lengths as read
   __shared__ int s_cnt[kPersistMaxB];           // positions the splits of a unit cover
   __shared__ int s_full[kPersistMaxUnits + 1];  // exclusive prefix over units: whole splits
-  __shared__ int s_part[kPersistMaxUnits + 1];  // exclusive prefix over units: last items
+  // exclusive prefixes over units of the last items of each length class,
+  // 16 bits per class
+  __shared__ uint64_t s_part[kPersistMaxUnits + 1];
   __shared__ uint32_t s_scan[256];
+  __shared__ uint64_t s_scan4[256];
   __shared__ int s_next;
 
   const int tid = threadIdx.x;
@@ -997,43 +1018,52 @@ __global__ __launch_bounds__(256, 2) void dense_persist_kernel(DenseParams p) {
   }
   __syncthreads();
   // per unit: count / S whole splits and one last item (a shorter split, or
-  // the empty item of a unit with nothing cached); exclusive prefix sums,
-  // each thread a run of units, the two counts packed (whole << 12 | last:
-  // at most 2048 units of at most 256 whole splits, so the sums stay below
-  // 2^31 + 2^12)
+  // the empty item of a unit with nothing cached) in one of four length
+  // classes; exclusive prefix sums, each thread a run of units (whole splits
+  // in 32 bits; the class counts, at most 2048 each, in 16-bit fields)
   const int per = (units + 255) / 256;
   const int u0 = min(tid * per, units), u1 = min(u0 + per, units);
-  uint32_t packed = 0;
+  uint32_t whole = 0;
+  uint64_t packed = 0;
   for (int u = u0; u < u1; ++u) {
     const int c = s_cnt[u / n_kv];
-    packed += ((uint32_t)(c / S) << 12) + ((c % S != 0 || c == 0) ? 1u : 0u);
+    whole += (uint32_t)(c / S);
+    const int q = last_class(c, S);
+    if (q >= 0) packed += 1ull << (16 * q);
   }
-  s_scan[tid] = packed;
+  s_scan[tid] = whole;
+  s_scan4[tid] = packed;
   __syncthreads();
   for (int off = 1; off < 256; off <<= 1) {
     const uint32_t x = tid >= off ? s_scan[tid - off] : 0u;
+    const uint64_t x4 = tid >= off ? s_scan4[tid - off] : 0ull;
     __syncthreads();
     s_scan[tid] += x;
+    s_scan4[tid] += x4;
     __syncthreads();
   }
   {
-    const uint32_t ex = tid ? s_scan[tid - 1] : 0u;
-    int sf = (int)(ex >> 12), sp = (int)(ex & 4095u);
+    int sf = tid ? (int)s_scan[tid - 1] : 0;
+    uint64_t sp = tid ? s_scan4[tid - 1] : 0ull;
     for (int u = u0; u < u1; ++u) {
       const int c = s_cnt[u / n_kv];
       s_full[u] = sf;
       s_part[u] = sp;
       sf += c / S;
-      sp += (c % S != 0 || c == 0) ? 1 : 0;
+      const int q = last_class(c, S);
+      if (q >= 0) sp += 1ull << (16 * q);
     }
     if (tid == 0) {
-      s_full[units] = (int)(s_scan[255] >> 12);
-      s_part[units] = (int)(s_scan[255] & 4095u);
+      s_full[units] = (int)s_scan[255];
+      s_part[units] = s_scan4[255];
     }
   }
   __syncthreads();
   const int total_full = s_full[units];
-  const int total = total_full + s_part[units];
+  const uint64_t cls = s_part[units];
+  const int n3 = (int)((cls >> 48) & 0xFFFF), n2 = (int)((cls >> 32) & 0xFFFF);
+  const int n1 = (int)((cls >> 16) & 0xFFFF), n0 = (int)(cls & 0xFFFF);
+  const int total = total_full + n3 + n2 + n1 + n0;
 
   ChunkIdx I0, I1;    // (top-k only; unused here)
   int k = blockIdx.x;
@@ -1047,7 +1077,12 @@ __global__ __launch_bounds__(256, 2) void dense_persist_kernel(DenseParams p) {
       u = last_at_or_below(s_full, units, k);
       split = k - s_full[u];
     } else {
-      u = last_at_or_below(s_part, units, k - total_full);
+      // last items, longest class first
+      int r = k - total_full, q = 3;
+      if (r >= n3) { r -= n3; q = 2;
+        if (r >= n2) { r -= n2; q = 1;
+          if (r >= n1) { r -= n1; q = 0; } } }
+      u = last_at_or_below16(s_part, units, q, r);
       split = s_cnt[u / n_kv] / S;
     }
     u = __builtin_amdgcn_readfirstlane(u);

@@ -219,8 +219,12 @@ def test_fp8_validation(L):
     assert dc(vs=float("nan")) == -8
     assert dc(out=A8) == -6
     assert dc(B=0) == 0
-    assert L.kvc_decode_attn_fp8_workspace_size(32, 64, 8, 32768, 128) == \
-        L.kvc_decode_attn_workspace_size(32, 64, 8, 32768, 128, kvc.KVC_BF16)
+    # (E4M3 caches have their own split plan in the persistent form: the
+    # workspace is the one their size query returns, and a byte less is
+    # refused before anything is enqueued)
+    w8 = L.kvc_decode_attn_fp8_workspace_size(32, 64, 8, 32768, 128)
+    assert w8 > 0
+    assert dc(B=32, n_h=64, n_kv=8, L_max=32768, wsb=w8 - 1) == -5
     assert L.kvc_decode_attn_fp8_workspace_size(32, 64, 8, 32768, 64) == 0
 
 
@@ -401,8 +405,9 @@ def test_noalloc_limits_and_validation(L):
     assert na(B=0) == 0
     # more (sequence, KV head) units than counter slots
     assert na(B=2049, n_h=64, n_kv=8, L_max=4096) == -9
-    # split partials beyond the scratch: 64 sequences x 128 heads at 32768
-    assert na(B=64, n_h=128, n_kv=8, L_max=32768) == -9
+    # split partials beyond the scratch: 64 sequences x 128 fp32 heads at
+    # 32768 (eight splits of float32 partials: 33.5 MB)
+    assert na(B=64, n_h=128, n_kv=8, L_max=32768, dt=kvc.KVC_F32) == -9
     # the benchmark's GQA layer shape fits (its own workspace is below 32 MiB)
     need = L.kvc_append_decode_attn_workspace_size(32, 64, 8, 32807, 128, kvc.KVC_BF16)
     assert 0 < need < 32 << 20
