@@ -775,7 +775,7 @@ class SelectWorkload(Workload):
     head, the 2048 highest of 131072 indexer scores (float32, seeded N(0,1)),
     32 index sets over 16 distinct score buffers (512 MB)."""
 
-    kernel = "seg_bound_kernel + seg_select_kernel"
+    kernel = "seg_select_kernel"
     unit_name = "score rows"
     NBUF = 16
 

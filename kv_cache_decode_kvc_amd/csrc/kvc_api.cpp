@@ -671,7 +671,6 @@ int kvc_topk_select(const float* scores, const int32_t* seq_lens, const int32_t*
     char* base = static_cast<char*>(workspace);
     p.S = sp.S; p.seg_len = sp.seg_len;
     p.ws_cnt = reinterpret_cast<int32_t*>(base + sp.cnt_off);
-    p.ws_info = reinterpret_cast<int32_t*>(base + sp.info_off);
     p.ws_cand = reinterpret_cast<uint32_t*>(base + sp.cand_off);
     p.ws_ccnt = reinterpret_cast<int32_t*>(base + sp.ccnt_off);
   }

@@ -117,7 +117,6 @@ struct SelectParams {
   // positions, spread over the compute units (workspace pointers below).
   int S, seg_len;
   int32_t* ws_cnt;          // [rows] arrival counters (returned to zero)
-  int32_t* ws_info;         // [rows] the row's sampled lower bound of its K-th largest key
   uint32_t* ws_cand;        // [rows, S, 16 waves, kSelSegCapw, 2] (key, position)
   int32_t* ws_ccnt;         // [rows, S, 16 waves] candidates per wave
 };
@@ -134,7 +133,7 @@ constexpr int kSelSegCapw = 128;
 constexpr int kSelSegWaves = 16;
 struct SelectSegPlan {
   int S = 1, seg_len = 0;
-  size_t cnt_off = 0, info_off = 0, cand_off = 0, ccnt_off = 0;
+  size_t cnt_off = 0, cand_off = 0, ccnt_off = 0;
   size_t bytes = 0;         // 0: no segmented form
 };
 SelectSegPlan select_seg_plan(int64_t rows, int L_max);

@@ -684,22 +684,13 @@ __device__ inline uint32_t row_bound(const SelectParams& p, int n, const uint32_
   return lb;
 }
 
-// One workgroup per row: the row's bound from its sample (to ws_info).
-__global__ __launch_bounds__(kSelThreads) void seg_bound_kernel(SelectParams p) {
-  __shared__ SelLds L;
-  const int row = blockIdx.x;
-  const int n = min(max(p.seq_lens[row / p.R], 0), p.L_max);
-  uint32_t smp[kSampleLoads];
-  sample_load(p, row, n, smp);
-  const uint32_t lb = row_bound(p, n, smp, L);
-  if (threadIdx.x == 0) p.ws_info[row] = (int32_t)lb;
-}
-
-// The workgroup of (row, segment): the row's bound, then every valid key of
-// the segment at or above it, with its position, into this wave's candidate
-// list (collected in LDS, then written out whole with device-coherent
-// stores; no atomics).  The last of the row's workgroups to finish (a
-// device-scope ticket) selects among all of them.
+// The workgroup of (row, segment): the row's bound (every workgroup of the
+// row computes the same one from the row's sample, while its own segment's
+// first loads are in flight), then every valid key of the segment at or
+// above it, with its position, into this wave's candidate list (collected
+// in LDS, then written out whole with device-coherent stores; no atomics).
+// The last of the row's workgroups to finish (a device-scope ticket)
+// selects among all of them.
 __global__ __launch_bounds__(kSelThreads) void seg_select_kernel(SelectParams p) {
   __shared__ SelLds L;
   __shared__ int s_last;
@@ -709,8 +700,8 @@ __global__ __launch_bounds__(kSelThreads) void seg_select_kernel(SelectParams p)
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
-  // the segment's first two steps in flight, then the row's bound (from
-  // seg_bound_kernel)
+  // the row's sample, then the segment's first two steps in flight; the
+  // bound is computed from the sample while the steps arrive
   const __amdgpu_buffer_rsrc_t sr =
       make_rsrc(p.scores + (size_t)q.row * p.L_max + q.s0, (uint32_t)q.sn * 4u);
   constexpr int kQ = kSelUnroll / 4;       // 16-byte loads per lane and step
@@ -721,9 +712,13 @@ __global__ __launch_bounds__(kSelThreads) void seg_select_kernel(SelectParams p)
       v[i] = __builtin_amdgcn_raw_buffer_load_b128(sr, tid * 16u,
                                                    (uint32_t)(base + i * kSelThreads * 4) * 4u, 0);
   };
+  uint32_t smp[kSampleLoads];
+  sample_load(p, q.row, q.n, smp);
+  __builtin_amdgcn_sched_barrier(0);
   load_step(st0, 0);
   load_step(st1, kSelStep);
-  const uint32_t lb = (uint32_t)p.ws_info[q.row];
+  __builtin_amdgcn_sched_barrier(0);
+  const uint32_t lb = row_bound(p, q.n, smp, L);
 
   const __amdgpu_buffer_rsrc_t wc_r = make_rsrc(p.ws_cand, kWsRecords);
   const __amdgpu_buffer_rsrc_t wn_r = make_rsrc(p.ws_ccnt, kWsRecords);
@@ -790,6 +785,20 @@ __global__ __launch_bounds__(kSelThreads) void seg_select_kernel(SelectParams p)
   const int c = tid < nreg ? (int)__builtin_amdgcn_raw_buffer_load_b32(
                                  wn_r, (uint32_t)(((size_t)q.row * nreg + tid) * 4), 0, kCoherent)
                            : 0;
+  // Wave w copies lists w, w + 16, ... (kSelSegCapw slots each: two per
+  // lane).  Its first batch (four lists) is loaded whole together with the
+  // counts, before they are known, so the gather costs no second round trip;
+  // slots past a list's count are loaded but not used.
+  auto load_batch = [&](u32x2 (&v)[8], int r0) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int r = r0 + (j >> 1) * kSelWaves, i = lane + (j & 1) * 64;
+      v[j] = __builtin_amdgcn_raw_buffer_load_b64(
+          wc_r, row_cand + (uint32_t)(((r < nreg ? r : 0) * kSelSegCapw + i) * 8), 0, kCoherent);
+    }
+  };
+  u32x2 v[8];
+  load_batch(v, wave);
   const int over = __syncthreads_or(c > kSelSegCapw);
   int total = 0;
   const int off = block_exclusive_scan(c, L, total);
@@ -809,21 +818,10 @@ __global__ __launch_bounds__(kSelThreads) void seg_select_kernel(SelectParams p)
   const int W = (n + 31) >> 5;
   for (int w = tid; w < W; w += kSelThreads) sel[w] = 0u;
   __syncthreads();
-  // gather: wave w copies lists w, w + 16, ... (at most kSelSegCapw entries
-  // each: two per lane), all of its loads in flight together; list r's
-  // entries go to s_off[r] onwards
+  // gather: list r's entries go to s_off[r] onwards
   {
     for (int r0 = wave; r0 < nreg; r0 += kSelWaves * 4) {
-      u32x2 v[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int r = r0 + (j >> 1) * kSelWaves, i = lane + (j & 1) * 64;
-        const bool ok = r < nreg && i < s_off[min(r + 1, nreg)] - s_off[min(r, nreg)];
-        // (slots past a list's count load its first slot, unused)
-        v[j] = __builtin_amdgcn_raw_buffer_load_b64(
-            wc_r, row_cand + (uint32_t)(((ok ? r : 0) * kSelSegCapw + (ok ? i : 0)) * 8), 0,
-            kCoherent);
-      }
+      if (r0 != wave) load_batch(v, r0);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int r = r0 + (j >> 1) * kSelWaves, i = lane + (j & 1) * 64;
@@ -895,7 +893,6 @@ SelectSegPlan select_seg_plan(int64_t rows, int L_max) {
   size_t off = 0;
   auto take = [&](size_t bytes) { const size_t o = off; off += round_up(bytes, 256); return o; };
   sp.cnt_off = take((size_t)rows * 4);          // arrival counters (zeroed once, kept zero)
-  sp.info_off = take((size_t)rows * 4);
   sp.cand_off = take((size_t)rows * sp.S * kSelSegWaves * kSelSegCapw * 8);
   sp.ccnt_off = take((size_t)rows * sp.S * kSelSegWaves * 4);
   sp.bytes = off;
@@ -919,7 +916,6 @@ hipError_t launch_topk_select(const SelectParams& p, hipStream_t s) {
   const unsigned rows = (unsigned)((size_t)p.B * p.R);
   if (p.S >= 2) {
     const unsigned segs = rows * (unsigned)p.S;
-    hipLaunchKernelGGL(seg_bound_kernel, dim3(rows), dim3(kSelThreads), 0, s, p);
     hipLaunchKernelGGL(seg_select_kernel, dim3(segs), dim3(kSelThreads), dyn, s, p);
   } else {
     hipLaunchKernelGGL(topk_select_kernel, dim3(rows), dim3(kSelThreads), dyn, s, p);
