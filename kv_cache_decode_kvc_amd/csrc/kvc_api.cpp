@@ -76,7 +76,12 @@ SplitPlan plan_splits(int kind, int64_t units, int64_t n_max) {
     return {Sf, ceil_div(n_max, Sf), 0};
   }
   if (units * dense_splits(n_max, kDenseMinSplit) <= kDenseRound + kDenseRound / 4) {
-    int64_t P = units >= kDenseRound ? 1 : kDenseRound / units;
+    // (top-k: one round of one workgroup per CU, so each wave has four
+    // listed chunks to pipeline its index and row loads over; measured on
+    // the 2048-of-131072 layer over 64 units: 21.6 us with 4 splits of 512
+    // against 23.1 with 8 of 256 and 23.1 with 640)
+    const int64_t round = kind == KVC_KIND_TOPK ? kCUs : kDenseRound;
+    int64_t P = units >= round ? 1 : round / units;
     if (P > kMaxSplits) P = kMaxSplits;
     // no more splits than n_max has minimum-size pieces
     const int64_t P_fill = dense_splits(n_max, kDenseMinEvenSplit);

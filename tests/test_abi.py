@@ -88,7 +88,7 @@ def test_split_policy_and_override(L):
     assert kvc.kvc_split_positions(kvc.KVC_KIND_DENSE, 1, 32, 4097) == 288
     assert kvc.kvc_split_positions(kvc.KVC_KIND_DENSE, 1, 32, 4096) == 256
     # top-k 2048 of 64 units: 8 splits of 256
-    assert kvc.kvc_split_positions(kvc.KVC_KIND_TOPK, 8, 64, 2048) == 256
+    assert kvc.kvc_split_positions(kvc.KVC_KIND_TOPK, 8, 64, 2048) == 512
     # tiny problem: at least 128 positions per split
     assert kvc.kvc_split_positions(kvc.KVC_KIND_DENSE, 1, 4, 300) == 128
     # at most 256 splits per sequence
