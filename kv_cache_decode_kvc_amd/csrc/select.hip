@@ -604,18 +604,22 @@ __device__ inline void find_bin_wave(const uint32_t* h, SelLds& L, int r) {
   __syncthreads();
 }
 
-// r-th largest of the values get(i) (i < kFinPer; counted where ok(i))
-// matching prefix under pmask, refined digit by digit at the shifts sh and
-// masks dm (which must cover every bit outside pmask; digits below 2048).
-// Two 2048-bin histograms h0, h1 alternate: each pass counts into one while
-// the other is cleared for the next; the caller clears h0 (with a barrier
-// after).  Two barriers per pass.  Returns the value; gt and eq count the
-// matching values above it and equal to it.
+// r-th largest of the values get(i) (i < nv, at most kFinPer, uniform;
+// counted where ok(i)) matching prefix under pmask, refined digit by digit
+// at the shifts sh and masks dm (which must cover every bit outside pmask;
+// digits below 2048).  Two 2048-bin histograms h0, h1 alternate: each pass
+// counts into one while the other is cleared for the next; the caller
+// clears h0 (with a barrier after).  Two barriers per pass.  The first pass
+// aggregates lanes that share a bin (candidates above a bound share a few
+// leading digits); later passes, whose digits are spread, add one atomic
+// per lane.  Returns the value; gt and eq count the matching values above
+// it and equal to it.
 template <int NP, typename Get, typename Ok>
 __device__ __forceinline__ uint32_t reg_select(Get get, Ok ok, int r, uint32_t prefix,
                                                uint32_t pmask, const int (&sh)[NP],
                                                const uint32_t (&dm)[NP], uint32_t* h0,
-                                               uint32_t* h1, SelLds& L, int& gt, int& eq) {
+                                               uint32_t* h1, SelLds& L, int& gt, int& eq,
+                                               int nv = kFinPer) {
   gt = 0;
   eq = 0;
 #pragma unroll
@@ -624,8 +628,12 @@ __device__ __forceinline__ uint32_t reg_select(Get get, Ok ok, int r, uint32_t p
     uint32_t* hn = (pass & 1) ? h0 : h1;
 #pragma unroll
     for (int i = 0; i < kFinPer; ++i) {
+      if (i >= nv) break;
       const uint32_t x = get(i);
-      hist_add(h, (x >> sh[pass]) & dm[pass], ok(i) && (x & pmask) == prefix);
+      const bool on = ok(i) && (x & pmask) == prefix;
+      const uint32_t bin = (x >> sh[pass]) & dm[pass];
+      if (pass == 0) hist_add(h, bin, on);
+      else if (on) atomicAdd(&h[bin], 1u);
     }
     if (pass + 1 < NP)
       for (int i = threadIdx.x; i < kBins; i += kSelThreads) hn[i] = 0u;
@@ -842,6 +850,7 @@ __global__ __launch_bounds__(kSelThreads) void seg_select_kernel(SelectParams p)
     rp[i] = e < total ? cp[e] : 0u;
   }
   auto valid = [&](int i) { return tid + i * kSelThreads < total; };
+  const int nv = (total + kSelThreads - 1) / kSelThreads;   // entries per thread, at most
   // (the candidate area is free again: two histograms there)
   uint32_t* h0 = dyn;
   uint32_t* h1 = dyn + kBins;
@@ -854,7 +863,7 @@ __global__ __launch_bounds__(kSelThreads) void seg_select_kernel(SelectParams p)
     const int shk[3] = {21, 10, 0};
     const uint32_t dmk[3] = {0x7FFu, 0x7FFu, 0x3FFu};
     thr = reg_select<3>([&](int i) { return rk[i]; }, valid, p.K, 0u, 0u, shk, dmk, h0, h1, L,
-                        gt, eq);
+                        gt, eq, nv);
     const int take = p.K - gt;
     if (take < eq) {
       // equal keys: the lowest positions (largest ~position; positions are
@@ -865,7 +874,7 @@ __global__ __launch_bounds__(kSelThreads) void seg_select_kernel(SelectParams p)
       const int shp[2] = {7, 0};
       const uint32_t dmp[2] = {0x7FFu, 0x7Fu};
       pthr = reg_select<2>([&](int i) { return rk[i] == thr ? ~rp[i] : 0u; }, valid, take,
-                           0xFFFC0000u, 0xFFFC0000u, shp, dmp, h0, h1, L, g2, e2);
+                           0xFFFC0000u, 0xFFFC0000u, shp, dmp, h0, h1, L, g2, e2, nv);
     }
   }
 #pragma unroll
