@@ -310,10 +310,14 @@ int kvc_append_fp4(void* k_codes, void* k_scales, void* v_codes, void* v_scales,
 
 /*
  * kvc_decode_attn_fp4 - kvc_decode_attn over an FP4 cache written by
- * kvc_append_fp4: keys and values are dequantised (exactly, to bf16) before
- * the attention.  q and out are bf16, lse float32 or NULL.  d = 128,
- * n_h / n_kv <= 16; scale arrays 8-byte aligned.  Workspace rules as for
- * kvc_decode_attn.
+ * kvc_append_fp4: keys and values are dequantised exactly (to f16: every
+ * E2M1 value times an E4M3 scale is an f16 number) and both products run
+ * in f16 with float32 accumulation; each head's query is taken to f16
+ * times a power of two (exact for every component within 2^29 of the
+ * head's largest), the softmax weights are rounded to f16.  q and out are
+ * bf16, lse float32 or NULL.  d = 128, n_h / n_kv <= 16; scale arrays
+ * 8-byte aligned; scale bytes are finite E4M3 values (as kvc_append_fp4
+ * writes them).  Workspace rules as for kvc_decode_attn.
  */
 size_t kvc_decode_attn_fp4_workspace_size(int B, int n_h, int n_kv, int L_max, int d);
 int kvc_decode_attn_fp4(const void* q, const void* k_codes, const void* k_scales,

@@ -493,25 +493,43 @@ struct WaveState {
   f32x4 acc[8];   // O^T tiles
 };
 
-template <bool TOPK>
+// F16: the chunk's rows, the query operand and the weights are f16 (bits
+// in the same containers) and both products are f16 MFMAs (the FP4 cache
+// path, whose rows widen to f16 at half the vector work of bf16).
+// scale_log2 is this lane's head's factor (lane r = head r).
+template <bool TOPK, bool F16 = false>
 __device__ inline void compute_chunk(const Chunk& c, int cs, int end,
-                                     const bf16x8 (&qop)[4], float scale_log2,
+                                     const u32x4 (&qop)[4], float scale_log2,
                                      int g, WaveState& st) {
+  auto mma = [](u32x4 a, u32x4 b, f32x4 acc) {
+    if constexpr (F16)
+      return __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(a), as_f16x8(b), acc, 0, 0, 0);
+    else
+      return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), acc, 0, 0, 0);
+  };
   f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
-    s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(c.k[0][kk]), qop[kk], s0, 0, 0, 0);
-    s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(c.k[1][kk]), qop[kk], s1, 0, 0, 0);
+    s0 = mma(c.k[0][kk], qop[kk], s0);
+    s1 = mma(c.k[1][kk], qop[kk], s1);
   }
   float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
   float mx = kNegInf;
+  if (!TOPK && cs + kDenseChunk <= end) {   // (wave-uniform) no row past the end
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    bool valid;
-    if constexpr (TOPK) valid = (c.vmask >> e) & 1;
-    else valid = cs + g * 8 + e < end;
-    sv[e] = valid ? sv[e] * scale_log2 : kNegInf;
-    mx = fmaxf(mx, sv[e]);
+    for (int e = 0; e < 8; ++e) {
+      sv[e] *= scale_log2;
+      mx = fmaxf(mx, sv[e]);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      bool valid;
+      if constexpr (TOPK) valid = (c.vmask >> e) & 1;
+      else valid = cs + g * 8 + e < end;
+      sv[e] = valid ? sv[e] * scale_log2 : kNegInf;
+      mx = fmaxf(mx, sv[e]);
+    }
   }
   mx = fmaxf(mx, __shfl_xor(mx, 16));
   mx = fmaxf(mx, __shfl_xor(mx, 32));
@@ -530,13 +548,19 @@ __device__ inline void compute_chunk(const Chunk& c, int cs, int end,
   float psum = 0.f;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    pp[e] = pack_bf16x2(__builtin_amdgcn_exp2f(sv[2 * e] - m_use),
-                        __builtin_amdgcn_exp2f(sv[2 * e + 1] - m_use));
-    psum += bf16_lo(pp[e]) + bf16_hi(pp[e]);
+    const float w0 = __builtin_amdgcn_exp2f(sv[2 * e] - m_use);
+    const float w1 = __builtin_amdgcn_exp2f(sv[2 * e + 1] - m_use);
+    if constexpr (F16) {
+      const f16x2 h = {(_Float16)w0, (_Float16)w1};
+      pp[e] = __builtin_bit_cast(uint32_t, h);
+      psum = __builtin_amdgcn_fdot2(h, f16x2{(_Float16)1.f, (_Float16)1.f}, psum, false);
+    } else {
+      pp[e] = pack_bf16x2(w0, w1);
+      psum += bf16_lo(pp[e]) + bf16_hi(pp[e]);
+    }
   }
   st.l = st.l * alpha + psum;
   const u32x4 pv = {pp[0], pp[1], pp[2], pp[3]};
-  const bf16x8 pop = as_bf16x8(pv);
 #pragma unroll
   for (int m = 0; m < 8; ++m) {
     const uint32_t sel = (m & 1) ? 0x07060302u : 0x05040100u;
@@ -546,7 +570,7 @@ __device__ inline void compute_chunk(const Chunk& c, int cs, int end,
     a[1] = __builtin_amdgcn_perm(c.v[3][dw], c.v[2][dw], sel);
     a[2] = __builtin_amdgcn_perm(c.v[5][dw], c.v[4][dw], sel);
     a[3] = __builtin_amdgcn_perm(c.v[7][dw], c.v[6][dw], sel);
-    st.acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), pop, st.acc[m], 0, 0, 0);
+    st.acc[m] = mma(a, pv, st.acc[m]);
   }
 }
 
@@ -595,9 +619,12 @@ __device__ inline void expand_chunk(const ChunkF8& f, Chunk& c) {
 // FP4 cache (d = 128): rows of 64 code bytes (E2M1, channel 2i in the low
 // nibble of byte i) and 8 scale bytes (E4M3, one per 16 channels).  K: lane
 // group g loads the 16 code bytes of channels 32g .. 32g + 31, so k-step kk
-// covers channels 32g + 8kk .. +7 (q is loaded in that order), and the scale
-// word holding blocks 2g and 2g + 1.  V keeps the bf16 layout: 4 code bytes
-// (channels 8r .. 8r + 7) per row and the word holding block r / 2.
+// covers channels 32g + 8kk .. +7 (q is loaded in that order), and the two
+// scale bytes of blocks 2g and 2g + 1.  V keeps the bf16 layout: 4 code
+// bytes (channels 8r .. 8r + 7) per row and the scale byte of block r / 2.
+// Each stream takes one offset select per chunk; its rows differ by
+// immediate offsets (a chunk past the split starts at kOobOffset, past every
+// buffer's range, and reads zeros like the rows past the length).
 struct ChunkF4 {
   u32x4 k[2];
   uint32_t ks[2];
@@ -612,35 +639,40 @@ __device__ inline void load_chunk(ChunkF4& c, int cs, int end, __amdgpu_buffer_r
                                   __amdgpu_buffer_rsrc_t vsr, int r, int g) {
   constexpr uint32_t kRow = 64, kSRow = 8;
   const bool live = cs < end;
+  const uint32_t krow = cs + (r >> 2) * 8 + (r & 3);           // rows krow + 4a
+  const uint32_t kb = live ? krow * kRow + g * 16 : kOobOffset;
+  const uint32_t ksb = live ? krow * kSRow + g * 2 : kOobOffset;
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
-    const uint32_t row = cs + (r >> 2) * 8 + a * 4 + (r & 3);
-    c.k[a] = buf_load16_stream(kr, live ? row * kRow + g * 16 : kOobOffset);
-    c.ks[a] = __builtin_amdgcn_raw_buffer_load_b32(
-        ksr, live ? row * kSRow + (g >> 1) * 4 : kOobOffset, 0, kStream);
+    c.k[a] = buf_load16_stream(kr, kb + a * 4 * kRow);
+    c.ks[a] = __builtin_amdgcn_raw_buffer_load_b16(ksr, ksb + a * 4 * kSRow, 0, kStream);
   }
-  const uint32_t row0 = cs + g * 8;
+  const uint32_t row0 = cs + g * 8;                           // rows row0 + e
+  const uint32_t vb = live ? row0 * kRow + r * 4 : kOobOffset;
+  const uint32_t vsb = live ? row0 * kSRow + (r >> 1) : kOobOffset;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    c.v[e] = __builtin_amdgcn_raw_buffer_load_b32(
-        vr, live ? (row0 + e) * kRow + r * 4 : kOobOffset, 0, kStream);
-    c.vs[e] = __builtin_amdgcn_raw_buffer_load_b32(
-        vsr, live ? (row0 + e) * kSRow + (r >> 3) * 4 : kOobOffset, 0, kStream);
+    c.v[e] = __builtin_amdgcn_raw_buffer_load_b32(vr, vb + e * kRow, 0, kStream);
+    c.vs[e] = __builtin_amdgcn_raw_buffer_load_b8(vsr, vsb + e * kSRow, 0, kStream);
   }
 }
 
-__device__ inline void expand_chunk(const ChunkF4& f, Chunk& c, int r, int g) {
+// Widened to f16 (exactly: fp4x8_to_f16x8) for the f16 products; the
+// scales two at a time (blocks 2g and 2g + 1 of a K row; the block of V rows
+// e and e + 1).
+__device__ inline void expand_chunk(const ChunkF4& f, Chunk& c) {
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
-    const uint32_t w = f.ks[a] >> (16 * (g & 1));          // blocks 2g, 2g + 1
-    const float s0 = __builtin_amdgcn_cvt_f32_fp8(w, 0);
-    const float s1 = __builtin_amdgcn_cvt_f32_fp8(w, 1);
+    const f16x2 s = e4m3x2_to_f16x2(f.ks[a]);
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) c.k[a][kk] = fp4x8_to_bf16x8(f.k[a][kk], kk < 2 ? s0 : s1);
+    for (int kk = 0; kk < 4; ++kk) c.k[a][kk] = fp4x8_to_f16x8(f.k[a][kk], kk < 2 ? s[0] : s[1]);
   }
 #pragma unroll
-  for (int e = 0; e < 8; ++e)
-    c.v[e] = fp4x8_to_bf16x8(f.v[e], __builtin_amdgcn_cvt_f32_fp8(f.vs[e] >> (8 * ((r >> 1) & 3)), 0));
+  for (int e = 0; e < 8; e += 2) {
+    const f16x2 s = e4m3x2_to_f16x2(f.vs[e] | (f.vs[e + 1] << 8));
+    c.v[e] = fp4x8_to_f16x8(f.v[e], s[0]);
+    c.v[e + 1] = fp4x8_to_f16x8(f.v[e + 1], s[1]);
+  }
   c.vmask = 0xFF;
 }
 
@@ -733,18 +765,43 @@ __device__ __forceinline__ void dense_mfma_item(const DenseParams& p, int b, int
            : PAGED ? make_rsrc(p.block_table + (size_t)b * p.max_blocks, (uint32_t)p.max_blocks * 4u)
                    : kr;
 
-  bf16x8 qop[4];
+  u32x4 qop[4];
   if (r < p.G) {
     const uint16_t* qrow =
         (const uint16_t*)p.q + ((size_t)b * p.n_h + j * p.G + r) * 128;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
-      qop[kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(
-          qrow + (FP4 ? fp4_q_col(kk, g) : FP8 ? fp8_q_col(kk, g) : kk * 32 + g * 8)));
+      qop[kk] = *reinterpret_cast<const u32x4*>(
+          qrow + (FP4 ? fp4_q_col(kk, g) : FP8 ? fp8_q_col(kk, g) : kk * 32 + g * 8));
   } else {
-    const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) qop[kk] = as_bf16x8(z);
+    for (int kk = 0; kk < 4; ++kk) qop[kk] = u32x4{0u, 0u, 0u, 0u};
+  }
+  // The FP4 path's f16 products take the query as f16: head r's row times
+  // 2^a with a = 14 - (exponent of its largest magnitude), so that the
+  // largest lies in [2^14, 2^15) and every bf16 component not 2^29 below it
+  // converts exactly; the head's score factor takes 2^-a back (exact).
+  float scale_log2 = p.scale_log2;
+  if constexpr (FP4) {
+    float qm = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        qm = fmaxf(qm, fmaxf(fabsf(bf16_lo(qop[kk][w])), fabsf(bf16_hi(qop[kk][w]))));
+    qm = fmaxf(qm, __shfl_xor(qm, 16));
+    qm = fmaxf(qm, __shfl_xor(qm, 32));
+    int sh = qm > 0.f ? 14 - ((int)((__float_as_uint(qm) >> 23) & 0xFF) - 127) : 0;
+    sh = sh < -126 ? -126 : (sh > 126 ? 126 : sh);
+    const float up = __uint_as_float((uint32_t)(127 + sh) << 23);
+    scale_log2 *= __uint_as_float((uint32_t)(127 - sh) << 23);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const f16x2 h = {(_Float16)(bf16_lo(qop[kk][w]) * up), (_Float16)(bf16_hi(qop[kk][w]) * up)};
+        qop[kk][w] = __builtin_bit_cast(uint32_t, h);
+      }
   }
 
   WaveState st;
@@ -774,8 +831,8 @@ __device__ __forceinline__ void dense_mfma_item(const DenseParams& p, int b, int
   auto compute = [&](Raw& c, int at) {
     if constexpr (FP4) {
       Chunk x;
-      expand_chunk(c, x, r, g);
-      compute_chunk<false>(x, at, end, qop, p.scale_log2, g, st);
+      expand_chunk(c, x);
+      compute_chunk<false, true>(x, at, end, qop, scale_log2, g, st);
     } else if constexpr (FP8) {
       Chunk x;
       expand_chunk(c, x);

@@ -112,14 +112,18 @@ struct DenseCheck {
 // depends on it).
 enum CacheFmt { kFmtPlain = 0, kFmtFp8 = 1, kFmtFp4 = 2 };
 
-// Persistent form: items of whole 1024-position multiples, about this many
-// per call (3.5 per workgroup for bf16 and FP4 caches, 5.5 for E4M3 ones).
-// Measured on the 32-sequence GQA layer (lengths 1024..32768, 256 units):
-// contiguous bf16 314.7 us at 5120 positions against 326.8 at 2048, FP4
-// 135.9 against 153.2, paged 325 against 333, E4M3 177.8 at 3072 against
-// 180.1 at 2048 and 183.9 at 5120.
+// Persistent form: items of whole 1024-position multiples (the multiple
+// nearest n_max / P, P = target / units), about this many per call (3.5 per
+// workgroup for bf16 caches, 5.5 for E4M3 ones, 2 for FP4 ones, whose items
+// are the quickest to stream and so pay most for each item's set-up and
+// merge).  Measured on the 32-sequence GQA layer (lengths 1024..32768, 256
+// units): contiguous bf16 314.7 us at 5120 positions against 326.8 at 2048,
+// paged 325 against 333, E4M3 177.8 at 3072 against 180.1 at 2048 and
+// 183.9 at 5120, FP4 123.7 at 8192 against 129.3 at 5120, 128.6 at 6144
+// and 131.6 at 9216.
 constexpr int64_t kPersistItems = 1792;
 constexpr int64_t kPersistItemsFp8 = 2816;
+constexpr int64_t kPersistItemsFp4 = 1024;
 constexpr int64_t kPersistGran = 1024;
 
 // window > 0: at most `window` positions are attended, which is what the
@@ -151,9 +155,12 @@ DenseCheck check_dense_shape(int B, int n_h, int n_kv, int L_max, int d,
   c.persist = !c.even && !topk && dtype == KVC_BF16 && d == 128 && B <= kPersistMaxB &&
               units <= kPersistMaxUnits;
   if (c.persist && g_split_override.load() == 0) {
-    const int64_t target = fmt == kFmtFp8 ? kPersistItemsFp8 : kPersistItems;
+    const int64_t target = fmt == kFmtFp8   ? kPersistItemsFp8
+                           : fmt == kFmtFp4 ? kPersistItemsFp4
+                                            : kPersistItems;
     const int64_t P_allowed = units < target ? target / units : 1;
-    int64_t S = (int64_t)round_up((size_t)ceil_div(n_max, P_allowed), (size_t)kPersistGran);
+    int64_t S = (n_max / P_allowed + kPersistGran / 2) / kPersistGran * kPersistGran;
+    if (S < kPersistGran) S = kPersistGran;
     const int64_t S_cap = (int64_t)round_up((size_t)ceil_div(n_max, kMaxSplits), (size_t)kDenseGran);
     if (S < S_cap) S = S_cap;
     if (S < c.S) S = c.S;

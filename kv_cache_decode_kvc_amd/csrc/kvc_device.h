@@ -57,19 +57,30 @@ __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+__device__ inline f16x8 as_f16x8(u32x4 x) { return __builtin_bit_cast(f16x8, x); }
+
 // Eight E2M1 codes (byte i holds channels 2i (low nibble) and 2i + 1) times
-// the block scale s, as eight bf16.  The conversion with scale 1.0 is exact,
-// and an E2M1 value times an E4M3 scale has at most 6 significant bits, so
-// the float32 product and its bf16 rounding are exact too.  (The
-// conversion's own scale operand only honours a power of two, hence the
-// separate multiply.)
-__device__ inline u32x4 fp4x8_to_bf16x8(uint32_t w, float s) {
-  const f32x2 f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
-  const f32x2 f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
-  const f32x2 f2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
-  const f32x2 f3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
-  return u32x4{pack_bf16x2(f0.x * s, f0.y * s), pack_bf16x2(f1.x * s, f1.y * s),
-               pack_bf16x2(f2.x * s, f2.y * s), pack_bf16x2(f3.x * s, f3.y * s)};
+// the block scale s (an E4M3 value, here as f16), as eight f16.  Exact: the
+// conversion (scale operand 1.0) gives the code values 0 .. 6, E4M3 values
+// are f16 numbers, and their product has at most 6 significant bits and
+// lies in 2^-10 .. 2688 (f16 normal numbers hold 11 bits from 2^-14 to
+// 65504).  One conversion and one packed f16 multiply per two numbers.
+__device__ inline u32x4 fp4x8_to_f16x8(uint32_t w, _Float16 s) {
+  const f16x2 m = {s, s};
+  u32x4 r;
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * m);
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * m);
+  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * m);
+  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * m);
+  return r;
+}
+
+// Two E4M3 codes (bits 0-7 and 8-15 of w) as two f16, exactly.
+__device__ inline f16x2 e4m3x2_to_f16x2(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
 }
 
 __device__ inline uint16_t to_bf16_bits(float x) {

@@ -257,11 +257,17 @@ def test_fp4_validation(L):
     assert dc(n_h=7) == -2
     assert dc(n_h=64, n_kv=2) == -4   # group of 32 heads
     assert dc(scale=float("nan")) == -8
-    assert dc(ks=A4) == -6            # scale rows are read 4 bytes at a time, 8-byte aligned
+    assert dc(ks=A4) == -6            # scale arrays 8-byte aligned (the header's contract)
     assert dc(out=A8) == -6
     assert dc(B=0) == 0
-    assert L.kvc_decode_attn_fp4_workspace_size(32, 64, 8, 32768, 128) == \
-        L.kvc_decode_attn_workspace_size(32, 64, 8, 32768, 128, kvc.KVC_BF16)
+    # FP4 caches take their own persistent split size (8192 positions for
+    # 256 units at L_max 32768: 4 splits where bf16 caches take 7), so the
+    # partials are fewer; the size query is still what the call checks
+    w4 = L.kvc_decode_attn_fp4_workspace_size(32, 64, 8, 32768, 128)
+    assert 0 < w4 < L.kvc_decode_attn_workspace_size(32, 64, 8, 32768, 128, kvc.KVC_BF16)
+    assert w4 >= 32 * 64 * 4 * 128 * 4
+    big = dict(B=32, n_h=64, n_kv=8, L_max=32768)
+    assert dc(wsb=w4 - 1, **big) == -5
     assert L.kvc_decode_attn_fp4_workspace_size(32, 64, 8, 32768, 64) == 0
 
 

@@ -160,27 +160,32 @@ def test_fp4_decode_parity(n_h, n_kv, pre, L_max, split):
 def test_fp4_every_code_exact():
     """One cached position per sequence: the output is that position's value
     row dequantised, and with a one-hot query at column c the lse is
-    scale * key[c].  Each 16-channel block takes a different scale code
-    (from tiny subnormal to 448) and holds all 16 E2M1 codes in a rotated
-    order, so every code meets every scale through both operands; the
-    one-hot columns pin the key column order against the query's."""
-    B, n_h, n_kv, d, L_max = 1, 128, 8, 128, 4
+    scale * key[c].  The 2 x 8 x 8 blocks of each operand take every finite
+    non-negative E4M3 scale code 0x00 .. 0x7E (zero, the subnormals up to
+    448) in a different order for keys and values, and each block holds all
+    16 E2M1 codes in a rotated order, so every code meets every scale
+    through both operands; the one-hot columns pin the key column order
+    against the query's."""
+    B, n_h, n_kv, d, L_max = 2, 128, 8, 128, 4
     G = n_h // n_kv
-    scale_codes = np.array([0x01, 0x05, 0x0F, 0x22, 0x38, 0x47, 0x5B, 0x7E], np.uint8)
+    all_scales = np.concatenate([np.arange(0x7F), [0x38]]).astype(np.uint8)   # 128 blocks
+    v_scales = all_scales.reshape(B, n_kv, 8)
+    k_scales = np.roll(all_scales, 37).reshape(B, n_kv, 8)
     kc = np.zeros((B, n_kv, L_max, d // 2), np.uint8)
     vc = np.zeros((B, n_kv, L_max, d // 2), np.uint8)
     ks = np.zeros((B, n_kv, L_max, d // 16), np.uint8)
     vs = np.zeros((B, n_kv, L_max, d // 16), np.uint8)
     q = np.zeros((B, n_h, d), np.float32)
-    for j in range(n_kv):
-        codes = np.concatenate([np.roll(np.arange(16), j + blk) for blk in range(8)])
-        kcodes = np.roll(codes, 5 * j)
-        vc[0, j, 0] = (codes[0::2] | (codes[1::2] << 4)).astype(np.uint8)
-        kc[0, j, 0] = (kcodes[0::2] | (kcodes[1::2] << 4)).astype(np.uint8)
-        ks[0, j, 0] = np.roll(scale_codes, j)
-        vs[0, j, 0] = np.roll(scale_codes, -j)
-        for h in range(G):
-            q[0, j * G + h, j * G + h] = 1.0
+    for b in range(B):
+        for j in range(n_kv):
+            codes = np.concatenate([np.roll(np.arange(16), j + blk + 3 * b) for blk in range(8)])
+            kcodes = np.roll(codes, 5 * j + b)
+            vc[b, j, 0] = (codes[0::2] | (codes[1::2] << 4)).astype(np.uint8)
+            kc[b, j, 0] = (kcodes[0::2] | (kcodes[1::2] << 4)).astype(np.uint8)
+            ks[b, j, 0] = k_scales[b, j]
+            vs[b, j, 0] = v_scales[b, j]
+            for h in range(G):
+                q[b, j * G + h, j * G + h] = 1.0
     scale = 0.25
     sl = torch.ones(B, dtype=torch.int32, device="cuda")
     qd = dev(syn.bf16_bits(q))
@@ -193,8 +198,11 @@ def test_fp4_every_code_exact():
     o = host_f64(out)
     want_v = oracle.dequantize_fp4(vc[:, :, 0], vs[:, :, 0])          # [B, n_kv, d]
     want_k = oracle.dequantize_fp4(kc[:, :, 0], ks[:, :, 0])
-    for j in range(n_kv):
-        assert np.array_equal(o[0, j * G:(j + 1) * G], np.broadcast_to(want_v[0, j], (G, d)))
-    want_l = np.array([scale * want_k[0, i // G, i] for i in range(n_h)])
-    got_l = host(lse)[0].astype(np.float64)
-    assert np.abs(got_l - want_l).max() <= 1e-6 * np.abs(want_l).max() + 1e-7
+    for b in range(B):
+        for j in range(n_kv):
+            assert np.array_equal(o[b, j * G:(j + 1) * G], np.broadcast_to(want_v[b, j], (G, d)))
+    for b in range(B):
+        want_l = np.array([scale * want_k[b, i // G, i] for i in range(n_h)])
+        got_l = host(lse)[b].astype(np.float64)
+        # a zero key gives lse = 0 (one position, weight 1)
+        assert np.abs(got_l - want_l).max() <= 1e-6 * np.abs(want_l).max() + 1e-7
