@@ -55,6 +55,10 @@ SEG_CASES = [
     ("few", 2, 50000, [1500, 2048, 2049], 2048),           # fewer than, exactly, one more than K
     ("normal", 1, 262144, [262144], 4096),                 # the longest row of the form
     ("lastmax", 2, 40000, [32769, 32770, 32771, 39999], 300),   # top scores in the row's last 3
+    # the K largest far above the rest, at positions the row's sample skips
+    # (offsets 64..2047 of each 2048-position block): the bound comes from
+    # the rest, and the K-th lies more than 2^22 key steps above it
+    ("hidden", 4, 70000, [70000, 65536], 512),
 ]
 
 
@@ -71,6 +75,12 @@ def test_select_segmented_matches_oracle(kind, R, L, lens, K, ws):
     elif kind == "zeros":
         sc = np.where(rng.random((B, R, L)) < 0.5, np.float32(0.0), np.float32(-0.0)).astype(np.float32)
         sc[:, :, ::9] = 1.0
+    elif kind == "hidden":
+        for b, n in enumerate(lens):
+            unsampled = np.arange(n)[np.arange(n) % 2048 >= 64]
+            for r in range(R):
+                pos = rng.choice(unsampled, size=K + 64, replace=False)
+                sc[b, r, pos] = np.float32(1000.0) + rng.random(K + 64).astype(np.float32)
     elif kind == "lastmax":
         # the highest scores sit in the last positions of each row (lengths
         # not multiples of 4: a 16-byte load straddles the end)
