@@ -708,24 +708,30 @@ __global__ __launch_bounds__(kSelThreads) void seg_select_kernel(SelectParams p)
   const SegPos q = seg_pos(p);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
   // the row's sample, then the segment's first two steps in flight; the
   // bound is computed from the sample while the steps arrive
   const __amdgpu_buffer_rsrc_t sr =
       make_rsrc(p.scores + (size_t)q.row * p.L_max + q.s0, (uint32_t)q.sn * 4u);
+  // Wave w takes positions [w R, (w + 1) R) of the segment (R = seg_len /
+  // 16, whole 1024-position steps), so that its list, and the lists taken
+  // in (segment, wave) order, run in ascending position order.  Step k of
+  // the wave: v[i][j] is position w R + 1024 k + 256 i + 4 lane + j.
   constexpr int kQ = kSelUnroll / 4;       // 16-byte loads per lane and step
+  constexpr int kWStep = 64 * kSelUnroll;  // positions per wave and step
+  const int R = p.seg_len / kSelWaves;
+  const int wsteps = R / kWStep;
   u32x4 st0[kQ], st1[kQ];
-  auto load_step = [&](u32x4 (&v)[kQ], int base) {
+  auto load_step = [&](u32x4 (&v)[kQ], int k) {
 #pragma unroll
     for (int i = 0; i < kQ; ++i)
-      v[i] = __builtin_amdgcn_raw_buffer_load_b128(sr, tid * 16u,
-                                                   (uint32_t)(base + i * kSelThreads * 4) * 4u, 0);
+      v[i] = __builtin_amdgcn_raw_buffer_load_b128(
+          sr, lane * 16u, (uint32_t)(wave * R + k * kWStep + i * 256) * 4u, 0);
   };
   uint32_t smp[kSampleLoads];
   sample_load(p, q.row, q.n, smp);
   __builtin_amdgcn_sched_barrier(0);
   load_step(st0, 0);
-  load_step(st1, kSelStep);
+  load_step(st1, 1);
   __builtin_amdgcn_sched_barrier(0);
   const uint32_t lb = row_bound(p, q.n, smp, L);
 
@@ -744,33 +750,43 @@ __global__ __launch_bounds__(kSelThreads) void seg_select_kernel(SelectParams p)
     float lbf = -__builtin_huge_valf();
     if (lb & 0x80000000u) lbf = __uint_as_float(lb & 0x7FFFFFFFu);          // >= +0
     else if (lb != 0u && ((~lb >> 23) & 0xFFu) != 0xFFu) lbf = __uint_as_float(~lb);
-    // v[i][j]: position base + 4 (i * kSelThreads + tid) + j of the segment
-    auto process = [&](const u32x4 (&v)[kQ], int base) {
-      const bool whole = base + kSelStep <= q.sn;
+    // a lane's candidates among its four positions of each 256, placed
+    // after those of the lanes below it (one wave scan per 256 positions)
+    auto process = [&](const u32x4 (&v)[kQ], int k) {
+      const int base = wave * R + k * kWStep;
+      const bool whole = base + kWStep <= q.sn;
 #pragma unroll
-      for (int i = 0; i < kQ; ++i)
+      for (int i = 0; i < kQ; ++i) {
+        uint32_t m = 0u;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int t = base + 4 * (i * kSelThreads + tid) + j;
-          const float f = __uint_as_float(v[i][j]);
-          const bool c = f >= lbf && (whole || t < q.sn);
-          const uint64_t bc = __ballot(c);
-          if (c) {
-            const int slot = wc + __popcll(bc & below);
-            if (slot < kSelSegCapw) stage[slot] = u32x2{score_key(f), (uint32_t)(q.s0 + t)};
-          }
-          wc += __popcll(bc);
+          const int t = base + 256 * i + 4 * lane + j;
+          const bool c = __uint_as_float(v[i][j]) >= lbf && (whole || t < q.sn);
+          m |= (c ? 1u : 0u) << j;
         }
+        const int cnt = __popc(m);
+        const int incl = wave_incl_scan(cnt);
+        int slot = wc + incl - cnt;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if ((m >> j) & 1u) {
+            if (slot < kSelSegCapw)
+              stage[slot] = u32x2{score_key(__uint_as_float(v[i][j])),
+                                  (uint32_t)(q.s0 + base + 256 * i + 4 * lane + j)};
+            ++slot;
+          }
+        wc += __builtin_amdgcn_readlane(incl, 63);
+      }
     };
     process(st0, 0);
-    if (q.sn > kSelStep) process(st1, kSelStep);
+    if (wsteps > 1) process(st1, 1);
     // longer segments: the remaining steps, each loaded while the previous
     // one is processed
-    for (int base = 2 * kSelStep; base < q.sn; base += 2 * kSelStep) {
-      load_step(st0, base);
-      load_step(st1, base + kSelStep);
-      process(st0, base);
-      if (base + kSelStep < q.sn) process(st1, base + kSelStep);
+    for (int k = 2; k < wsteps; k += 2) {
+      load_step(st0, k);
+      load_step(st1, k + 1);
+      process(st0, k);
+      if (k + 1 < wsteps) process(st1, k + 1);
     }
     // (the wave's own LDS writes are complete for its own reads below)
     const int kept = wc < kSelSegCapw ? wc : kSelSegCapw;
@@ -833,15 +849,12 @@ __global__ __launch_bounds__(kSelThreads) void seg_select_kernel(SelectParams p)
   }
   uint32_t* ck = dyn;
   uint32_t* cp = dyn + kFinCand;
-  uint32_t* sel = dyn + kHistCopies * kBins;
   // the digit passes' two histograms lie outside the candidate area (the
-  // sample's, free since the bound, and one past the map), so h0 is cleared
-  // here with the map and the passes start as soon as the candidates are in
+  // sample's, free since the bound, and one past the map area), so h0 is
+  // cleared here and the passes start as soon as the candidates are in
   // registers
   uint32_t* h0 = L.hist;
-  uint32_t* h1 = sel + p.sel_words;
-  const int W = (n + 31) >> 5;
-  for (int w = tid; w < W; w += kSelThreads) sel[w] = 0u;
+  uint32_t* h1 = dyn + kHistCopies * kBins + p.sel_words;
   for (int i = tid; i < kBins; i += kSelThreads) h0[i] = 0u;
   __syncthreads();
   const int total = s_off[nreg];
@@ -853,7 +866,8 @@ __global__ __launch_bounds__(kSelThreads) void seg_select_kernel(SelectParams p)
     select_row(p, q.row, L, dyn);
     return;
   }
-  // gather: list r's entries go to s_off[r] onwards
+  // gather: list r's entries go to s_off[r] onwards (lists in (segment,
+  // wave) order: the candidates in ascending position order)
   {
     for (int r0 = wave; r0 < nreg; r0 += kSelWaves * 4) {
       if (r0 != wave) load_batch(v, r0);
@@ -868,16 +882,17 @@ __global__ __launch_bounds__(kSelThreads) void seg_select_kernel(SelectParams p)
     }
   }
   __syncthreads();
-  // each thread's candidates in registers: entries tid + i * kSelThreads
+  // each thread's candidates in registers: entries nv tid .. nv tid + nv - 1
+  const int nv = (total + kSelThreads - 1) / kSelThreads;   // entries per thread, at most
   uint32_t rk[kFinPer], rp[kFinPer];
 #pragma unroll
   for (int i = 0; i < kFinPer; ++i) {
-    const int e = tid + i * kSelThreads;
-    rk[i] = e < total ? ck[e] : 0u;
-    rp[i] = e < total ? cp[e] : 0u;
+    const int e = tid * nv + i;
+    const bool ok = i < nv && e < total;
+    rk[i] = ok ? ck[e] : 0u;
+    rp[i] = ok ? cp[e] : 0u;
   }
-  auto valid = [&](int i) { return tid + i * kSelThreads < total; };
-  const int nv = (total + kSelThreads - 1) / kSelThreads;   // entries per thread, at most
+  auto valid = [&](int i) { return i < nv && tid * nv + i < total; };
   uint32_t thr = 0u, pthr = 0u;
   if (!all) {
     int gt = 0, eq = 0;
@@ -923,12 +938,19 @@ __global__ __launch_bounds__(kSelThreads) void seg_select_kernel(SelectParams p)
                            0xFFFC0000u, 0xFFFC0000u, shp, dmp, h0, h1, L, g2, e2, nv);
     }
   }
+  // the chosen entries, already in position order: each thread's go after
+  // those of the threads below it; the rest of the row's K slots get -1
+  uint32_t chosen = 0u;
 #pragma unroll
   for (int i = 0; i < kFinPer; ++i)
-    if (valid(i) && (all || rk[i] > thr || (rk[i] == thr && ~rp[i] >= pthr)))
-      atomicOr(&sel[rp[i] >> 5], 1u << (rp[i] & 31));
-  __syncthreads();
-  write_out_map(sel, n, p.out + (size_t)q.row * p.K, p.K, L);
+    if (valid(i) && (all || rk[i] > thr || (rk[i] == thr && ~rp[i] >= pthr))) chosen |= 1u << i;
+  int kept = 0;
+  int o = block_exclusive_scan(__popc(chosen), L, kept);
+  int32_t* out = p.out + (size_t)q.row * p.K;
+#pragma unroll
+  for (int i = 0; i < kFinPer; ++i)
+    if ((chosen >> i) & 1u) out[o++] = (int32_t)rp[i];
+  for (int i = kept + tid; i < p.K; i += kSelThreads) out[i] = -1;
 }
 
 }  // namespace
