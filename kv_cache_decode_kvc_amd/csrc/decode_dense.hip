@@ -495,7 +495,9 @@ struct WaveState {
 
 // F16: the chunk's rows, the query operand and the weights are f16 (bits
 // in the same containers) and both products are f16 MFMAs (the FP4 cache
-// path, whose rows widen to f16 at half the vector work of bf16).
+// path, whose rows widen to f16 at half the vector work of bf16); its value
+// rows come already arranged as the value product's operands: c.v[m] is
+// MFMA m's (word w: rows 2w and 2w + 1 of channel 8r + m).
 // scale_log2 is this lane's head's factor (lane r = head r).
 template <bool TOPK, bool F16 = false>
 __device__ inline void compute_chunk(const Chunk& c, int cs, int end,
@@ -563,13 +565,17 @@ __device__ inline void compute_chunk(const Chunk& c, int cs, int end,
   const u32x4 pv = {pp[0], pp[1], pp[2], pp[3]};
 #pragma unroll
   for (int m = 0; m < 8; ++m) {
-    const uint32_t sel = (m & 1) ? 0x07060302u : 0x05040100u;
-    const int dw = m >> 1;
     u32x4 a;
-    a[0] = __builtin_amdgcn_perm(c.v[1][dw], c.v[0][dw], sel);
-    a[1] = __builtin_amdgcn_perm(c.v[3][dw], c.v[2][dw], sel);
-    a[2] = __builtin_amdgcn_perm(c.v[5][dw], c.v[4][dw], sel);
-    a[3] = __builtin_amdgcn_perm(c.v[7][dw], c.v[6][dw], sel);
+    if constexpr (F16) {
+      a = c.v[m];
+    } else {
+      const uint32_t sel = (m & 1) ? 0x07060302u : 0x05040100u;
+      const int dw = m >> 1;
+      a[0] = __builtin_amdgcn_perm(c.v[1][dw], c.v[0][dw], sel);
+      a[1] = __builtin_amdgcn_perm(c.v[3][dw], c.v[2][dw], sel);
+      a[2] = __builtin_amdgcn_perm(c.v[5][dw], c.v[4][dw], sel);
+      a[3] = __builtin_amdgcn_perm(c.v[7][dw], c.v[6][dw], sel);
+    }
     st.acc[m] = mma(a, pv, st.acc[m]);
   }
 }
@@ -657,9 +663,13 @@ __device__ inline void load_chunk(ChunkF4& c, int cs, int end, __amdgpu_buffer_r
   }
 }
 
-// Widened to f16 (exactly: fp4x8_to_f16x8) for the f16 products; the
-// scales two at a time (blocks 2g and 2g + 1 of a K row; the block of V rows
-// e and e + 1).
+// Widened to f16 (exactly) for the f16 products; the scales two at a time
+// (blocks 2g and 2g + 1 of a K row; the block of V rows e and e + 1).  K as
+// fp4x8_to_f16x8 gives it.  V straight into the value product's operand
+// layout: the codes of rows 2w and 2w + 1 are first interleaved by nibble
+// (byte k of x: channel 2k of each row; of y: channel 2k + 1), so that one
+// conversion gives the pair (row 2w, row 2w + 1) of one channel, and one
+// packed multiply applies the two rows' scales.
 __device__ inline void expand_chunk(const ChunkF4& f, Chunk& c) {
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
@@ -668,10 +678,17 @@ __device__ inline void expand_chunk(const ChunkF4& f, Chunk& c) {
     for (int kk = 0; kk < 4; ++kk) c.k[a][kk] = fp4x8_to_f16x8(f.k[a][kk], kk < 2 ? s[0] : s[1]);
   }
 #pragma unroll
-  for (int e = 0; e < 8; e += 2) {
-    const f16x2 s = e4m3x2_to_f16x2(f.vs[e] | (f.vs[e + 1] << 8));
-    c.v[e] = fp4x8_to_f16x8(f.v[e], s[0]);
-    c.v[e + 1] = fp4x8_to_f16x8(f.v[e + 1], s[1]);
+  for (int w = 0; w < 4; ++w) {
+    const f16x2 s = e4m3x2_to_f16x2(f.vs[2 * w] | (f.vs[2 * w + 1] << 8));
+    const uint32_t r0 = f.v[2 * w], r1 = f.v[2 * w + 1];
+    const uint32_t x = (r0 & 0x0F0F0F0Fu) | ((r1 << 4) & 0xF0F0F0F0u);
+    const uint32_t y = ((r0 >> 4) & 0x0F0F0F0Fu) | (r1 & 0xF0F0F0F0u);
+    const u32x4 ev = fp4x8_to_f16x8(x, s), od = fp4x8_to_f16x8(y, s);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      c.v[2 * k][w] = ev[k];
+      c.v[2 * k + 1][w] = od[k];
+    }
   }
   c.vmask = 0xFF;
 }

@@ -68,14 +68,17 @@ __device__ inline f16x8 as_f16x8(u32x4 x) { return __builtin_bit_cast(f16x8, x);
 // are f16 numbers, and their product has at most 6 significant bits and
 // lies in 2^-10 .. 2688 (f16 normal numbers hold 11 bits from 2^-14 to
 // 65504).  One conversion and one packed f16 multiply per two numbers.
-__device__ inline u32x4 fp4x8_to_f16x8(uint32_t w, _Float16 s) {
-  const f16x2 m = {s, s};
+// (m: the multipliers of the low and the high code of each byte)
+__device__ inline u32x4 fp4x8_to_f16x8(uint32_t w, f16x2 m) {
   u32x4 r;
   r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * m);
   r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * m);
   r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * m);
   r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * m);
   return r;
+}
+__device__ inline u32x4 fp4x8_to_f16x8(uint32_t w, _Float16 s) {
+  return fp4x8_to_f16x8(w, f16x2{s, s});
 }
 
 // Two E4M3 codes (bits 0-7 and 8-15 of w) as two f16, exactly.
