@@ -36,20 +36,23 @@
 // Segmented form (a workspace given, no pool, rows of at most 2^18
 // positions): one workgroup per row leaves most compute units idle when
 // there are few rows, so each row is cut into segments of whole
-// 16384-position steps, about 512 workgroups in all, one kernel:
+// 16384-position steps, about 256 workgroups in all, one kernel:
 //  - every workgroup of a row reads the same 1/32 sample of it (64
 //    positions of every 2048) and takes a lower bound of the row's K-th
 //    largest key that leaves, in expectation, about K + 4 standard
 //    deviations' worth of keys above it;
-//  - it writes the keys of its segment at or above the bound, with
-//    positions, to per-wave candidate lists (no atomics);
+//  - each of its waves writes the keys of its own contiguous part of the
+//    segment at or above the bound, with positions, to its candidate list
+//    (no atomics), so the lists in (segment, wave) order run in ascending
+//    position order;
 //  - the last workgroup of the row to finish (a ticket) gathers all the
-//    candidates into LDS, finds the exact K-th largest among them (8-bit
-//    digits, one wave scanning each 256-bin histogram), breaks ties by
-//    position, marks the chosen positions in a map and writes them out in
-//    order.  A row whose lists overflowed, or whose bound left fewer than K
-//    keys above it, is finished by the one-workgroup algorithm above
-//    instead.
+//    candidates into LDS in that order, finds the exact K-th largest among
+//    them (two 11-bit digit passes over its distance from the bound, three
+//    over whole keys when it lies 2^22 or more above it; one wave scanning
+//    each 2048-bin histogram), breaks ties by position, and writes the
+//    chosen ones out by a prefix count.  A row whose lists overflowed, or
+//    whose bound left fewer than K keys above it, is finished by the
+//    one-workgroup algorithm above instead.
 // The chosen set is the same as the one-workgroup algorithm's (the
 // selection is defined uniquely), so the output is too.
 
