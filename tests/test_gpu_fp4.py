@@ -157,35 +157,43 @@ def test_fp4_decode_parity(n_h, n_kv, pre, L_max, split):
     compare_lse(host(lse), l_ref, 4e-3)
 
 
-def test_fp4_every_code_exact():
+@pytest.mark.parametrize("n_h", [128, 64])
+def test_fp4_every_code_exact(n_h):
     """One cached position per sequence: the output is that position's value
     row dequantised, and with a one-hot query at column c the lse is
-    scale * key[c].  The 2 x 8 x 8 blocks of each operand take every finite
-    non-negative E4M3 scale code 0x00 .. 0x7E (zero, the subnormals up to
-    448) in a different order for keys and values, and each block holds all
-    16 E2M1 codes in a rotated order, so every code meets every scale
-    through both operands; the one-hot columns pin the key column order
-    against the query's."""
-    B, n_h, n_kv, d, L_max = 2, 128, 8, 128, 4
+    scale * key[c].  The 2 x 8 x 8 blocks of each operand pattern take every
+    finite non-negative E4M3 scale code 0x00 .. 0x7E (zero, the subnormals
+    up to 448) in a different order for keys and values, and each block
+    holds all 16 E2M1 codes in a rotated order, so every code meets every
+    scale through both operands; the one-hot columns pin the key column
+    order against the query's.  16 heads per KV head (every score column
+    used) and 8 (half of them padding); sequence b holds pattern b % 2 and
+    its heads read columns h + G * (b // 2), so each pattern's 128 columns
+    are all read."""
+    n_kv, d, L_max = 8, 128, 4
     G = n_h // n_kv
+    B = 2 * (128 // G)
     all_scales = np.concatenate([np.arange(0x7F), [0x38]]).astype(np.uint8)   # 128 blocks
-    v_scales = all_scales.reshape(B, n_kv, 8)
-    k_scales = np.roll(all_scales, 37).reshape(B, n_kv, 8)
+    v_scales = all_scales.reshape(2, n_kv, 8)
+    k_scales = np.roll(all_scales, 37).reshape(2, n_kv, 8)
     kc = np.zeros((B, n_kv, L_max, d // 2), np.uint8)
     vc = np.zeros((B, n_kv, L_max, d // 2), np.uint8)
     ks = np.zeros((B, n_kv, L_max, d // 16), np.uint8)
     vs = np.zeros((B, n_kv, L_max, d // 16), np.uint8)
     q = np.zeros((B, n_h, d), np.float32)
+    col = np.zeros((B, n_h), np.int64)
     for b in range(B):
+        pb = b % 2
         for j in range(n_kv):
-            codes = np.concatenate([np.roll(np.arange(16), j + blk + 3 * b) for blk in range(8)])
-            kcodes = np.roll(codes, 5 * j + b)
+            codes = np.concatenate([np.roll(np.arange(16), j + blk + 3 * pb) for blk in range(8)])
+            kcodes = np.roll(codes, 5 * j + pb)
             vc[b, j, 0] = (codes[0::2] | (codes[1::2] << 4)).astype(np.uint8)
             kc[b, j, 0] = (kcodes[0::2] | (kcodes[1::2] << 4)).astype(np.uint8)
-            ks[b, j, 0] = k_scales[b, j]
-            vs[b, j, 0] = v_scales[b, j]
+            ks[b, j, 0] = k_scales[pb, j]
+            vs[b, j, 0] = v_scales[pb, j]
             for h in range(G):
-                q[b, j * G + h, j * G + h] = 1.0
+                col[b, j * G + h] = h + G * (b // 2)
+                q[b, j * G + h, col[b, j * G + h]] = 1.0
     scale = 0.25
     sl = torch.ones(B, dtype=torch.int32, device="cuda")
     qd = dev(syn.bf16_bits(q))
@@ -201,8 +209,7 @@ def test_fp4_every_code_exact():
     for b in range(B):
         for j in range(n_kv):
             assert np.array_equal(o[b, j * G:(j + 1) * G], np.broadcast_to(want_v[b, j], (G, d)))
-    for b in range(B):
-        want_l = np.array([scale * want_k[b, i // G, i] for i in range(n_h)])
-        got_l = host(lse)[b].astype(np.float64)
-        # a zero key gives lse = 0 (one position, weight 1)
-        assert np.abs(got_l - want_l).max() <= 1e-6 * np.abs(want_l).max() + 1e-7
+    got_l = host(lse).astype(np.float64)
+    want_l = np.array([[scale * want_k[b, i // G, col[b, i]] for i in range(n_h)] for b in range(B)])
+    # a zero key gives lse = 0 (one position, weight 1)
+    assert np.abs(got_l - want_l).max() <= 1e-6 * np.abs(want_l).max() + 1e-7
