@@ -584,10 +584,14 @@ __device__ inline void compute_chunk(const Chunk& c, int cs, int end,
 // codes and expanded to bf16 (exactly) just before its MFMAs.  The dot
 // product's column order is free as long as q uses the same one, so K k-step
 // kk, lane group g covers columns (kk/2)*64 + g*16 + (kk%2)*8 .. +7: one
-// 16-byte load per (row, kk/2).  V keeps the bf16 layout (8 bytes per row).
+// 16-byte load per (row, kk/2).  V ends in the bf16 layout (8 bytes per
+// row and lane) but is loaded 16 bytes at a time: lanes 2k and 2k + 1 load
+// channels 16k .. 16k + 15 of rows 2w and 2w + 1 respectively, then swap
+// halves (one adjacent-lane move per dword), so each lane ends with its 8
+// channels of both rows: half the value load instructions.
 struct ChunkF8 {
   u32x4 k[2][2];
-  u32x2 v[8];
+  u32x4 v[4];
 };
 
 __device__ inline int fp8_q_col(int kk, int g) { return (kk >> 1) * 64 + g * 16 + (kk & 1) * 8; }
@@ -603,9 +607,10 @@ __device__ inline void load_chunk(ChunkF8& c, int cs, int end, __amdgpu_buffer_r
 #pragma unroll
     for (int h = 0; h < 2; ++h) c.k[a][h] = buf_load16_stream(kr, kb + h * 64);
   }
-  const uint32_t vb = live ? (uint32_t)(cs + g * 8) * kRow + r * 8 : kOobOffset;
+  const uint32_t vb =
+      live ? (uint32_t)(cs + g * 8 + (r & 1)) * kRow + (r >> 1) * 16 : kOobOffset;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) c.v[e] = buf_load8_stream(vr, vb + e * kRow);
+  for (int w = 0; w < 4; ++w) c.v[w] = buf_load16_stream(vr, vb + 2 * w * kRow);
 }
 
 __device__ inline void expand_chunk(const ChunkF8& f, Chunk& c) {
@@ -617,8 +622,18 @@ __device__ inline void expand_chunk(const ChunkF8& f, Chunk& c) {
       const u32x2 h = (kk & 1) ? u32x2{w[2], w[3]} : u32x2{w[0], w[1]};
       c.k[a][kk] = fp8x8_to_bf16x8(h);
     }
+  const bool odd = threadIdx.x & 1;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) c.v[e] = fp8x8_to_bf16x8(f.v[e]);
+  for (int w = 0; w < 4; ++w) {
+    const u32x4 d = f.v[w];                 // row 2w + odd, channels 16k .. 16k + 15
+    const uint32_t s0 = odd ? d[0] : d[2], s1 = odd ? d[1] : d[3];
+    const uint32_t t0 = (uint32_t)__builtin_amdgcn_mov_dpp((int)s0, 0xB1, 0xF, 0xF, false);
+    const uint32_t t1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)s1, 0xB1, 0xF, 0xF, false);
+    const u32x2 re = odd ? u32x2{t0, t1} : u32x2{d[0], d[1]};   // row 2w, own channels
+    const u32x2 ro = odd ? u32x2{d[2], d[3]} : u32x2{t0, t1};   // row 2w + 1
+    c.v[2 * w] = fp8x8_to_bf16x8(re);
+    c.v[2 * w + 1] = fp8x8_to_bf16x8(ro);
+  }
   c.vmask = 0xFF;
 }
 
