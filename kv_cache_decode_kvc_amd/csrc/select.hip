@@ -809,7 +809,6 @@ __global__ __launch_bounds__(kSelThreads) void seg_select_kernel(SelectParams p)
 
   // ---- the row's last workgroup: select among all the candidates
   if (tid == 0) p.ws_cnt[q.row] = 0;
-  const int n = q.n;
   const int c = tid < nreg ? (int)__builtin_amdgcn_raw_buffer_load_b32(
                                  wn_r, (uint32_t)(((size_t)q.row * nreg + tid) * 4), 0, kCoherent)
                            : 0;
