@@ -114,15 +114,14 @@ enum CacheFmt { kFmtPlain = 0, kFmtFp8 = 1, kFmtFp4 = 2 };
 
 // Persistent form: items of whole 1024-position multiples (the multiple
 // nearest n_max / P, P = target / units), about this many per call (3.5 per
-// workgroup for bf16 caches, 5.5 for E4M3 ones, 2 for FP4 ones, whose items
-// are the quickest to stream and so pay most for each item's set-up and
-// merge).  Measured on the 32-sequence GQA layer (lengths 1024..32768, 256
-// units): contiguous bf16 314.7 us at 5120 positions against 326.8 at 2048,
-// paged 325 against 333, E4M3 177.8 at 3072 against 180.1 at 2048 and
-// 183.9 at 5120, FP4 123.7 at 8192 against 129.3 at 5120, 128.6 at 6144
-// and 131.6 at 9216.
+// workgroup for bf16 and E4M3 caches, 2 for FP4 ones, whose items are the
+// quickest to stream and so pay most for each item's set-up and merge).
+// Measured on the 32-sequence GQA layer (lengths 1024..32768, 256 units):
+// contiguous bf16 314.7 us at 5120 positions against 326.8 at 2048, paged
+// 325 against 333, E4M3 171.7 at 5120 against 177.6 at 3072, 183.0 at 4096
+// and 181.4 at 6144 (with 16-byte value loads), FP4 123.7 at 8192 against
+// 129.3 at 5120, 128.6 at 6144 and 131.6 at 9216.
 constexpr int64_t kPersistItems = 1792;
-constexpr int64_t kPersistItemsFp8 = 2816;
 constexpr int64_t kPersistItemsFp4 = 1024;
 constexpr int64_t kPersistGran = 1024;
 
@@ -155,9 +154,7 @@ DenseCheck check_dense_shape(int B, int n_h, int n_kv, int L_max, int d,
   c.persist = !c.even && !topk && dtype == KVC_BF16 && d == 128 && B <= kPersistMaxB &&
               units <= kPersistMaxUnits;
   if (c.persist && g_split_override.load() == 0) {
-    const int64_t target = fmt == kFmtFp8   ? kPersistItemsFp8
-                           : fmt == kFmtFp4 ? kPersistItemsFp4
-                                            : kPersistItems;
+    const int64_t target = fmt == kFmtFp4 ? kPersistItemsFp4 : kPersistItems;
     const int64_t P_allowed = units < target ? target / units : 1;
     int64_t S = (n_max / P_allowed + kPersistGran / 2) / kPersistGran * kPersistGran;
     if (S < kPersistGran) S = kPersistGran;
