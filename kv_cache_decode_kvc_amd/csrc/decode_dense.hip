@@ -641,7 +641,7 @@ __device__ inline void expand_chunk(const ChunkF8& f, Chunk& c) {
 // nibble of byte i) and 8 scale bytes (E4M3, one per 16 channels).  K: lane
 // group g loads the 16 code bytes of channels 32g .. 32g + 31, so k-step kk
 // covers channels 32g + 8kk .. +7 (q is loaded in that order), and the two
-// scale bytes of blocks 2g and 2g + 1.  V keeps the bf16 layout: 4 code
+// scale bytes of blocks 2g and 2g + 1.  V ends in the bf16 layout: 4 code
 // bytes (channels 8r .. 8r + 7) per row and the scale byte of block r / 2.
 // Each stream takes one offset select per chunk; its rows differ by
 // immediate offsets (a chunk past the split starts at kOobOffset, past every
@@ -649,8 +649,8 @@ __device__ inline void expand_chunk(const ChunkF8& f, Chunk& c) {
 struct ChunkF4 {
   u32x4 k[2];
   uint32_t ks[2];
-  uint32_t v[8];
-  uint32_t vs[8];
+  u32x2 v[4];       // row 2w + (r & 1), channels 16(r / 2) .. + 15
+  uint32_t vs[4];   // scale byte of row 2w + (r & 1), block r / 2
 };
 
 __device__ inline int fp4_q_col(int kk, int g) { return g * 32 + kk * 8; }
@@ -669,13 +669,17 @@ __device__ inline void load_chunk(ChunkF4& c, int cs, int end, __amdgpu_buffer_r
     c.ks[a] = __builtin_amdgcn_raw_buffer_load_b16(ksr, ksb + a * 4 * kSRow, 0, kStream);
   }
   const uint32_t row0 = cs + g * 8;                           // rows row0 + e
-  const uint32_t vb = live ? row0 * kRow + r * 4 : kOobOffset;
-  const uint32_t vsb = live ? row0 * kSRow + (r >> 1) : kOobOffset;
+  // value codes 8 bytes at a time: lanes 2k and 2k + 1 load the 16
+  // channels they share of rows 2w and 2w + 1, and the scale byte of their
+  // (shared) block of those rows (swapped into place when widened): half
+  // the value load instructions
+  const uint32_t vb = live ? (row0 + (r & 1)) * kRow + (r >> 1) * 8 : kOobOffset;
+  const uint32_t vsb = live ? (row0 + (r & 1)) * kSRow + (r >> 1) : kOobOffset;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    c.v[e] = __builtin_amdgcn_raw_buffer_load_b32(vr, vb + e * kRow, 0, kStream);
-    c.vs[e] = __builtin_amdgcn_raw_buffer_load_b8(vsr, vsb + e * kSRow, 0, kStream);
-  }
+  for (int w = 0; w < 4; ++w) c.v[w] = buf_load8_stream(vr, vb + 2 * w * kRow);
+#pragma unroll
+  for (int w = 0; w < 4; ++w)
+    c.vs[w] = __builtin_amdgcn_raw_buffer_load_b8(vsr, vsb + 2 * w * kSRow, 0, kStream);
 }
 
 // Widened to f16 (exactly) for the f16 products; the scales two at a time
@@ -694,8 +698,16 @@ __device__ inline void expand_chunk(const ChunkF4& f, Chunk& c) {
   }
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
-    const f16x2 s = e4m3x2_to_f16x2(f.vs[2 * w] | (f.vs[2 * w + 1] << 8));
-    const uint32_t r0 = f.v[2 * w], r1 = f.v[2 * w + 1];
+    // this lane's channels of rows 2w and 2w + 1 (one adjacent-lane swap;
+    // the two rows' scale bytes the same way)
+    const bool odd = threadIdx.x & 1;
+    const uint32_t so = f.vs[w];
+    const uint32_t st = (uint32_t)__builtin_amdgcn_mov_dpp((int)so, 0xB1, 0xF, 0xF, false);
+    const f16x2 s = e4m3x2_to_f16x2(odd ? (st | (so << 8)) : (so | (st << 8)));
+    const u32x2 d = f.v[w];
+    const uint32_t t = (uint32_t)__builtin_amdgcn_mov_dpp((int)(odd ? d[0] : d[1]), 0xB1, 0xF, 0xF,
+                                                          false);
+    const uint32_t r0 = odd ? t : d[0], r1 = odd ? d[1] : t;
     const uint32_t x = (r0 & 0x0F0F0F0Fu) | ((r1 << 4) & 0xF0F0F0F0u);
     const uint32_t y = ((r0 >> 4) & 0x0F0F0F0Fu) | (r1 & 0xF0F0F0F0u);
     const u32x4 ev = fp4x8_to_f16x8(x, s), od = fp4x8_to_f16x8(y, s);
