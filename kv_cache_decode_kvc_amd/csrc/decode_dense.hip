@@ -646,11 +646,21 @@ __device__ inline void expand_chunk(const ChunkF8& f, Chunk& c) {
 // Each stream takes one offset select per chunk; its rows differ by
 // immediate offsets (a chunk past the split starts at kOobOffset, past every
 // buffer's range, and reads zeros like the rows past the length).
+// lane j's value in each quad of lanes (j a constant after unrolling)
+__device__ inline uint32_t quad_bcast(int x, int j) {
+  switch (j) {
+    case 0: return (uint32_t)__builtin_amdgcn_mov_dpp(x, 0x00, 0xF, 0xF, false);
+    case 1: return (uint32_t)__builtin_amdgcn_mov_dpp(x, 0x55, 0xF, 0xF, false);
+    case 2: return (uint32_t)__builtin_amdgcn_mov_dpp(x, 0xAA, 0xF, 0xF, false);
+    default: return (uint32_t)__builtin_amdgcn_mov_dpp(x, 0xFF, 0xF, 0xF, false);
+  }
+}
+
 struct ChunkF4 {
   u32x4 k[2];
   uint32_t ks[2];
   u32x2 v[4];       // row 2w + (r & 1), channels 16(r / 2) .. + 15
-  uint32_t vs[4];   // scale byte of row 2w + (r & 1), block r / 2
+  uint32_t vs[2];   // scale bytes of rows (r & 3) and 4 + (r & 3), blocks 2(r / 4) .. + 1
 };
 
 __device__ inline int fp4_q_col(int kk, int g) { return g * 32 + kk * 8; }
@@ -670,16 +680,17 @@ __device__ inline void load_chunk(ChunkF4& c, int cs, int end, __amdgpu_buffer_r
   }
   const uint32_t row0 = cs + g * 8;                           // rows row0 + e
   // value codes 8 bytes at a time: lanes 2k and 2k + 1 load the 16
-  // channels they share of rows 2w and 2w + 1, and the scale byte of their
-  // (shared) block of those rows (swapped into place when widened): half
-  // the value load instructions
+  // channels they share of rows 2w and 2w + 1 (swapped into place when
+  // widened); value scales 2 bytes at a time: lane 4k + i loads the two
+  // blocks its quad shares (2k, 2k + 1) of rows i and 4 + i (broadcast
+  // within the quad when widened): 6 value load instructions instead of 16
   const uint32_t vb = live ? (row0 + (r & 1)) * kRow + (r >> 1) * 8 : kOobOffset;
-  const uint32_t vsb = live ? (row0 + (r & 1)) * kSRow + (r >> 1) : kOobOffset;
+  const uint32_t vsb = live ? (row0 + (r & 3)) * kSRow + (r >> 2) * 2 : kOobOffset;
 #pragma unroll
   for (int w = 0; w < 4; ++w) c.v[w] = buf_load8_stream(vr, vb + 2 * w * kRow);
 #pragma unroll
-  for (int w = 0; w < 4; ++w)
-    c.vs[w] = __builtin_amdgcn_raw_buffer_load_b8(vsr, vsb + 2 * w * kSRow, 0, kStream);
+  for (int h = 0; h < 2; ++h)
+    c.vs[h] = __builtin_amdgcn_raw_buffer_load_b16(vsr, vsb + 4 * h * kSRow, 0, kStream);
 }
 
 // Widened to f16 (exactly) for the f16 products; the scales two at a time
@@ -698,12 +709,16 @@ __device__ inline void expand_chunk(const ChunkF4& f, Chunk& c) {
   }
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
-    // this lane's channels of rows 2w and 2w + 1 (one adjacent-lane swap;
-    // the two rows' scale bytes the same way)
+    // this lane's channels of rows 2w and 2w + 1 (one adjacent-lane swap)
     const bool odd = threadIdx.x & 1;
-    const uint32_t so = f.vs[w];
-    const uint32_t st = (uint32_t)__builtin_amdgcn_mov_dpp((int)so, 0xB1, 0xF, 0xF, false);
-    const f16x2 s = e4m3x2_to_f16x2(odd ? (st | (so << 8)) : (so | (st << 8)));
+    // rows 2w and 2w + 1 come from quad lanes (2w) % 4 and (2w + 1) % 4;
+    // this lane's block is byte (r / 2) % 2 of each
+    const int vsrc = (int)f.vs[w >> 1];
+    const uint32_t sa = quad_bcast(vsrc, (2 * w) & 3);
+    const uint32_t sb = quad_bcast(vsrc, (2 * w + 1) & 3);
+    const uint32_t bsel = (threadIdx.x >> 1) & 1;
+    const f16x2 s =
+        e4m3x2_to_f16x2(__builtin_amdgcn_perm(sb, sa, 0x0C0C0000u | bsel | ((4u + bsel) << 8)));
     const u32x2 d = f.v[w];
     const uint32_t t = (uint32_t)__builtin_amdgcn_mov_dpp((int)(odd ? d[0] : d[1]), 0xB1, 0xF, 0xF,
                                                           false);
