@@ -422,12 +422,14 @@ struct PageIdx {
   uint32_t v;
 };
 
+// (cs is a multiple of 32 and blocks hold at least 8 positions, so a lane's
+// two key rows, 4 apart within one aligned group of 8, share a block: one
+// table load serves both)
 __device__ inline void load_page_idx(PageIdx& x, int cs, __amdgpu_buffer_rsrc_t tr, int shift,
                                      int r, int g) {
-#pragma unroll
-  for (int a = 0; a < 2; ++a)
-    x.k[a] = __builtin_amdgcn_raw_buffer_load_b32(
-        tr, (uint32_t)((cs + (r >> 2) * 8 + a * 4 + (r & 3)) >> shift) * 4, 0, 0);
+  x.k[0] = __builtin_amdgcn_raw_buffer_load_b32(
+      tr, (uint32_t)((cs + (r >> 2) * 8) >> shift) * 4, 0, 0);
+  x.k[1] = x.k[0];
   x.v = __builtin_amdgcn_raw_buffer_load_b32(tr, (uint32_t)((cs + g * 8) >> shift) * 4, 0, 0);
 }
 
