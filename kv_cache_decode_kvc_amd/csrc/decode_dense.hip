@@ -372,18 +372,18 @@ __device__ inline void load_chunk(Chunk& c, int cs, int end,
 // they address (entries past K read as zero and are masked).  Lane (r, g)
 // takes the slots of its V rows, cs + g*8 + 0..7, and of its K rows,
 // cs + pi(a, r).
+// A chunk's list entries as lane group g loads them: slots g*8 .. g*8 + 7
+// (the value rows).  The key rows' entries are among them (lane (r, g)
+// scores slots (r/4)*8 + 4a + r%4, held by lane group r/4) and are fetched
+// across the wave when used.
 struct ChunkIdx {
   u32x4 v0, v1;
-  uint32_t k[2];
 };
 
 __device__ inline void load_idx(ChunkIdx& x, int cs, __amdgpu_buffer_rsrc_t ir, int r, int g) {
+  (void)r;
   x.v0 = buf_load16(ir, (uint32_t)(cs + g * 8) * 4);
   x.v1 = buf_load16(ir, (uint32_t)(cs + g * 8 + 4) * 4);
-#pragma unroll
-  for (int a = 0; a < 2; ++a)
-    x.k[a] = __builtin_amdgcn_raw_buffer_load_b32(
-        ir, (uint32_t)(cs + (r >> 2) * 8 + a * 4 + (r & 3)) * 4, 0, 0);
 }
 
 __device__ inline void load_listed(Chunk& c, const ChunkIdx& x, int cs, int end, int n,
@@ -402,11 +402,18 @@ __device__ inline void load_listed(Chunk& c, const ChunkIdx& x, int cs, int end,
     c.v[e] = buf_load16_stream(vr, use ? iv[e] * kRow + r * 16 : kOobOffset);
   }
   c.vmask = mask;
+  // key entries: each lane offers entry lane % 4 of its group's slice a,
+  // and lane (r, g) takes it from lane 16 (r / 4) + r % 4
+  const int lane = threadIdx.x & 63;
+  const int src = ((r >> 2) * 16 + (r & 3)) * 4;
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
+    const u32x4 va = a ? x.v1 : x.v0;
+    const uint32_t own = (lane & 2) ? ((lane & 1) ? va[3] : va[2]) : ((lane & 1) ? va[1] : va[0]);
+    const uint32_t ka = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)own);
     const int slot = cs + (r >> 2) * 8 + a * 4 + (r & 3);
-    const bool use = slot < end && x.k[a] < (uint32_t)n;
-    const uint32_t kb = use ? x.k[a] * kRow + g * 16 : kOobOffset;
+    const bool use = slot < end && ka < (uint32_t)n;
+    const uint32_t kb = use ? ka * kRow + g * 16 : kOobOffset;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) c.k[a][kk] = buf_load16_stream(kr, kb + kk * 64);
   }
